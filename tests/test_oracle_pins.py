@@ -1,0 +1,161 @@
+"""The CPU oracle against its pins, and planted mistakes that the pins must catch."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import lora as olora
+from oracle import nf4 as onf4
+
+from . import pins
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+def test_representable_midpoints():
+    # the exact-tie pin is only meaningful if some midpoints are fp32 values
+    assert pins.representable_midpoints(oracle.nf4_table()) == [2, 6, 7, 14]
+
+
+def test_golden_table():
+    """Stored table (written by tests/golden/make_golden.py from the oracle) still matches."""
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "nf4_table.txt")
+    bits = []
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            bits.append(int(line.split()[1], 16))
+    assert np.array_equal(np.array(bits, np.uint32), oracle.nf4_table().view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each broken oracle variant must fail at least one pin
+# ---------------------------------------------------------------------------
+
+def _fails(fn, *args, **kw):
+    try:
+        fn(*args, **kw)
+    except AssertionError:
+        return True
+    return False
+
+
+def test_mistake_symmetric_table():
+    # 8 negative / 7 positive instead of 7 / 8 (sign flipped construction)
+    bad = lambda: -oracle.nf4_table()[::-1].copy()
+    assert _fails(pins.pin_table_structure, bad) or _fails(pins.pin_table_independent, bad)
+
+
+def test_mistake_table_offset():
+    import statistics
+    def bad():
+        inv = statistics.NormalDist().inv_cdf
+        delta = 0.97                              # wrong outermost probability
+        z = inv(delta)
+        v = [inv(delta - j * (delta - .5) / 8) / z for j in range(8)]
+        v += [-inv(delta - j * (delta - .5) / 7) / z for j in range(7)] + [0.0]
+        return np.array(sorted(v)).astype(np.float32)
+    assert _fails(pins.pin_table_independent, bad)
+
+
+def test_mistake_upper_tie():
+    def bad_quantize(W, block=64, dq=0):
+        q = onf4.quantize(W, block, dq)
+        t = onf4.nf4_table().astype(np.float64)
+        Wb = np.asarray(W, np.float32).reshape(-1, block)
+        a = np.max(np.abs(Wb), axis=1)
+        x = (Wb / np.where(a == 0, 1, a)[:, None]).astype(np.float32).astype(np.float64)
+        d = np.abs(x[..., None] - t)
+        # last minimum instead of the first
+        q.codes = (15 - np.argmin(d[..., ::-1], axis=-1)).astype(np.uint8).reshape(-1)
+        return q
+    assert _fails(pins.pin_exact_ties, bad_quantize)
+
+
+def test_mistake_reciprocal_multiply():
+    # w * (1/a) instead of the correctly rounded w / a
+    def bad_quantize(W, block=64, dq=0):
+        q = onf4.quantize(W, block, dq)
+        Wb = np.asarray(W, np.float32).reshape(-1, block)
+        a = np.max(np.abs(Wb), axis=1).astype(np.float32)
+        inv = (np.float32(1) / np.where(a == 0, np.float32(1), a)).astype(np.float32)
+        x = (Wb * inv[:, None]).astype(np.float32)
+        q.codes = onf4._encode(x, onf4.nf4_table()).reshape(-1)
+        return q
+    assert _fails(pins.pin_midpoint_sweeps, bad_quantize, n_scales=6)
+
+
+def test_mistake_nibble_order():
+    bad = lambda c: (np.asarray(c, np.uint8)[1::2] | (np.asarray(c, np.uint8)[0::2] << 4)).astype(np.uint8)
+    assert _fails(pins.pin_pack, bad)
+
+
+def test_mistake_dq_256_levels():
+    def bad_quantize(W, block=64, dq=0):
+        q = onf4.quantize(W, block, dq)
+        if dq:
+            nb = q.absmax.size
+            for g in range(q.dq_scale.size):
+                q.dq_scale[g] = np.float32(q.absmax[g * dq:(g + 1) * dq].max()) / np.float32(256)
+            Sb = q.dq_scale[np.arange(nb) // dq]
+            q.c8 = np.minimum(255, np.rint(q.absmax / Sb)).astype(np.uint8)
+        return q
+    assert _fails(pins.pin_dq_exact, bad_quantize)
+
+
+def test_mistake_dq_truncation():
+    def bad_quantize(W, block=64, dq=0):
+        q = onf4.quantize(W, block, dq)
+        if dq:
+            Sb = q.dq_scale[np.arange(q.absmax.size) // dq]
+            q.c8 = np.floor(q.absmax / Sb).astype(np.uint8)
+        return q
+    assert _fails(pins.pin_dq_bound, bad_quantize) or _fails(pins.pin_dq_exact, bad_quantize)
+
+
+def test_mistake_transposed_weight():
+    # reads the [o][h] storage as if it were laid out [h][o]
+    def bad_fwd(X, W, L1, L2, s):
+        X, W, A, B = (np.asarray(v, np.float64) for v in (X, W, L1, L2))
+        T = X @ A
+        return X @ W.reshape(W.shape[1], W.shape[0]) + s * (T @ B), T
+    assert _fails(pins.pin_fwd_bruteforce, bad_fwd)
+
+
+def test_mistake_dropped_scale():
+    def bad_fwd(X, W, L1, L2, s):
+        return olora.fwd(X, W, L1, L2, 1.0)
+    assert _fails(pins.pin_fwd_bruteforce, bad_fwd)
+    assert _fails(pins.pin_fwd_special, bad_fwd)
+
+
+def test_mistake_bwd_missing_scale():
+    def bad_bwd(X, dY, W, L1, L2, s):
+        dX, dL1, dL2, G = olora.bwd(X, dY, W, L1, L2, s)
+        return dX, dL1, dL2 / s, G                  # dL2 without s
+    assert _fails(pins.pin_bwd_finite_diff, bwd_fn=bad_bwd)
+
+
+def test_mistake_bwd_adapter_term():
+    def bad_bwd(X, dY, W, L1, L2, s):
+        X64, dY64, W64 = (np.asarray(v, np.float64) for v in (X, dY, W))
+        dX, dL1, dL2, G = olora.bwd(X, dY, W, L1, L2, s)
+        return dY64 @ W64, dL1, dL2, G              # dX without the G L1^T term
+    assert _fails(pins.pin_bwd_finite_diff, bwd_fn=bad_bwd)
+
+
+def test_mistake_error_without_sqrt():
+    def bad_error(W, block=64, dq=0):
+        return onf4.layer_error(W, block, dq) ** 2
+    assert _fails(pins.pin_error_bruteforce, bad_error)
+
+
+def test_mistake_topk_ties():
+    def bad_topk(e, k):
+        return list(np.argsort(-np.asarray(e), kind="stable")[::-1][:k][::-1])
+    assert _fails(pins.pin_topk, bad_topk)
