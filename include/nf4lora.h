@@ -1,0 +1,212 @@
+/*
+ * libnf4lora: the QLoRA linear layer on an NF4-quantized frozen base, for
+ * AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The layer is equation (3) of "QLoRA: How to fine-tune large language
+ * models with less memory" ("The algebra" section):
+ *     Y = X W + s X L1 L2
+ * with the frozen W stored 4-bit NF4 ("1. NormalFloat"), one scale per block
+ * of 64 weights, optionally double quantized ("2. Double quantization").
+ * Only the adapters L1, L2 and the input X receive gradients; the frozen W
+ * is read, never differentiated ("Lesson 17. What QLoRA Actually Costs",
+ * Warm-up).
+ *
+ * Conventions used by every entry point
+ * -------------------------------------
+ * - W is stored [rows][cols] row-major: rows = o (outputs), cols = h
+ *   (inputs), the usual layout of a linear layer's weight; X W in the
+ *   equation is X * W_st^T here.
+ * - bf16 values travel as uint16_t bit patterns.  X [M][h], dY [M][o],
+ *   Y [M][o], dX [M][h], T [M][r] are row-major bf16; L1 [h][r] and
+ *   L2 [r][o] are row-major bf16; dL1 [h][r] and dL2 [r][o] are fp32.
+ * - Every pointer argument except the nf4_tensor descriptor itself and the
+ *   host scalars is a DEVICE pointer, and every device base pointer must be
+ *   16-byte aligned (NF4_ERR_ALIGN otherwise).
+ * - The caller owns every buffer.  The library allocates and frees nothing,
+ *   keeps no mutable global state, and is safe to call from several host
+ *   threads (calls on one stream run in stream order).
+ * - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *   asynchronously; nothing synchronizes.  Arguments are validated before
+ *   any launch and the first failure is returned; a failed launch returns
+ *   NF4_ERR_HIP; faults inside kernels surface at the caller's next
+ *   synchronization.  No C++ exception crosses this boundary.
+ * - Outputs must not overlap inputs (NF4_ERR_ALIAS).
+ * - Results are deterministic: all reductions run in a fixed order (no
+ *   floating-point atomics), so repeated calls give identical bits.
+ */
+#ifndef NF4LORA_H
+#define NF4LORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NF4LORA_ABI_VERSION 1
+
+typedef enum nf4_status {
+  NF4_OK = 0,
+  NF4_ERR_NULL = 1,       /* a required pointer is NULL */
+  NF4_ERR_SHAPE = 2,      /* a size is out of range or the sizes disagree */
+  NF4_ERR_ALIGN = 3,      /* a device pointer is not 16-byte aligned */
+  NF4_ERR_WORKSPACE = 4,  /* workspace NULL or smaller than nf4_workspace_bytes() */
+  NF4_ERR_ALIAS = 5,      /* an output buffer overlaps an input buffer */
+  NF4_ERR_HIP = 6,        /* a HIP runtime call or kernel launch failed */
+  NF4_ERR_ARG = 7         /* unsupported option (block size, group size, op id) */
+} nf4_status;
+
+/*
+ * Quantized weight descriptor (host struct; the buffers it points to are
+ * device memory owned by the caller).
+ *   rows, cols : W is [rows][cols]; cols % block == 0; rows >= 0.
+ *   block      : weights per scale block along a row; must be 64 (the block
+ *                size of "1. NormalFloat" / AQLoRA section 3.1).
+ *   dq_group   : 0  -> absmax is float[nblocks] (fp32 per block);
+ *                256 -> absmax is uint8[nblocks] (8-bit scale codes) and
+ *                dq_scale is float[ceil(nblocks/256)], one fp32 step per
+ *                group of 256 blocks ("2. Double quantization").
+ *   codes      : rows*cols/2 bytes; byte t holds element 2t in its low
+ *                nibble and element 2t+1 in its high nibble (row-major order).
+ * Dequantized weight: w_hat = fl32(table[code] * scale), scale = absmax
+ * (fp32) or fl32(c8 * dq_scale[group]).  nblocks = rows*cols/64.
+ */
+typedef struct nf4_tensor {
+  int64_t rows;
+  int64_t cols;
+  int32_t block;
+  int32_t dq_group;
+  uint8_t *codes;
+  void *absmax;
+  float *dq_scale;
+} nf4_tensor;
+
+/* Operation ids for nf4_workspace_bytes. */
+enum { NF4_OP_FWD = 1, NF4_OP_BWD = 2, NF4_OP_ERROR = 3 };
+
+/* ABI version of the loaded library (NF4LORA_ABI_VERSION). */
+int nf4_abi_version(void);
+
+/* Static string naming a status code; never NULL. */
+const char *nf4_status_str(int status);
+
+/*
+ * The 16 NF4 code values (fp32, ascending) the kernels use, written to the
+ * HOST array out[16].  They are normal quantiles at evenly spaced
+ * probabilities, seven negative, an exact zero and eight positive, each side
+ * scaled so its outermost value is exactly -1 or +1 (the NormalFloat layout
+ * of "1. NormalFloat", QLoRA blog).  Computed once in fp64 by the library's
+ * own inverse normal CDF and rounded to nearest fp32.
+ */
+void nf4_code_table(float out[16]);
+
+/*
+ * Byte sizes of the three buffers of a quantized [rows][cols] weight
+ * (host outputs; any may be NULL).  Storage follows the worked 65B budget in
+ * the QLoRA blog: 0.5 byte/weight of codes, plus 4 bytes per 64-weight block
+ * without double quantization, or 1 byte per block + 4 bytes per 256 blocks
+ * with it.  Errors: NF4_ERR_SHAPE, NF4_ERR_ARG.
+ */
+nf4_status nf4_tensor_bytes(int64_t rows, int64_t cols, int32_t block, int32_t dq_group,
+                            size_t *codes_bytes, size_t *absmax_bytes, size_t *dq_scale_bytes);
+
+/*
+ * Blockwise NF4 quantization of W (device fp32 [rows][cols], finite values)
+ * into the buffers of *q ("1. NormalFloat" and "2. Double quantization",
+ * QLoRA blog):
+ *   a_b  = max |w| over each block of 64;
+ *   x    = w / a_b (IEEE fp32 division; 0 for an all-zero block);
+ *   code = the nearest table value to x, the lower code on an exact tie;
+ *   with dq_group = 256, per group: S = fl32(max a_b / 255),
+ *   c8 = min(255, round-half-even(fl32(a_b / S))) (0 when S = 0).
+ * Codes do not depend on dq_group.  Errors: NF4_ERR_NULL, _SHAPE, _ARG,
+ * _ALIGN, _ALIAS, _HIP.
+ */
+nf4_status nf4_quantize(const float *W, const nf4_tensor *q, void *stream);
+
+/*
+ * Dequantize *q into W_out [rows][cols]: fp32 w_hat when out_is_bf16 == 0,
+ * else the bf16 round-to-nearest-even of w_hat ("1. NormalFloat": weights
+ * are reconstructed into bf16 before the matmul).  Errors as nf4_quantize.
+ */
+nf4_status nf4_dequantize(const nf4_tensor *q, void *W_out, int32_t out_is_bf16, void *stream);
+
+/*
+ * Workspace bytes for an operation (host output *bytes).
+ *   op = NF4_OP_FWD or NF4_OP_BWD: M tokens, W [rows][cols], rank r;
+ *   op = NF4_OP_ERROR: W [rows][cols] (M and r ignored).
+ * Errors: NF4_ERR_NULL, _SHAPE, _ARG.
+ */
+nf4_status nf4_workspace_bytes(int32_t op, int64_t M, int64_t rows, int64_t cols, int32_t r,
+                               size_t *bytes);
+
+/*
+ * Forward pass, equation (3): T = X L1 and Y = X W_hat^T + s T L2 with the
+ * NF4 weight dequantized to bf16 inside the matmul (never written out) and
+ * fp32 accumulation.  s is alpha/r ("LoRA: Fine-tuning a model by learning a
+ * small update", the algebra section; rsLoRA callers pass alpha/sqrt(r)).
+ *   W    : quantized [o][h], h % 64 == 0, o % 64 == 0.
+ *   X    : bf16 [M][h]; M >= 0 (M == 0 does nothing).
+ *   L1   : bf16 [h][r];  L2 : bf16 [r][o];  1 <= r <= 256.
+ *   Y    : bf16 [M][o] output.
+ *   T_out: bf16 [M][r] output (X L1, to hand to nf4lora_bwd), or NULL.
+ *   ws   : device workspace of at least nf4_workspace_bytes(NF4_OP_FWD,...).
+ * Errors: NF4_ERR_NULL, _SHAPE, _ARG, _ALIGN, _WORKSPACE, _ALIAS, _HIP.
+ */
+nf4_status nf4lora_fwd(const nf4_tensor *W, const uint16_t *X, int64_t M,
+                       const uint16_t *L1, const uint16_t *L2, int32_t r, float s,
+                       uint16_t *Y, uint16_t *T_out,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward pass of equation (3) for the adapters and the input; the frozen
+ * W gets no gradient ("Lesson 17", Warm-up):
+ *   G   = s dY L2^T                 (bf16 [M][r], internal)
+ *   dL2 = s T^T dY                  -> fp32 [r][o]
+ *   dL1 = X^T G                     -> fp32 [h][r]
+ *   dX  = dY W_hat + G L1^T         -> bf16 [M][h], optional
+ *   T   : the forward's T_out (bf16 [M][r]), or NULL to recompute X L1.
+ *   dX  : NULL skips the input gradient (the early backward stop of
+ *         AQLoRA's speed setting, section 3.3 Adapter placement).
+ * M == 0 writes zeros to dL1 and dL2.  Shapes and errors as nf4lora_fwd.
+ */
+nf4_status nf4lora_bwd(const nf4_tensor *W, const uint16_t *X, const uint16_t *dY, int64_t M,
+                       const uint16_t *L1, const uint16_t *L2, int32_t r, float s,
+                       const uint16_t *T, uint16_t *dX, float *dL1, float *dL2,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Per-layer NF4 reconstruction error of W (device fp32 [rows][cols]):
+ *   e = sqrt(sum (w - w_hat)^2) / sqrt(sum w^2)   (0 when W is all zero),
+ * w_hat from 64-weight blocks (dq_group 0) or with double quantization
+ * (dq_group 256).  This is the ranking quantity of AQLoRA's profiling pass
+ * (section 3.1; the page's equation is missing, the relative Frobenius norm
+ * is the reading).  fp32 per element, fp64 across blocks, fixed reduction
+ * order.  err_dev: device double[1].  ws: nf4_workspace_bytes(NF4_OP_ERROR).
+ * Errors: NF4_ERR_NULL, _SHAPE, _ARG, _ALIGN, _WORKSPACE, _HIP.
+ */
+nf4_status nf4_layer_error(const float *W, int64_t rows, int64_t cols, int32_t block,
+                           int32_t dq_group, double *err_dev, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/*
+ * The protected set of AQLoRA's precision allocation (section 3.2): indices
+ * of the k largest of n errors (device double[n]), largest first, equal
+ * errors ordered by lower index, written to device int32 idx_dev[k].
+ * 0 <= k <= n <= 65536.  Errors: NF4_ERR_NULL, _SHAPE, _ALIGN, _HIP.
+ */
+nf4_status nf4_topk(const double *err_dev, int32_t n, int32_t k, int32_t *idx_dev, void *stream);
+
+/*
+ * Protection count for a budget rho over n linears: round-half-up(rho * n)
+ * (AQLoRA section 3.2; K = 29 at rho = .2 over 144 linears).  Host only;
+ * returns -1 for rho outside [0, 1] or n < 0.
+ */
+int32_t nf4_protect_count(double rho, int32_t n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NF4LORA_H */

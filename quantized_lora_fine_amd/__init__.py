@@ -1,0 +1,218 @@
+"""Python binding of libnf4lora (the NF4-LoRA linear layer on MI355X).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  torch supplies device memory and the current stream; tensors are
+passed as raw device pointers.  There is no fallback: if the shared library
+is missing this module raises on import, and every call checks the status
+the library returns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnf4lora.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libnf4lora.so not found at {LIB_PATH}; build it with `python -m quantized_lora_fine_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_WORKSPACE, NF4_ERR_ALIAS, NF4_ERR_HIP, NF4_ERR_ARG = range(8)
+NF4_OP_FWD, NF4_OP_BWD, NF4_OP_ERROR = 1, 2, 3
+BLOCK = 64
+DQ_GROUP = 256
+
+
+class _NF4Tensor(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("block", ctypes.c_int32),
+                ("dq_group", ctypes.c_int32), ("codes", ctypes.c_void_p), ("absmax", ctypes.c_void_p),
+                ("dq_scale", ctypes.c_void_p)]
+
+
+_vp, _i64, _i32, _sz, _f32, _f64 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t,
+                                    ctypes.c_float, ctypes.c_double)
+_T = ctypes.POINTER(_NF4Tensor)
+_SIGS = {
+    "nf4_abi_version": ([], ctypes.c_int),
+    "nf4_status_str": ([ctypes.c_int], ctypes.c_char_p),
+    "nf4_code_table": ([ctypes.POINTER(ctypes.c_float)], None),
+    "nf4_tensor_bytes": ([_i64, _i64, _i32, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz), ctypes.POINTER(_sz)],
+                         ctypes.c_int),
+    "nf4_quantize": ([_vp, _T, _vp], ctypes.c_int),
+    "nf4_dequantize": ([_T, _vp, _i32, _vp], ctypes.c_int),
+    "nf4_workspace_bytes": ([_i32, _i64, _i64, _i64, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
+    "nf4lora_fwd": ([_T, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "nf4lora_bwd": ([_T, _vp, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "nf4_layer_error": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "nf4_topk": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
+    "nf4_protect_count": ([_f64, _i32], _i32),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+EXPORTS = tuple(_SIGS)
+
+
+class NF4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_str(status)} ({status})")
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != NF4_OK:
+        raise NF4Error(status, where)
+
+
+def abi_version() -> int:
+    return _lib.nf4_abi_version()
+
+
+def status_str(status: int) -> str:
+    return _lib.nf4_status_str(int(status)).decode()
+
+
+def code_table() -> torch.Tensor:
+    out = (ctypes.c_float * 16)()
+    _lib.nf4_code_table(out)
+    return torch.tensor(list(out), dtype=torch.float32)
+
+
+def tensor_bytes(rows: int, cols: int, dq_group: int = 0, block: int = BLOCK):
+    c, a, d = _sz(), _sz(), _sz()
+    _check(_lib.nf4_tensor_bytes(rows, cols, block, dq_group, ctypes.byref(c), ctypes.byref(a), ctypes.byref(d)),
+           "nf4_tensor_bytes")
+    return c.value, a.value, d.value
+
+
+def workspace_bytes(op: int, M: int, rows: int, cols: int, r: int) -> int:
+    b = _sz()
+    _check(_lib.nf4_workspace_bytes(op, M, rows, cols, r, ctypes.byref(b)), "nf4_workspace_bytes")
+    return b.value
+
+
+def protect_count(rho: float, n: int) -> int:
+    return int(_lib.nf4_protect_count(float(rho), int(n)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _u16(t: torch.Tensor) -> torch.Tensor:
+    assert t.dtype == torch.bfloat16 and t.is_cuda and t.is_contiguous(), "expected a contiguous cuda bf16 tensor"
+    return t
+
+
+class NF4Weight:
+    """A quantized weight: the three device buffers plus the C descriptor."""
+
+    def __init__(self, rows: int, cols: int, dq_group: int = 0, device="cuda"):
+        cb, ab, db = tensor_bytes(rows, cols, dq_group)
+        self.rows, self.cols, self.dq_group = rows, cols, dq_group
+        self.codes = torch.empty(max(cb, 1), dtype=torch.uint8, device=device)
+        self.absmax = torch.empty(max(ab, 1), dtype=torch.uint8, device=device)
+        self.dq_scale = torch.empty(max(db, 1), dtype=torch.uint8, device=device) if dq_group else None
+        self.desc = _NF4Tensor(rows, cols, BLOCK, dq_group, self.codes.data_ptr(), self.absmax.data_ptr(),
+                               self.dq_scale.data_ptr() if dq_group else None)
+        self._cb, self._ab, self._db = cb, ab, db
+
+    @property
+    def absmax_f32(self) -> torch.Tensor:
+        return self.absmax[:self._ab].view(torch.float32)
+
+    @property
+    def c8(self) -> torch.Tensor:
+        return self.absmax[:self._ab]
+
+    @property
+    def dq_step(self) -> torch.Tensor:
+        return self.dq_scale[:self._db].view(torch.float32)
+
+    @property
+    def packed_codes(self) -> torch.Tensor:
+        return self.codes[:self._cb]
+
+
+def quantize(W: torch.Tensor, dq_group: int = 0) -> NF4Weight:
+    """nf4_quantize of a cuda fp32 [rows][cols] tensor."""
+    assert W.dtype == torch.float32 and W.is_cuda and W.is_contiguous() and W.dim() == 2
+    q = NF4Weight(W.shape[0], W.shape[1], dq_group, W.device)
+    _check(_lib.nf4_quantize(_ptr(W), ctypes.byref(q.desc), _stream()), "nf4_quantize")
+    return q
+
+
+def dequantize(q: NF4Weight, bf16: bool = False) -> torch.Tensor:
+    out = torch.empty(q.rows, q.cols, dtype=torch.bfloat16 if bf16 else torch.float32, device=q.codes.device)
+    _check(_lib.nf4_dequantize(ctypes.byref(q.desc), _ptr(out), 1 if bf16 else 0, _stream()), "nf4_dequantize")
+    return out
+
+
+def workspace(op: int, M: int, q: NF4Weight, r: int) -> torch.Tensor:
+    n = workspace_bytes(op, M, q.rows, q.cols, r)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=q.codes.device)
+
+
+def fwd(q: NF4Weight, X: torch.Tensor, L1: torch.Tensor, L2: torch.Tensor, s: float, want_T: bool = True,
+        ws: torch.Tensor | None = None, out: torch.Tensor | None = None, T_out: torch.Tensor | None = None):
+    """nf4lora_fwd: returns (Y bf16 [M][o], T bf16 [M][r] or None)."""
+    M, r = X.shape[0], L1.shape[1]
+    Y = out if out is not None else torch.empty(M, q.rows, dtype=torch.bfloat16, device=X.device)
+    T = T_out if T_out is not None else (
+        torch.empty(M, r, dtype=torch.bfloat16, device=X.device) if want_T else None)
+    if ws is None:
+        ws = workspace(NF4_OP_FWD, M, q, r)
+    _check(_lib.nf4lora_fwd(ctypes.byref(q.desc), _ptr(_u16(X)), M, _ptr(_u16(L1)), _ptr(_u16(L2)), r, float(s),
+                            _ptr(Y), _ptr(T), _ptr(ws), ws.numel(), _stream()), "nf4lora_fwd")
+    return Y, T
+
+
+def bwd(q: NF4Weight, X: torch.Tensor, dY: torch.Tensor, L1: torch.Tensor, L2: torch.Tensor, s: float,
+        T: torch.Tensor | None = None, want_dX: bool = True, ws: torch.Tensor | None = None, outs=None):
+    """nf4lora_bwd: returns (dX bf16 [M][h] or None, dL1 fp32 [h][r], dL2 fp32 [r][o])."""
+    M, r = X.shape[0], L1.shape[1]
+    if outs is None:
+        dX = torch.empty(M, q.cols, dtype=torch.bfloat16, device=X.device) if want_dX else None
+        dL1 = torch.empty(q.cols, r, dtype=torch.float32, device=X.device)
+        dL2 = torch.empty(r, q.rows, dtype=torch.float32, device=X.device)
+    else:
+        dX, dL1, dL2 = outs
+    if ws is None:
+        ws = workspace(NF4_OP_BWD, M, q, r)
+    _check(_lib.nf4lora_bwd(ctypes.byref(q.desc), _ptr(_u16(X)), _ptr(_u16(dY)), M, _ptr(_u16(L1)), _ptr(_u16(L2)),
+                            r, float(s), _ptr(T), _ptr(dX), _ptr(dL1), _ptr(dL2), _ptr(ws), ws.numel(), _stream()),
+           "nf4lora_bwd")
+    return dX, dL1, dL2
+
+
+def layer_error(W: torch.Tensor, dq_group: int = 0, out: torch.Tensor | None = None,
+                ws: torch.Tensor | None = None) -> torch.Tensor:
+    """nf4_layer_error: a cuda float64 tensor of shape [1] (no host sync)."""
+    assert W.dtype == torch.float32 and W.is_cuda and W.is_contiguous() and W.dim() == 2
+    rows, cols = W.shape
+    err = out if out is not None else torch.empty(1, dtype=torch.float64, device=W.device)
+    if ws is None:
+        n = workspace_bytes(NF4_OP_ERROR, 0, rows, cols, 1)
+        ws = torch.empty(n, dtype=torch.uint8, device=W.device)
+    _check(_lib.nf4_layer_error(_ptr(W), rows, cols, BLOCK, dq_group, _ptr(err), _ptr(ws), ws.numel(), _stream()),
+           "nf4_layer_error")
+    return err
+
+
+def topk(errors: torch.Tensor, k: int) -> torch.Tensor:
+    """nf4_topk over a cuda float64 vector: int32 indices, largest first, ties to the lower index."""
+    assert errors.dtype == torch.float64 and errors.is_cuda and errors.is_contiguous()
+    idx = torch.empty(max(k, 1), dtype=torch.int32, device=errors.device)
+    _check(_lib.nf4_topk(_ptr(errors), errors.numel(), k, _ptr(idx), _stream()), "nf4_topk")
+    return idx[:k]

@@ -1,0 +1,391 @@
+// C ABI of libnf4lora: argument validation, workspace planning and the
+// launch sequence of each entry point.  See include/nf4lora.h for the
+// contract of every function.
+#include "nf4lora.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "launch.hpp"
+
+using namespace nf4k;
+
+namespace {
+
+constexpr int64_t kBlock = 64;
+constexpr int64_t kGroup = 256;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+Range rng(const void* p, size_t bytes) { return Range{(uintptr_t)p, (uintptr_t)p + bytes}; }
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+int32_t round16(int32_t r) { return (r + 15) / 16 * 16; }
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+nf4_status hip_status(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ERR_HIP; }
+
+#define NF4_TRY(expr)                    \
+  do {                                   \
+    hipError_t e_ = (expr);              \
+    if (e_ != hipSuccess) return NF4_ERR_HIP; \
+  } while (0)
+
+// Sizes of the three buffers of a quantized tensor.
+void tensor_sizes(int64_t rows, int64_t cols, int32_t dq, size_t* codes, size_t* absmax, size_t* dqs) {
+  const int64_t n = rows * cols;
+  const int64_t nb = n / kBlock;
+  *codes = (size_t)(n / 2);
+  if (dq == 0) {
+    *absmax = (size_t)(4 * nb);
+    *dqs = 0;
+  } else {
+    *absmax = (size_t)nb;
+    *dqs = (size_t)(4 * ((nb + kGroup - 1) / kGroup));
+  }
+}
+
+nf4_status check_shape(int64_t rows, int64_t cols, int32_t block, int32_t dq) {
+  if (block != kBlock) return NF4_ERR_ARG;
+  if (dq != 0 && dq != kGroup) return NF4_ERR_ARG;
+  if (rows < 0 || cols < 0) return NF4_ERR_SHAPE;
+  if (cols % kBlock != 0) return NF4_ERR_SHAPE;
+  if (rows > 0 && cols > (((int64_t)1 << 40) / rows)) return NF4_ERR_SHAPE;
+  return NF4_OK;
+}
+
+nf4_status check_tensor(const nf4_tensor* q) {
+  if (!q) return NF4_ERR_NULL;
+  nf4_status st = check_shape(q->rows, q->cols, q->block, q->dq_group);
+  if (st != NF4_OK) return st;
+  if (q->rows * q->cols > 0) {
+    if (!q->codes || !q->absmax) return NF4_ERR_NULL;
+    if (q->dq_group && !q->dq_scale) return NF4_ERR_NULL;
+    if (!aligned16(q->codes) || !aligned16(q->absmax)) return NF4_ERR_ALIGN;
+    if (q->dq_group && !aligned16(q->dq_scale)) return NF4_ERR_ALIGN;
+  }
+  return NF4_OK;
+}
+
+// ---------------------------------------------------------------------------
+// workspace plans
+// ---------------------------------------------------------------------------
+struct FwdPlan {
+  int32_t RP;
+  int ks, kr;
+  size_t off_l1t, off_l2t, off_ts, off_part, total;
+};
+
+FwdPlan plan_fwd(int64_t M, int64_t o, int64_t h, int32_t r) {
+  FwdPlan p;
+  p.RP = round16(r);
+  plan_nt(M, (int)h, &p.ks, &p.kr);
+  size_t off = 0;
+  p.off_l1t = off;
+  off += align256((size_t)p.RP * h * 2);
+  p.off_l2t = off;
+  off += align256((size_t)o * p.RP * 2);
+  p.off_ts = off;
+  off += align256((size_t)M * p.RP * 2);
+  p.off_part = off;
+  off += align256((size_t)p.ks * M * p.RP * 4);
+  p.total = off;
+  return p;
+}
+
+struct BwdPlan {
+  int32_t RP;
+  int ks_t, kr_t, ks_g, kr_g, ms2, ms1;
+  int64_t mr2, mr1;
+  size_t off_l1t, off_l1p, off_l2p, off_tb, off_g, off_pnt, off_p2, off_p1, total;
+};
+
+BwdPlan plan_bwd(int64_t M, int64_t o, int64_t h, int32_t r) {
+  BwdPlan p;
+  p.RP = round16(r);
+  plan_nt(M, (int)h, &p.ks_t, &p.kr_t);
+  plan_nt(M, (int)o, &p.ks_g, &p.kr_g);
+  plan_tn(M, (int)o, &p.ms2, &p.mr2);
+  plan_tn(M, (int)h, &p.ms1, &p.mr1);
+  const int ksmax = p.ks_t > p.ks_g ? p.ks_t : p.ks_g;
+  size_t off = 0;
+  p.off_l1t = off;
+  off += align256((size_t)p.RP * h * 2);
+  p.off_l1p = off;
+  off += align256((size_t)h * p.RP * 2);
+  p.off_l2p = off;
+  off += align256((size_t)p.RP * o * 2);
+  p.off_tb = off;
+  off += align256((size_t)M * p.RP * 2);
+  p.off_g = off;
+  off += align256((size_t)M * p.RP * 2);
+  p.off_pnt = off;
+  off += align256((size_t)ksmax * M * p.RP * 4);
+  p.off_p2 = off;
+  off += align256((size_t)p.ms2 * p.RP * o * 4);
+  p.off_p1 = off;
+  off += align256((size_t)p.ms1 * p.RP * h * 4);
+  p.total = off;
+  return p;
+}
+
+size_t error_ws(int64_t rows, int64_t cols) {
+  const int64_t nb = rows * cols / kBlock;
+  const int64_t ng = (nb + kGroup - 1) / kGroup;
+  return align256((size_t)(ng > 0 ? ng : 1) * 16);
+}
+
+nf4_status check_layer(const nf4_tensor* W, int64_t M, int32_t r) {
+  nf4_status st = check_tensor(W);
+  if (st != NF4_OK) return st;
+  if (W->rows % kBlock != 0 || W->rows <= 0 || W->cols <= 0) return NF4_ERR_SHAPE;
+  if (W->rows > INT32_MAX / 2 || W->cols > INT32_MAX / 2) return NF4_ERR_SHAPE;
+  if (M < 0 || M > ((int64_t)1 << 31)) return NF4_ERR_SHAPE;
+  if (r < 1 || r > 256) return NF4_ERR_SHAPE;
+  return NF4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nf4_abi_version(void) { return NF4LORA_ABI_VERSION; }
+
+const char* nf4_status_str(int s) {
+  switch (s) {
+    case NF4_OK: return "NF4_OK";
+    case NF4_ERR_NULL: return "NF4_ERR_NULL: a required pointer is NULL";
+    case NF4_ERR_SHAPE: return "NF4_ERR_SHAPE: a size is out of range or the sizes disagree";
+    case NF4_ERR_ALIGN: return "NF4_ERR_ALIGN: a device pointer is not 16-byte aligned";
+    case NF4_ERR_WORKSPACE: return "NF4_ERR_WORKSPACE: workspace missing or too small";
+    case NF4_ERR_ALIAS: return "NF4_ERR_ALIAS: an output overlaps an input";
+    case NF4_ERR_HIP: return "NF4_ERR_HIP: a HIP call or kernel launch failed";
+    case NF4_ERR_ARG: return "NF4_ERR_ARG: unsupported option";
+    default: return "unknown nf4_status";
+  }
+}
+
+void nf4_code_table(float out[16]) {
+  if (!out) return;
+  const NF4Consts& c = nf4_consts();
+  std::memcpy(out, c.table, sizeof(c.table));
+}
+
+nf4_status nf4_tensor_bytes(int64_t rows, int64_t cols, int32_t block, int32_t dq_group, size_t* codes_bytes,
+                            size_t* absmax_bytes, size_t* dq_scale_bytes) {
+  nf4_status st = check_shape(rows, cols, block, dq_group);
+  if (st != NF4_OK) return st;
+  size_t c, a, d;
+  tensor_sizes(rows, cols, dq_group, &c, &a, &d);
+  if (codes_bytes) *codes_bytes = c;
+  if (absmax_bytes) *absmax_bytes = a;
+  if (dq_scale_bytes) *dq_scale_bytes = d;
+  return NF4_OK;
+}
+
+nf4_status nf4_quantize(const float* W, const nf4_tensor* q, void* stream) {
+  nf4_status st = check_tensor(q);
+  if (st != NF4_OK) return st;
+  const int64_t n = q->rows * q->cols;
+  if (n == 0) return NF4_OK;
+  if (!W) return NF4_ERR_NULL;
+  if (!aligned16(W)) return NF4_ERR_ALIGN;
+  size_t cb, ab, db;
+  tensor_sizes(q->rows, q->cols, q->dq_group, &cb, &ab, &db);
+  const Range in = rng(W, (size_t)n * 4);
+  if (overlap(in, rng(q->codes, cb)) || overlap(in, rng(q->absmax, ab)) ||
+      (db && overlap(in, rng(q->dq_scale, db))) || overlap(rng(q->codes, cb), rng(q->absmax, ab)))
+    return NF4_ERR_ALIAS;
+  return hip_status(launch_quantize(W, n / kBlock, q->dq_group != 0, q->codes, q->absmax, q->dq_scale,
+                                    nf4_consts(), (hipStream_t)stream));
+}
+
+nf4_status nf4_dequantize(const nf4_tensor* q, void* W_out, int32_t out_is_bf16, void* stream) {
+  nf4_status st = check_tensor(q);
+  if (st != NF4_OK) return st;
+  const int64_t n = q->rows * q->cols;
+  if (n == 0) return NF4_OK;
+  if (!W_out) return NF4_ERR_NULL;
+  if (!aligned16(W_out)) return NF4_ERR_ALIGN;
+  size_t cb, ab, db;
+  tensor_sizes(q->rows, q->cols, q->dq_group, &cb, &ab, &db);
+  const Range out = rng(W_out, (size_t)n * (out_is_bf16 ? 2 : 4));
+  if (overlap(out, rng(q->codes, cb)) || overlap(out, rng(q->absmax, ab)) ||
+      (db && overlap(out, rng(q->dq_scale, db))))
+    return NF4_ERR_ALIAS;
+  return hip_status(launch_dequantize(q->codes, q->absmax, q->dq_scale, n, q->dq_group != 0, out_is_bf16 != 0,
+                                      W_out, nf4_consts(), (hipStream_t)stream));
+}
+
+nf4_status nf4_workspace_bytes(int32_t op, int64_t M, int64_t rows, int64_t cols, int32_t r, size_t* bytes) {
+  if (!bytes) return NF4_ERR_NULL;
+  if (op == NF4_OP_ERROR) {
+    nf4_status st = check_shape(rows, cols, kBlock, 0);
+    if (st != NF4_OK) return st;
+    *bytes = error_ws(rows, cols);
+    return NF4_OK;
+  }
+  if (op != NF4_OP_FWD && op != NF4_OP_BWD) return NF4_ERR_ARG;
+  if (rows <= 0 || cols <= 0 || rows % kBlock || cols % kBlock || M < 0 || r < 1 || r > 256) return NF4_ERR_SHAPE;
+  *bytes = (op == NF4_OP_FWD) ? plan_fwd(M, rows, cols, r).total : plan_bwd(M, rows, cols, r).total;
+  return NF4_OK;
+}
+
+nf4_status nf4lora_fwd(const nf4_tensor* W, const uint16_t* X, int64_t M, const uint16_t* L1, const uint16_t* L2,
+                       int32_t r, float s, uint16_t* Y, uint16_t* T_out, void* ws, size_t ws_bytes, void* stream) {
+  nf4_status st = check_layer(W, M, r);
+  if (st != NF4_OK) return st;
+  if (M == 0) return NF4_OK;
+  if (!X || !L1 || !L2 || !Y) return NF4_ERR_NULL;
+  if (!aligned16(X) || !aligned16(L1) || !aligned16(L2) || !aligned16(Y) || (T_out && !aligned16(T_out)))
+    return NF4_ERR_ALIGN;
+  const int64_t o = W->rows, h = W->cols;
+  const FwdPlan p = plan_fwd(M, o, h, r);
+  if (!ws) return NF4_ERR_WORKSPACE;
+  if (ws_bytes < p.total) return NF4_ERR_WORKSPACE;
+  if (!aligned16(ws)) return NF4_ERR_ALIGN;
+  size_t cb, ab, db;
+  tensor_sizes(o, h, W->dq_group, &cb, &ab, &db);
+  const Range ins[] = {rng(X, (size_t)M * h * 2), rng(L1, (size_t)h * r * 2), rng(L2, (size_t)r * o * 2),
+                       rng(W->codes, cb), rng(W->absmax, ab), rng(W->dq_scale, db)};
+  const Range outs[] = {rng(Y, (size_t)M * o * 2), rng(T_out, T_out ? (size_t)M * r * 2 : 0),
+                        rng(ws, p.total)};
+  for (const Range& a : outs) {
+    for (const Range& b : ins)
+      if (overlap(a, b)) return NF4_ERR_ALIAS;
+  }
+  if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2])) return NF4_ERR_ALIAS;
+
+  hipStream_t hs = (hipStream_t)stream;
+  uint8_t* w = (uint8_t*)ws;
+  uint16_t* l1t = (uint16_t*)(w + p.off_l1t);
+  uint16_t* l2t = (uint16_t*)(w + p.off_l2t);
+  uint16_t* ts = (uint16_t*)(w + p.off_ts);
+  float* part = (float*)(w + p.off_part);
+  // L1^T [RP][h] (rows >= r zero) and L2^T [o][RP] (columns >= r zero)
+  NF4_TRY(launch_pad_transpose(L1, 1, r, r, h, l1t, p.RP, h, hs));
+  NF4_TRY(launch_pad_transpose(L2, 1, o, o, r, l2t, o, p.RP, hs));
+  // T = X L1 (split K, fixed-order reduce) -> T_out (bf16) and s*T (bf16, padded)
+  NF4_TRY(launch_skinny_nt(X, l1t, M, (int)h, p.RP, part, p.ks, p.kr, hs));
+  NF4_TRY(launch_reduce_nt(part, M, p.RP, r, p.ks, 1.0f, T_out, r, s, ts, hs));
+  // Y = X w_hat^T + (s T) L2
+  NF4_TRY(launch_nf4_gemm(MODE_FWD, W->dq_group != 0, X, W->codes, W->absmax, W->dq_scale, ts, l2t, p.RP, Y, M,
+                          (int)o, (int)h, nf4_consts(), hs));
+  return NF4_OK;
+}
+
+nf4_status nf4lora_bwd(const nf4_tensor* W, const uint16_t* X, const uint16_t* dY, int64_t M, const uint16_t* L1,
+                       const uint16_t* L2, int32_t r, float s, const uint16_t* T, uint16_t* dX, float* dL1,
+                       float* dL2, void* ws, size_t ws_bytes, void* stream) {
+  nf4_status st = check_layer(W, M, r);
+  if (st != NF4_OK) return st;
+  if (!dL1 || !dL2) return NF4_ERR_NULL;
+  if (M > 0 && (!X || !dY || !L1 || !L2)) return NF4_ERR_NULL;
+  const int64_t o = W->rows, h = W->cols;
+  const BwdPlan p = plan_bwd(M, o, h, r);
+  if (!ws) return NF4_ERR_WORKSPACE;
+  if (ws_bytes < p.total) return NF4_ERR_WORKSPACE;
+  if (!aligned16(ws) || !aligned16(dL1) || !aligned16(dL2)) return NF4_ERR_ALIGN;
+  if (M > 0 && (!aligned16(X) || !aligned16(dY) || !aligned16(L1) || !aligned16(L2) || (T && !aligned16(T)) ||
+                (dX && !aligned16(dX))))
+    return NF4_ERR_ALIGN;
+  size_t cb, ab, db;
+  tensor_sizes(o, h, W->dq_group, &cb, &ab, &db);
+  const Range ins[] = {rng(X, (size_t)M * h * 2),     rng(dY, (size_t)M * o * 2),
+                       rng(L1, (size_t)h * r * 2),    rng(L2, (size_t)r * o * 2),
+                       rng(T, T ? (size_t)M * r * 2 : 0), rng(W->codes, cb),
+                       rng(W->absmax, ab),            rng(W->dq_scale, db)};
+  const Range outs[] = {rng(dX, dX ? (size_t)M * h * 2 : 0), rng(dL1, (size_t)h * r * 4),
+                        rng(dL2, (size_t)r * o * 4), rng(ws, p.total)};
+  for (const Range& a : outs) {
+    for (const Range& b : ins)
+      if (overlap(a, b)) return NF4_ERR_ALIAS;
+  }
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return NF4_ERR_ALIAS;
+
+  hipStream_t hs = (hipStream_t)stream;
+  uint8_t* w = (uint8_t*)ws;
+  if (M == 0) {
+    // empty token set: both adapter gradients are exactly zero
+    NF4_TRY(launch_reduce_tn((const float*)(w + p.off_p2), p.RP, r, (int)o, 0, s, 0, dL2, hs));
+    NF4_TRY(launch_reduce_tn((const float*)(w + p.off_p1), p.RP, r, (int)h, 0, 1.0f, 1, dL1, hs));
+    return NF4_OK;
+  }
+  uint16_t* l1t = (uint16_t*)(w + p.off_l1t);
+  uint16_t* l1p = (uint16_t*)(w + p.off_l1p);
+  uint16_t* l2p = (uint16_t*)(w + p.off_l2p);
+  uint16_t* tb = (uint16_t*)(w + p.off_tb);
+  uint16_t* g = (uint16_t*)(w + p.off_g);
+  float* pnt = (float*)(w + p.off_pnt);
+  float* p2 = (float*)(w + p.off_p2);
+  float* p1 = (float*)(w + p.off_p1);
+
+  // adapters in the layouts the products read: L1 [h][RP], L2 [RP][o]
+  NF4_TRY(launch_pad_transpose(L1, r, 1, h, r, l1p, h, p.RP, hs));
+  NF4_TRY(launch_pad_transpose(L2, o, 1, r, o, l2p, p.RP, o, hs));
+  const uint16_t* tsrc = T;
+  int ldt = r;
+  if (!T) {
+    NF4_TRY(launch_pad_transpose(L1, 1, r, r, h, l1t, p.RP, h, hs));
+    NF4_TRY(launch_skinny_nt(X, l1t, M, (int)h, p.RP, pnt, p.ks_t, p.kr_t, hs));
+    NF4_TRY(launch_reduce_nt(pnt, M, p.RP, r, p.ks_t, 1.0f, nullptr, 0, 1.0f, tb, hs));
+    tsrc = tb;
+    ldt = p.RP;
+  }
+  // G = s dY L2^T  (bf16 [M][RP])
+  NF4_TRY(launch_skinny_nt(dY, l2p, M, (int)o, p.RP, pnt, p.ks_g, p.kr_g, hs));
+  NF4_TRY(launch_reduce_nt(pnt, M, p.RP, r, p.ks_g, 1.0f, nullptr, 0, s, g, hs));
+  // dL2 = s T^T dY  ([r][o]),  dL1 = X^T G  (stored [h][r])
+  NF4_TRY(launch_skinny_tn(tsrc, ldt, r, dY, M, (int)o, p.RP, p2, p.ms2, p.mr2, hs));
+  NF4_TRY(launch_reduce_tn(p2, p.RP, r, (int)o, p.ms2, s, 0, dL2, hs));
+  NF4_TRY(launch_skinny_tn(g, p.RP, r, X, M, (int)h, p.RP, p1, p.ms1, p.mr1, hs));
+  NF4_TRY(launch_reduce_tn(p1, p.RP, r, (int)h, p.ms1, 1.0f, 1, dL1, hs));
+  // dX = dY w_hat + G L1^T
+  if (dX) {
+    NF4_TRY(launch_nf4_gemm(MODE_DX, W->dq_group != 0, dY, W->codes, W->absmax, W->dq_scale, g, l1p, p.RP, dX, M,
+                            (int)h, (int)o, nf4_consts(), hs));
+  }
+  return NF4_OK;
+}
+
+nf4_status nf4_layer_error(const float* W, int64_t rows, int64_t cols, int32_t block, int32_t dq_group,
+                           double* err_dev, void* ws, size_t ws_bytes, void* stream) {
+  nf4_status st = check_shape(rows, cols, block, dq_group);
+  if (st != NF4_OK) return st;
+  if (!err_dev) return NF4_ERR_NULL;
+  const int64_t n = rows * cols;
+  if (n > 0 && !W) return NF4_ERR_NULL;
+  if (!ws) return NF4_ERR_WORKSPACE;
+  const size_t need = error_ws(rows, cols);
+  if (ws_bytes < need) return NF4_ERR_WORKSPACE;
+  if ((W && !aligned16(W)) || !aligned16(ws) || !aligned16(err_dev)) return NF4_ERR_ALIGN;
+  const Range in = rng(W, (size_t)n * 4);
+  if (overlap(in, rng(ws, need)) || overlap(in, rng(err_dev, 8)) || overlap(rng(ws, need), rng(err_dev, 8)))
+    return NF4_ERR_ALIAS;
+  return hip_status(launch_error(W, n / kBlock, dq_group != 0, (double*)ws, err_dev, nf4_consts(),
+                                 (hipStream_t)stream));
+}
+
+nf4_status nf4_topk(const double* err_dev, int32_t n, int32_t k, int32_t* idx_dev, void* stream) {
+  if (n < 0 || k < 0 || k > n || n > 65536) return NF4_ERR_SHAPE;
+  if (k == 0) return NF4_OK;
+  if (!err_dev || !idx_dev) return NF4_ERR_NULL;
+  if (!aligned16(err_dev) || !aligned16(idx_dev)) return NF4_ERR_ALIGN;
+  if (overlap(rng(err_dev, (size_t)n * 8), rng(idx_dev, (size_t)k * 4))) return NF4_ERR_ALIAS;
+  return hip_status(launch_topk(err_dev, n, k, idx_dev, (hipStream_t)stream));
+}
+
+int32_t nf4_protect_count(double rho, int32_t n) {
+  if (!(rho >= 0.0 && rho <= 1.0) || n < 0) return -1;
+  return (int32_t)std::floor(rho * (double)n + 0.5);
+}
+
+}  // extern "C"

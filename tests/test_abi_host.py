@@ -1,0 +1,180 @@
+"""Host-side checks of the C ABI (no GPU): exports, the code table, sizes and argument validation.
+
+Every call here fails validation before the library touches HIP, so fake device
+addresses are safe: they are compared and range-checked, never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nf4lora.h")
+
+nf4 = pytest.importorskip("quantized_lora_fine_amd", reason="libnf4lora.so not built")
+lib = nf4._lib
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b(nf4\w*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_match_header():
+    names = header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(nf4.EXPORTS) == names
+
+
+def test_abi_version_and_status_strings():
+    assert nf4.abi_version() == 1
+    for s in range(8):
+        assert nf4.status_str(s)
+    assert "unknown" in nf4.status_str(99)
+
+
+def test_code_table_bit_exact():
+    lib_t = nf4.code_table().numpy().astype(np.float32)
+    assert np.array_equal(lib_t.view(np.uint32), oracle.nf4_table().view(np.uint32))
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 64), (512, 512), (4096, 4096), (11008, 4096), (28672, 8192),
+                                       (3, 192), (65_000_000_000 // 64, 64)])
+@pytest.mark.parametrize("dq", [0, 256])
+def test_tensor_bytes(rows, cols, dq):
+    assert nf4.tensor_bytes(rows, cols, dq) == oracle.storage_bytes(rows, cols, 64, dq)
+
+
+def test_protect_count():
+    assert nf4.protect_count(0.2, 144) == 29
+    assert nf4.protect_count(0.2, 280) == 56
+    assert nf4.protect_count(0.0, 10) == 0
+    assert nf4.protect_count(1.5, 10) == -1
+
+
+def test_workspace_sizes():
+    for op in (nf4.NF4_OP_FWD, nf4.NF4_OP_BWD):
+        a = nf4.workspace_bytes(op, 2048, 4096, 4096, 16)
+        b = nf4.workspace_bytes(op, 4096, 4096, 4096, 16)
+        assert 0 < a < b
+        assert a % 256 == 0
+    assert nf4.workspace_bytes(nf4.NF4_OP_ERROR, 0, 4096, 4096, 1) >= 16 * 1024
+    with pytest.raises(nf4.NF4Error):
+        nf4.workspace_bytes(9, 1, 64, 64, 1)
+    with pytest.raises(nf4.NF4Error):
+        nf4.workspace_bytes(nf4.NF4_OP_FWD, 1, 64, 64, 0)
+
+
+# ---------------------------------------------------------------------------
+# validation (fake device addresses; every call is rejected before any launch)
+# ---------------------------------------------------------------------------
+A = 0x10000000          # aligned fake addresses, far apart
+B = 0x20000000
+C = 0x30000000
+D = 0x40000000
+E = 0x50000000
+F = 0x60000000
+G = 0x70000000
+H = 0x80000000
+
+
+def desc(rows=64, cols=64, block=64, dq=0, codes=A, absmax=B, dqs=None):
+    return nf4._NF4Tensor(rows, cols, block, dq, codes, absmax, dqs)
+
+
+def st_quant(d, W=C):
+    return lib.nf4_quantize(ctypes.c_void_p(W), ctypes.byref(d) if d is not None else None, None)
+
+
+def test_quantize_validation():
+    assert st_quant(None) == nf4.NF4_ERR_NULL
+    assert st_quant(desc(block=32)) == nf4.NF4_ERR_ARG
+    assert st_quant(desc(dq=128, dqs=D)) == nf4.NF4_ERR_ARG
+    assert st_quant(desc(cols=100)) == nf4.NF4_ERR_SHAPE
+    assert st_quant(desc(rows=-1)) == nf4.NF4_ERR_SHAPE
+    assert st_quant(desc(codes=None)) == nf4.NF4_ERR_NULL
+    assert st_quant(desc(dq=256, dqs=None)) == nf4.NF4_ERR_NULL
+    assert st_quant(desc(), W=0) == nf4.NF4_ERR_NULL
+    assert st_quant(desc(codes=A + 8)) == nf4.NF4_ERR_ALIGN
+    assert st_quant(desc(), W=C + 4) == nf4.NF4_ERR_ALIGN
+    assert st_quant(desc(dq=256, dqs=D + 2)) == nf4.NF4_ERR_ALIGN
+    # codes inside the input weight
+    assert st_quant(desc(codes=C + 64)) == nf4.NF4_ERR_ALIAS
+    assert st_quant(desc(absmax=A + 16)) == nf4.NF4_ERR_ALIAS
+    # empty tensors are accepted without touching the device
+    assert st_quant(desc(rows=0)) == nf4.NF4_OK
+
+
+def test_dequantize_validation():
+    d = desc()
+    assert lib.nf4_dequantize(ctypes.byref(d), None, 0, None) == nf4.NF4_ERR_NULL
+    assert lib.nf4_dequantize(ctypes.byref(d), ctypes.c_void_p(C + 8), 0, None) == nf4.NF4_ERR_ALIGN
+    assert lib.nf4_dequantize(ctypes.byref(d), ctypes.c_void_p(A), 1, None) == nf4.NF4_ERR_ALIAS
+    assert lib.nf4_dequantize(ctypes.byref(desc(block=128)), ctypes.c_void_p(C), 0, None) == nf4.NF4_ERR_ARG
+
+
+def fwd_call(d, X=C, M=16, L1=D, L2=E, r=8, Y=F, T=G, ws=H, ws_bytes=1 << 30):
+    return lib.nf4lora_fwd(ctypes.byref(d) if d is not None else None, ctypes.c_void_p(X), M, ctypes.c_void_p(L1),
+                           ctypes.c_void_p(L2), r, 2.0, ctypes.c_void_p(Y), ctypes.c_void_p(T) if T else None,
+                           ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+
+
+def test_fwd_validation():
+    d = desc(rows=128, cols=128)
+    assert fwd_call(None) == nf4.NF4_ERR_NULL
+    assert fwd_call(desc(rows=100, cols=128)) == nf4.NF4_ERR_SHAPE     # rows % 64
+    assert fwd_call(d, r=0) == nf4.NF4_ERR_SHAPE
+    assert fwd_call(d, r=257) == nf4.NF4_ERR_SHAPE
+    assert fwd_call(d, M=-1) == nf4.NF4_ERR_SHAPE
+    assert fwd_call(d, X=0) == nf4.NF4_ERR_NULL
+    assert fwd_call(d, Y=0) == nf4.NF4_ERR_NULL
+    assert fwd_call(d, X=C + 2) == nf4.NF4_ERR_ALIGN
+    assert fwd_call(d, T=G + 8) == nf4.NF4_ERR_ALIGN
+    assert fwd_call(d, ws=0) == nf4.NF4_ERR_WORKSPACE
+    need = nf4.workspace_bytes(nf4.NF4_OP_FWD, 16, 128, 128, 8)
+    assert fwd_call(d, ws_bytes=need - 1) == nf4.NF4_ERR_WORKSPACE
+    assert fwd_call(d, Y=C) == nf4.NF4_ERR_ALIAS                          # Y == X
+    assert fwd_call(d, T=F + 64) == nf4.NF4_ERR_ALIAS                     # T inside Y
+    assert fwd_call(d, ws=A) == nf4.NF4_ERR_ALIAS                         # workspace over the codes
+    assert fwd_call(d, M=0) == nf4.NF4_OK                                 # empty batch: nothing to do
+
+
+def bwd_call(d, X=C, dY=D, M=16, L1=E, L2=F, r=8, T=None, dX=G, dL1=H, dL2=H + 0x1000000, ws=H + 0x2000000,
+             ws_bytes=1 << 30):
+    v = lambda p: ctypes.c_void_p(p) if p else None
+    return lib.nf4lora_bwd(ctypes.byref(d), v(X), v(dY), M, v(L1), v(L2), r, 2.0, v(T), v(dX), v(dL1), v(dL2),
+                           v(ws), ws_bytes, None)
+
+
+def test_bwd_validation():
+    d = desc(rows=128, cols=128)
+    assert bwd_call(d, dL1=0) == nf4.NF4_ERR_NULL
+    assert bwd_call(d, dY=0) == nf4.NF4_ERR_NULL
+    assert bwd_call(d, dL2=H + 0x1000004) == nf4.NF4_ERR_ALIGN
+    assert bwd_call(d, ws_bytes=16) == nf4.NF4_ERR_WORKSPACE
+    assert bwd_call(d, dX=C) == nf4.NF4_ERR_ALIAS
+    assert bwd_call(d, dL1=E) == nf4.NF4_ERR_ALIAS
+    assert bwd_call(d, T=G) == nf4.NF4_ERR_ALIAS                          # T overlaps dX
+    assert bwd_call(desc(rows=128, cols=96)) == nf4.NF4_ERR_SHAPE
+
+
+def test_error_and_topk_validation():
+    v = ctypes.c_void_p
+    assert lib.nf4_layer_error(v(C), 64, 64, 64, 0, None, v(D), 1 << 20, None) == nf4.NF4_ERR_NULL
+    assert lib.nf4_layer_error(v(C), 64, 65, 64, 0, v(E), v(D), 1 << 20, None) == nf4.NF4_ERR_SHAPE
+    assert lib.nf4_layer_error(v(C), 64, 64, 64, 7, v(E), v(D), 1 << 20, None) == nf4.NF4_ERR_ARG
+    assert lib.nf4_layer_error(v(C), 64, 64, 64, 0, v(E), None, 0, None) == nf4.NF4_ERR_WORKSPACE
+    assert lib.nf4_layer_error(v(C), 64, 64, 64, 0, v(E), v(D), 8, None) == nf4.NF4_ERR_WORKSPACE
+    assert lib.nf4_layer_error(v(C), 64, 64, 64, 0, v(C + 16), v(D), 1 << 20, None) == nf4.NF4_ERR_ALIAS
+    assert lib.nf4_topk(v(C), 10, 11, v(D), None) == nf4.NF4_ERR_SHAPE
+    assert lib.nf4_topk(v(C), 10, 3, None, None) == nf4.NF4_ERR_NULL
+    assert lib.nf4_topk(v(C), 10, 3, v(C + 16), None) == nf4.NF4_ERR_ALIAS
+    assert lib.nf4_topk(v(C), 10, 0, None, None) == nf4.NF4_OK

@@ -1,0 +1,264 @@
+"""HIP path against the CPU oracle, through the C ABI (needs an MI355X).
+
+Bar: bit-exact for codes, scales and dequantized weights; for Y, dX, dL1 and
+dL2 max |err| <= 2e-2 * max |ref| (bf16 operands, fp32 accumulation), plus a
+tighter relative-RMS check; layer error within 1e-6 relative.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+nf4 = pytest.importorskip("quantized_lora_fine_amd")
+
+DEV = "cuda"
+TOL_MAX = 2e-2
+TOL_RMS = 5e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev(a):
+    if isinstance(a, np.ndarray):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    return a.to(DEV).contiguous()
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check_close(name, got, want, tol_max=TOL_MAX, tol_rms=TOL_RMS):
+    g = f64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
+    w = np.asarray(want, np.float64)
+    assert g.shape == w.shape, (name, g.shape, w.shape)
+    ref = np.max(np.abs(w))
+    err = np.max(np.abs(g - w))
+    rms = np.sqrt(np.mean((g - w) ** 2)) / max(np.sqrt(np.mean(w ** 2)), 1e-300)
+    say(f"  {name}: max|err|/max|ref| = {err / max(ref, 1e-300):.2e}  rel-rms = {rms:.2e}")
+    assert err <= tol_max * ref, f"{name}: max|err| {err:.3e} > {tol_max} * {ref:.3e}"
+    if ref > 0:
+        assert rms <= tol_rms, f"{name}: relative rms {rms:.3e}"
+
+
+def check_quant(q, ref):
+    assert np.array_equal(q.packed_codes.cpu().numpy(), ref.packed), "codes"
+    if ref.dq_group:
+        assert np.array_equal(q.c8.cpu().numpy(), ref.c8), "c8"
+        assert np.array_equal(q.dq_step.cpu().numpy().view(np.uint32), ref.dq_scale.view(np.uint32)), "dq step"
+    else:
+        assert np.array_equal(q.absmax_f32.cpu().numpy().view(np.uint32), ref.absmax.view(np.uint32)), "absmax"
+
+
+# ---------------------------------------------------------------------------
+# quantize / dequantize
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dq", [0, 256])
+def test_quantize_c1(dq):
+    W = synth.layer_inputs(synth.C1)["W"]
+    q = nf4.quantize(dev(W), dq)
+    check_quant(q, oracle.quantize(W, 64, dq))
+
+
+def test_quantize_dequantize_c2():
+    W = synth.layer_weight(synth.C2)
+    q = nf4.quantize(dev(W), 256)
+    ref = oracle.quantize(W, 64, 256)
+    check_quant(q, ref)
+    wh = nf4.dequantize(q).cpu().numpy()
+    assert np.array_equal(wh.view(np.uint32), oracle.dequantize(ref).view(np.uint32))
+    whb = nf4.dequantize(q, bf16=True).cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(whb, oracle.dequantize_bf16_bits(ref))
+
+
+def edge_weights():
+    """Blocks that stress the encoder: exact ties, zero/subnormal/huge blocks, spikes, ragged groups."""
+    rng = np.random.default_rng(11)
+    t = oracle.nf4_table()
+    blocks = []
+    # exact midpoints at several scales (ties take the lower code)
+    for k in (0, -7, 9):
+        for j in range(15):
+            m = np.float32((np.float64(t[j]) + np.float64(t[j + 1])) / 2)
+            b = np.zeros(64, np.float32)
+            b[0] = np.float32(2.0 ** k)
+            b[1] = m * np.float32(2.0 ** k)
+            b[2] = -b[1]
+            b[3:] = rng.uniform(-1, 1, 61).astype(np.float32) * np.float32(2.0 ** k)
+            blocks.append(b)
+    # sweeps of +-8 ulp around every midpoint for a random scale
+    a = np.float32(0.0371)
+    for j in range(15):
+        m = np.float32((np.float64(t[j]) + np.float64(t[j + 1])) / 2)
+        xs = [m]
+        for _ in range(8):
+            xs.insert(0, np.nextafter(xs[0], np.float32(-2)))
+            xs.append(np.nextafter(xs[-1], np.float32(2)))
+        b = np.zeros(64, np.float32)
+        b[0] = a
+        b[1:1 + len(xs)] = np.array(xs, np.float32) * a
+        blocks.append(b)
+    blocks.append(np.zeros(64, np.float32))                                 # all zero
+    blocks.append(np.full(64, -0.0, np.float32))                             # negative zeros
+    sub = np.zeros(64, np.float32)
+    sub[:8] = np.array([1e-40, -3e-41, 7e-42, 1e-45, -1e-45, 2e-40, 0, 5e-39], np.float32)
+    blocks.append(sub)                                                       # subnormal block
+    blocks.append((rng.standard_normal(64) * 1e30).astype(np.float32))       # huge
+    blocks.append((rng.standard_normal(64) * 1e-30).astype(np.float32))      # tiny
+    spike = np.zeros(64, np.float32)
+    spike[17] = -3.5
+    blocks.append(spike)                                                     # single spike
+    blocks.append(np.full(64, 0.25, np.float32))                              # constant
+    while len(blocks) % 5:
+        blocks.append((rng.standard_normal(64) * 0.02).astype(np.float32))
+    return np.stack(blocks).reshape(5, -1)                                   # 5 rows, ragged group count
+
+
+@pytest.mark.parametrize("dq", [0, 256])
+def test_quantize_edges(dq):
+    W = edge_weights()
+    q = nf4.quantize(dev(W), dq)
+    ref = oracle.quantize(W, 64, dq)
+    check_quant(q, ref)
+    wh = nf4.dequantize(q).cpu().numpy()
+    assert np.array_equal(wh.view(np.uint32), oracle.dequantize(ref).view(np.uint32))
+
+
+@pytest.mark.parametrize("rows,cols,dq", [(1, 64, 0), (3, 64 * 100, 256), (7, 64 * 37, 256), (300, 64 * 9, 0)])
+def test_quantize_shapes(rows, cols, dq):
+    rng = np.random.default_rng(rows * 1000 + cols)
+    W = (rng.standard_t(4, (rows, cols)) * 0.03).astype(np.float32)
+    q = nf4.quantize(dev(W), dq)
+    ref = oracle.quantize(W, 64, dq)
+    check_quant(q, ref)
+    whb = nf4.dequantize(q, bf16=True).cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(whb, oracle.dequantize_bf16_bits(ref))
+
+
+# ---------------------------------------------------------------------------
+# error and top-K
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dq", [0, 256])
+def test_layer_error(dq):
+    for W in (synth.layer_inputs(synth.C1)["W"], edge_weights(),
+              (np.random.default_rng(3).standard_t(3, (640, 1280)) * 0.02).astype(np.float32)):
+        got = float(nf4.layer_error(dev(W), dq).cpu()[0])
+        want = oracle.layer_error(W, 64, dq)
+        say(f"  error dq={dq}: gpu {got:.12g} oracle {want:.12g}")
+        assert abs(got - want) <= 1e-6 * want
+    assert float(nf4.layer_error(dev(np.zeros((4, 128), np.float32)), dq).cpu()[0]) == 0.0
+
+
+def test_topk():
+    rng = np.random.default_rng(5)
+    for n, k in ((280, 8), (144, 29), (1000, 1000), (5, 1), (3000, 17)):
+        e = rng.integers(0, 40, n).astype(np.float64) / 13.0
+        got = nf4.topk(dev(e), k).cpu().numpy().tolist()
+        assert got == oracle.topk(e, k), (n, k)
+
+
+# ---------------------------------------------------------------------------
+# forward / backward
+# ---------------------------------------------------------------------------
+
+def run_layer(d, s, dq, use_T=True, want_dX=True):
+    W = dev(d["W"])
+    q = nf4.quantize(W, dq)
+    X, L1, L2, dY = (dev(d[k]) for k in ("X", "L1", "L2", "dY"))
+    Y, T = nf4.fwd(q, X, L1, L2, s)
+    dX, dL1, dL2 = nf4.bwd(q, X, dY, L1, L2, s, T=T if use_T else None, want_dX=want_dX)
+    torch.cuda.synchronize()
+    return Y, T, dX, dL1, dL2
+
+
+def oracle_layer(d, s, dq):
+    wh = oracle.dequantize(oracle.quantize(d["W"], 64, dq))
+    Y, T = oracle.fwd(d["X"], wh, d["L1"], d["L2"], s)
+    dX, dL1, dL2, _ = oracle.bwd(d["X"], d["dY"], wh, d["L1"], d["L2"], s)
+    return Y, T, dX, dL1, dL2
+
+
+def check_layer(d, s, dq):
+    Y, T, dX, dL1, dL2 = run_layer(d, s, dq)
+    Yr, Tr, dXr, dL1r, dL2r = oracle_layer(d, s, dq)
+    check_close("T", T, Tr)
+    check_close("Y", Y, Yr)
+    check_close("dX", dX, dXr)
+    check_close("dL1", dL1, dL1r)
+    check_close("dL2", dL2, dL2r)
+
+
+def test_layer_c1():
+    d = synth.layer_inputs(synth.C1)
+    say("c1 512x512 r=8 M=128")
+    check_layer(d, d["s"], d["dq_group"])
+
+
+@pytest.mark.parametrize("M,o,h,r,dq,s", [
+    (1, 64, 64, 1, 0, 2.0),
+    (37, 320, 192, 17, 256, 0.5),
+    (300, 128, 576, 8, 0, 2.0),
+    (257, 384, 256, 64, 256, 2.0),
+    (129, 192, 128, 100, 0, 1.0 / 3.0),
+    (513, 704, 640, 16, 256, 2.0),
+])
+def test_layer_ragged(M, o, h, r, dq, s):
+    say(f"ragged M={M} o={o} h={h} r={r} dq={dq}")
+    d = synth.random_case(seed=M + o + h + r, rows=o, cols=h, M=M, r=r)
+    check_layer(d, s, dq)
+
+
+def test_layer_options_and_determinism():
+    d = synth.random_case(seed=21, rows=256, cols=320, M=200, r=16)
+    a = run_layer(d, 2.0, 256, use_T=True)
+    b = run_layer(d, 2.0, 256, use_T=False)
+    c = run_layer(d, 2.0, 256, use_T=True, want_dX=False)
+    e = run_layer(d, 2.0, 256, use_T=True)
+    for x, y in zip(a, e):                      # repeat: identical bits
+        assert torch.equal(x, y)
+    for i in (2, 3, 4):                         # T recomputed inside bwd: identical bits
+        assert torch.equal(a[i], b[i])
+    assert c[2] is None                          # early backward stop: no dX, same adapter grads
+    assert torch.equal(a[3], c[3]) and torch.equal(a[4], c[4])
+
+
+def test_adapter_zero_cases():
+    d = synth.random_case(seed=23, rows=192, cols=256, M=96, r=8)
+    d["L2"] = torch.zeros_like(d["L2"])
+    Y, T, dX, dL1, dL2 = run_layer(d, 2.0, 0)
+    Yr, _, dXr, _, dL2r = oracle_layer(d, 2.0, 0)
+    assert not torch.any(dL1)                   # G = 0 -> dL1 = 0 exactly
+    check_close("Y (L2=0)", Y, Yr)
+    check_close("dL2 (L2=0)", dL2, dL2r)
+    d = synth.random_case(seed=24, rows=192, cols=256, M=96, r=8)
+    d["L1"] = torch.zeros_like(d["L1"])
+    _, T, _, _, dL2 = run_layer(d, 2.0, 0)
+    assert not torch.any(T) and not torch.any(dL2)   # T = 0 -> dL2 = 0 exactly
+
+
+def test_empty_batch():
+    d = synth.random_case(seed=25, rows=128, cols=128, M=1, r=8)
+    q = nf4.quantize(dev(d["W"]), 0)
+    X = torch.empty(0, 128, dtype=torch.bfloat16, device=DEV)
+    L1, L2 = dev(d["L1"]), dev(d["L2"])
+    Y, T = nf4.fwd(q, X, L1, L2, 2.0)
+    assert Y.shape == (0, 128)
+    dL1 = torch.full((128, 8), 7.0, device=DEV)
+    dL2 = torch.full((8, 128), 7.0, device=DEV)
+    nf4.bwd(q, X, torch.empty(0, 128, dtype=torch.bfloat16, device=DEV), L1, L2, 2.0, outs=(None, dL1, dL2))
+    torch.cuda.synchronize()
+    assert not torch.any(dL1) and not torch.any(dL2)
+
+
+def test_layer_c2_full():
+    say("c2 4096x4096 r=16 M=2048, double quant")
+    d = synth.layer_inputs(synth.C2)
+    check_layer(d, d["s"], d["dq_group"])
