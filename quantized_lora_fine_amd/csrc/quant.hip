@@ -132,7 +132,8 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // reconstruction error, stage 1: per-group fp64 partial sums of (w - w_hat)^2
-// and w^2.  Same block/group mapping as k_quantize; the weights stay in
+// and w^2 (encode/decode in fp32 as the format defines, differences and
+// squares in fp64).  Same block/group mapping as k_quantize; the weights stay in
 // registers between the absmax, group-max and encode/decode steps.
 // ---------------------------------------------------------------------------
 template <bool DQ>
@@ -188,17 +189,16 @@ __global__ __launch_bounds__(256) void k_error_partial(const float* __restrict__
     float sc = m;
     if constexpr (DQ) sc = (S > 0.f) ? fminf(255.f, rintf(m / S)) * S : 0.f;
     const float w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-    float d2 = 0.f, w2 = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t c = (m > 0.f) ? nf4_encode(w4[e] / m, cst) : 7u;
       const float wh = tab[c] * sc;
-      const float d = w4[e] - wh;
-      d2 = fmaf(d, d, d2);
-      w2 = fmaf(w4[e], w4[e], w2);
+      // fp64 from here on: squares of fp32 weights can leave the fp32 range
+      const double wd = (double)w4[e];
+      const double d = wd - (double)wh;
+      dsum = fma(d, d, dsum);
+      wsum = fma(wd, wd, wsum);
     }
-    dsum += (double)d2;
-    wsum += (double)w2;
   }
   // fixed-order reduction: xor tree inside the wave, then waves 0..3 in order
 #pragma unroll
