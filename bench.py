@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the NF4-LoRA linear layer on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic
+input: NF4 quantize with double quantization, the per-layer reconstruction
+error, the top-K protected set, the fused forward and the backward (dX, dL1,
+dL2), on the Llama-7B attention projection: W 4096x4096 (NF4, blocks of 64,
+8-bit scales in groups of 256), 2048 tokens, rank 16, s = 2.
+
+`value` is the forward+backward algorithmic work F = 4 M h o + 6 M r (h + o)
+divided by the wall time of a whole step (quantize, error and top-K count as
+overhead).  The JSON line also carries the forward+backward time on its own,
+a per-op breakdown, the roofline of the dominant kernel timed with HIP events
+on the stream it is launched on, and the CPU oracle timed on this host.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused NF4-LoRA linear fwd+bwd TFLOP/s and % bf16 MFMA peak, 4096² r=16"
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_nf4_gemm_c2.json")
+GEMM_SOURCES = ["quantized_lora_fine_amd/csrc/gemm.hip", "quantized_lora_fine_amd/csrc/common.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def flops_fwd_bwd(M, h, o, r):
+    return 4.0 * M * h * o + 6.0 * M * r * (h + o)
+
+
+def cpu_baseline(d, s, steps=2):
+    """The oracle, as it stands, on this host: `steps` full c2 steps."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    best = None
+    for _ in range(steps):
+        t0 = time.perf_counter()
+        q = oracle.quantize(d["W"], 64, 256)
+        e = oracle.layer_error(d["W"], 64, 0)
+        oracle.topk([e], 1)
+        wh = oracle.dequantize(q)
+        oracle.fwd(d["X"], wh, d["L1"], d["L2"], s)
+        oracle.bwd(d["X"], d["dY"], wh, d["L1"], d["L2"], s)
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+    return best, threads
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (the layer runs on a single MI355X); "
+              "multi-GPU runs are not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantized_lora_fine_amd as nf4
+    import synth
+
+    cfg = synth.C2
+    M, o, h, r, s = cfg.M, cfg.rows, cfg.cols, cfg.r, cfg.s
+    d = synth.layer_inputs(cfg)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"# device {torch.cuda.get_device_name(0)}; workload {cfg.name}", file=sys.stderr, flush=True)
+
+    W = torch.from_numpy(d["W"]).to(dev)
+    X, L1, L2, dY = (d[k].to(dev).contiguous() for k in ("X", "L1", "L2", "dY"))
+    q = nf4.NF4Weight(o, h, 256, dev)
+    err = torch.empty(1, dtype=torch.float64, device=dev)
+    idx = torch.empty(1, dtype=torch.int32, device=dev)
+    ws_e = torch.empty(nf4.workspace_bytes(nf4.NF4_OP_ERROR, 0, o, h, 1), dtype=torch.uint8, device=dev)
+    ws_f = nf4.workspace(nf4.NF4_OP_FWD, M, q, r)
+    ws_b = nf4.workspace(nf4.NF4_OP_BWD, M, q, r)
+    Y = torch.empty(M, o, dtype=torch.bfloat16, device=dev)
+    T = torch.empty(M, r, dtype=torch.bfloat16, device=dev)
+    dX = torch.empty(M, h, dtype=torch.bfloat16, device=dev)
+    dL1 = torch.empty(h, r, dtype=torch.float32, device=dev)
+    dL2 = torch.empty(r, o, dtype=torch.float32, device=dev)
+
+    ops = [
+        ("quantize", lambda: nf4.quantize(W, 256, out=q)),
+        ("error", lambda: nf4.layer_error(W, 0, out=err, ws=ws_e)),
+        ("topk", lambda: nf4.topk(err, 1, out=idx)),
+        ("fwd", lambda: nf4.fwd(q, X, L1, L2, s, ws=ws_f, out=Y, T_out=T)),
+        ("bwd", lambda: nf4.bwd(q, X, dY, L1, L2, s, T=T, ws=ws_b, outs=(dX, dL1, dL2))),
+    ]
+
+    def step():
+        for _, f in ops:
+            f()
+
+    # ---- the timed region: exactly `steps` steps ----
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / max(args.steps, 1)
+    F = flops_fwd_bwd(M, h, o, r)
+    value = F / (ms_per_step * 1e-3) / 1e12
+    print(f"# timed {args.steps} steps: {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # ---- per-op breakdown: HIP events between the ops of each step ----
+    stream = torch.cuda.current_stream()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        for j, (_, f) in enumerate(ops):
+            f()
+            evs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    op_ms = {}
+    for j, (name, _) in enumerate(ops):
+        op_ms[name] = sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
+    fb_ms = op_ms["fwd"] + op_ms["bwd"]
+
+    # ---- roofline: the fused NF4 GEMMs alone, K launches between two events ----
+    RP = (r + 15) // 16 * 16
+    g = torch.Generator(device="cpu").manual_seed(0)
+    A2f = torch.zeros(M, RP, dtype=torch.bfloat16, device=dev)
+    A2f[:, :r] = (torch.randn(M, r, generator=g) * 0.5).to(torch.bfloat16).to(dev)
+    B2f = torch.zeros(o, RP, dtype=torch.bfloat16, device=dev)
+    B2f[:, :r] = L2.t()
+    A2b = torch.zeros(M, RP, dtype=torch.bfloat16, device=dev)
+    A2b[:, :r] = (torch.randn(M, r, generator=g) * 0.5).to(torch.bfloat16).to(dev)
+    B2b = torch.zeros(h, RP, dtype=torch.bfloat16, device=dev)
+    B2b[:, :r] = L1
+    Cf = torch.empty(M, o, dtype=torch.bfloat16, device=dev)
+    Cb = torch.empty(M, h, dtype=torch.bfloat16, device=dev)
+    kernels = {}
+    for name, fn, flops in (
+        ("nf4_gemm_fwd", lambda: nf4.matmul(q, X, False, A2f, B2f, out=Cf), 2.0 * M * h * o + 2.0 * M * r * o),
+        ("nf4_gemm_dx", lambda: nf4.matmul(q, dY, True, A2b, B2b, out=Cb), 2.0 * M * h * o + 2.0 * M * r * h),
+    ):
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / args.steps
+        kernels[name] = {"us": round(us, 3), "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+                         "flops_per_launch": flops}
+    # HBM-bound passes: algorithmic bytes per launch
+    n = o * h
+    q_bytes = 4 * n + n // 2 + n // 64 + 4 * (n // 64 // 256)
+    e_bytes = 4 * n
+    kernels["quantize_dq"] = {"us": round(1e3 * op_ms["quantize"], 3),
+                              "GBps": round(q_bytes / (op_ms["quantize"] * 1e-3) / 1e9, 1), "bytes": q_bytes}
+    kernels["layer_error"] = {"us": round(1e3 * op_ms["error"], 3),
+                              "GBps": round(e_bytes / (op_ms["error"] * 1e-3) / 1e9, 1), "bytes": e_bytes}
+
+    dom = max(("nf4_gemm_fwd", "nf4_gemm_dx"), key=lambda k: kernels[k]["us"])
+    ach = kernels[dom]["tflops"]
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_hash") == kernel_source_hash() and dom in tr.get("kernels", {}):
+            traffic = tr["kernels"][dom]["bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        traffic = None
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+
+    if args.calib_copy:
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        sec, threads = cpu_baseline(d, s)
+        cpu = {"value": round(F / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "sample": f"2 full steps of this workload on the CPU oracle (numpy; fp32 quantize, fp64 "
+                         f"products), best {sec:.2f} s/step", "host_cpus": os.cpu_count()}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama7b-attn-proj W 4096x4096 NF4 block 64 + 8-bit DQ/256, M=2048 tokens, r=16, s=2",
+                   "step": "quantize+error+topk+fwd+bwd", "tokens": M, "rank": r, "flops_fwd_bwd": F},
+        "fwd_bwd_ms": round(fb_ms, 5),
+        "fwd_bwd_tflops": round(F / (fb_ms * 1e-3) / 1e12, 2),
+        "fwd_bwd_pct_bf16_peak": round(100 * F / (fb_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "op_ms": {k: round(v, 5) for k, v in op_ms.items()},
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

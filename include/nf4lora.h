@@ -177,6 +177,21 @@ nf4_status nf4lora_bwd(const nf4_tensor *W, const uint16_t *X, const uint16_t *d
                        void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The fused NF4 matmul on its own (the base product inside nf4lora_fwd and
+ * nf4lora_bwd), with an optional low-rank term in the same output tile:
+ *   transpose = 0:  C [M][o] = A [M][h] * W_hat^T + A2 [M][R] * B2 [o][R]^T
+ *   transpose = 1:  C [M][h] = A [M][o] * W_hat   + A2 [M][R] * B2 [h][R]^T
+ * W_hat is dequantized to bf16 inside the kernel (equation (3) base term of
+ * the QLoRA blog, "1. NormalFloat": bf16 reconstruction before the matmul);
+ * fp32 accumulation, bf16 C.  R is a multiple of 16 in [0, 256] (pad the
+ * low-rank operands with zero columns); A2 and B2 may be NULL only when
+ * R == 0.  Shapes as nf4lora_fwd (W rows and cols multiples of 64).
+ * Errors: NF4_ERR_NULL, _SHAPE, _ARG, _ALIGN, _ALIAS, _HIP.
+ */
+nf4_status nf4_matmul(const nf4_tensor *W, int32_t transpose, const uint16_t *A, int64_t M,
+                      const uint16_t *A2, const uint16_t *B2, int32_t R, uint16_t *C, void *stream);
+
+/*
  * Per-layer NF4 reconstruction error of W (device fp32 [rows][cols]):
  *   e = sqrt(sum (w - w_hat)^2) / sqrt(sum w^2)   (0 when W is all zero),
  * w_hat from 64-weight blocks (dq_group 0) or with double quantization

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libnf4lora.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"libnf4lora.so not found at {LIB_PATH}; build it with `python -m quantized_lora_fine_amd.build`")
+        f"libnf4lora.so not found at {LIB_PATH}; build it with `python quantized_lora_fine_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -48,6 +48,7 @@ _SIGS = {
     "nf4_workspace_bytes": ([_i32, _i64, _i64, _i64, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
     "nf4lora_fwd": ([_T, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "nf4lora_bwd": ([_T, _vp, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "nf4_matmul": ([_T, _i32, _vp, _i64, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
     "nf4_layer_error": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _sz, _vp], ctypes.c_int),
     "nf4_topk": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
     "nf4_protect_count": ([_f64, _i32], _i32),
@@ -145,10 +146,10 @@ class NF4Weight:
         return self.codes[:self._cb]
 
 
-def quantize(W: torch.Tensor, dq_group: int = 0) -> NF4Weight:
-    """nf4_quantize of a cuda fp32 [rows][cols] tensor."""
+def quantize(W: torch.Tensor, dq_group: int = 0, out: NF4Weight | None = None) -> NF4Weight:
+    """nf4_quantize of a cuda fp32 [rows][cols] tensor (into `out` when given)."""
     assert W.dtype == torch.float32 and W.is_cuda and W.is_contiguous() and W.dim() == 2
-    q = NF4Weight(W.shape[0], W.shape[1], dq_group, W.device)
+    q = out if out is not None else NF4Weight(W.shape[0], W.shape[1], dq_group, W.device)
     _check(_lib.nf4_quantize(_ptr(W), ctypes.byref(q.desc), _stream()), "nf4_quantize")
     return q
 
@@ -210,9 +211,21 @@ def layer_error(W: torch.Tensor, dq_group: int = 0, out: torch.Tensor | None = N
     return err
 
 
-def topk(errors: torch.Tensor, k: int) -> torch.Tensor:
+def matmul(q: NF4Weight, A: torch.Tensor, transpose: bool = False, A2: torch.Tensor | None = None,
+           B2: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """nf4_matmul: A * W_hat^T (+ A2 * B2^T), or A * W_hat (+ ...) with transpose=True."""
+    M = A.shape[0]
+    R = 0 if A2 is None else A2.shape[1]
+    N = q.cols if transpose else q.rows
+    C = out if out is not None else torch.empty(M, N, dtype=torch.bfloat16, device=A.device)
+    _check(_lib.nf4_matmul(ctypes.byref(q.desc), 1 if transpose else 0, _ptr(_u16(A)), M,
+                           _ptr(A2), _ptr(B2), R, _ptr(C), _stream()), "nf4_matmul")
+    return C
+
+
+def topk(errors: torch.Tensor, k: int, out: torch.Tensor | None = None) -> torch.Tensor:
     """nf4_topk over a cuda float64 vector: int32 indices, largest first, ties to the lower index."""
     assert errors.dtype == torch.float64 and errors.is_cuda and errors.is_contiguous()
-    idx = torch.empty(max(k, 1), dtype=torch.int32, device=errors.device)
+    idx = out if out is not None else torch.empty(max(k, 1), dtype=torch.int32, device=errors.device)
     _check(_lib.nf4_topk(_ptr(errors), errors.numel(), k, _ptr(idx), _stream()), "nf4_topk")
     return idx[:k]

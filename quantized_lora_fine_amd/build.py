@@ -1,6 +1,8 @@
 """Builds libnf4lora.so in-tree with hipcc for gfx950.
 
-    python -m quantized_lora_fine_amd.build
+    python quantized_lora_fine_amd/build.py
+
+(run by path: importing the package would load the library being rebuilt)
 
 Every HIP source is compiled with packed fp32 vector ops disabled, without
 fast-math (IEEE fp32 division, denormals kept), then linked with the host

@@ -356,6 +356,30 @@ nf4_status nf4lora_bwd(const nf4_tensor* W, const uint16_t* X, const uint16_t* d
   return NF4_OK;
 }
 
+nf4_status nf4_matmul(const nf4_tensor* W, int32_t transpose, const uint16_t* A, int64_t M, const uint16_t* A2,
+                      const uint16_t* B2, int32_t R, uint16_t* C, void* stream) {
+  nf4_status st = check_tensor(W);
+  if (st != NF4_OK) return st;
+  if (W->rows % kBlock != 0 || W->rows <= 0 || W->cols <= 0) return NF4_ERR_SHAPE;
+  if (W->rows > INT32_MAX / 2 || W->cols > INT32_MAX / 2) return NF4_ERR_SHAPE;
+  if (transpose != 0 && transpose != 1) return NF4_ERR_ARG;
+  if (M < 0 || M > ((int64_t)1 << 31) || R < 0 || R > 256 || R % 16 != 0) return NF4_ERR_SHAPE;
+  if (M == 0) return NF4_OK;
+  if (!A || !C || (R > 0 && (!A2 || !B2))) return NF4_ERR_NULL;
+  if (!aligned16(A) || !aligned16(C) || (R > 0 && (!aligned16(A2) || !aligned16(B2)))) return NF4_ERR_ALIGN;
+  const int64_t o = W->rows, h = W->cols;
+  const int64_t K = transpose ? o : h, N = transpose ? h : o;
+  size_t cb, ab, db;
+  tensor_sizes(o, h, W->dq_group, &cb, &ab, &db);
+  const Range out = rng(C, (size_t)M * N * 2);
+  const Range ins[] = {rng(A, (size_t)M * K * 2), rng(A2, R ? (size_t)M * R * 2 : 0), rng(B2, R ? (size_t)N * R * 2 : 0),
+                       rng(W->codes, cb), rng(W->absmax, ab), rng(W->dq_scale, db)};
+  for (const Range& b : ins)
+    if (overlap(out, b)) return NF4_ERR_ALIAS;
+  return hip_status(launch_nf4_gemm(transpose ? MODE_DX : MODE_FWD, W->dq_group != 0, A, W->codes, W->absmax,
+                                    W->dq_scale, A2, B2, R, C, M, (int)N, (int)K, nf4_consts(), (hipStream_t)stream));
+}
+
 nf4_status nf4_layer_error(const float* W, int64_t rows, int64_t cols, int32_t block, int32_t dq_group,
                            double* err_dev, void* ws, size_t ws_bytes, void* stream) {
   nf4_status st = check_shape(rows, cols, block, dq_group);
