@@ -14,7 +14,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libnf4lora.so")
+# NF4LORA_LIB selects another build of the same library (e.g. a debug build)
+LIB_PATH = os.environ.get("NF4LORA_LIB") or os.path.join(_HERE, "libnf4lora.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

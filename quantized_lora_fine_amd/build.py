@@ -26,7 +26,10 @@ ARCH = os.environ.get("NF4LORA_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
-COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
+def _common(csrc):
+    return ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{csrc}", "-Wall", "-Wno-unused-function"]
+
+
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # per-source extra flags: the quantization kernels must round exactly as the
 # format defines (one rounding per multiply, no fused multiply-add across
@@ -45,27 +48,27 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, csrc: str = CSRC, out: str = LIB, build_dir: str = BUILD) -> str:
+    os.makedirs(build_dir, exist_ok=True)
     jobs = []
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
-        jobs.append([HIPCC, "-x", "hip", *COMMON, *DEVICE, *EXTRA.get(src, []), "-c",
-                     os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(build_dir, src + ".o")
+        jobs.append([HIPCC, "-x", "hip", *_common(csrc), *DEVICE, *EXTRA.get(src, []), "-c",
+                     os.path.join(csrc, src), "-o", obj])
     for src in CPP_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
-        jobs.append([HIPCC, *COMMON, "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(build_dir, src + ".o")
+        jobs.append([HIPCC, *_common(csrc), "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(csrc, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         outs = list(ex.map(_run, jobs))
     if verbose:
         for o in outs:
             if o.strip():
                 print(o)
-    objs = [os.path.join(BUILD, s + ".o") for s in HIP_SOURCES + CPP_SOURCES]
-    tmp = LIB + ".tmp"
+    objs = [os.path.join(build_dir, s + ".o") for s in HIP_SOURCES + CPP_SOURCES]
+    tmp = out + ".tmp"
     _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -15,16 +15,22 @@
 // dequantized W tile exists only in LDS: packed 4-bit codes and scales are
 // the only weight bytes read from HBM.
 //
-// Tiling: 256 x 128 output tile per 256-thread workgroup (4 wave64s, 2 x 2,
-// each wave 128 x 64 as 4 x 2 v_mfma_f32_32x32x16_bf16), K step 64 (one NF4
-// block per W row per step), double-buffered LDS.
-//   * A (X or dY) goes straight from global memory into LDS with
-//     buffer_load_dwordx4 ... lds, one K step ahead; rows past M read as zero
-//     through the buffer descriptor's range check, so the loop has no branches.
-//   * W codes and scales are loaded into registers two K steps ahead; while
-//     the MFMAs of step k run, the codes of step k+1 are dequantized into the
-//     other B buffer a quarter at a time between the K=16 MFMA groups, so the
-//     dequant VALU work hides under the matrix cores.
+// Tiling: 256 x 128 output tile per 512-thread workgroup, K step 64 (one NF4
+// block per W row per step), three LDS buffers each for A and the
+// dequantized B.  The eight wave64s split into two roles:
+//   * waves 0..3 (consumers) only read MFMA fragments from LDS and issue
+//     v_mfma_f32_32x32x16_bf16; they sit 2 x 2 over the tile, 128 x 64 each
+//     (4 x 2 accumulators), and read the next K=16 group's fragments while the
+//     current group's MFMAs run;
+//   * waves 4..7 (producers) copy A (X or dY) from global memory straight into
+//     LDS with buffer_load_dwordx4 ... lds two K steps ahead, fetch W codes and
+//     scales into registers three steps ahead, and dequantize the codes into
+//     the B buffer two steps ahead.  Their VALU work runs on the other wave
+//     slot of each SIMD, beside the consumers' MFMAs, instead of inside the
+//     MFMA instruction stream.
+//   One barrier per K step publishes tile s+2 and retires tile s-1, whose
+//   buffer is the next one written.  Rows past M read as zero through the
+//   buffer descriptor's range check, so the loop has no branches.
 //   * dequant: each code byte (two NF4 codes) indexes a 256-entry LDS table of
 //     fp32 value pairs; the pair is multiplied by the block scale and packed to
 //     bf16 with v_cvt_pk_bf16_f32 (round to nearest even), exactly the bf16 of
@@ -41,7 +47,7 @@ namespace nf4k {
 constexpr int GBM = 256;
 constexpr int GBN = 128;
 constexpr int GBK = 64;
-constexpr int GNT = 256;
+constexpr int GNT = 512;
 constexpr uint32_t kRsrcFlags = 0x00020000u;  // raw buffer, gfx9-family dword3
 constexpr uint32_t kOOB = 0x80000000u;        // an offset past every buffer's range
 
@@ -63,7 +69,7 @@ struct GemmArgs {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 7); }
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 3); }
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ swz(row)) << 4); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -72,20 +78,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 template <int MODE, bool DQ>
 __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
-  // separate arrays per buffer: the compiler then knows a direct-to-LDS load
-  // into one A buffer cannot alias fragment reads from the other, and does not
-  // wait for the next tile's loads before reading the current one
+  // three buffers each for A and the dequantized B: tile t lives in buffer t%3
   __shared__ __attribute__((aligned(16))) uint8_t As0[GBM * 128];
   __shared__ __attribute__((aligned(16))) uint8_t As1[GBM * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t As2[GBM * 128];
   __shared__ __attribute__((aligned(16))) uint8_t Bs0[GBN * 128];
   __shared__ __attribute__((aligned(16))) uint8_t Bs1[GBN * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs2[GBN * 128];
   __shared__ __attribute__((aligned(16))) float2 ptab[256];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
+  const int wave = tid >> 6;            // 0..7
+  const bool producer = wave >= 4;      // waves 4..7 load and dequantize, waves 0..3 multiply
+  const int ptid = tid - 256;           // producer thread id 0..255
+  const int wm = wave & 1;              // consumer wave tile (128 x 64)
+  const int wn = (wave >> 1) & 1;
 
   int lid = blockIdx.x;
   const int nwg = gridDim.x;
@@ -98,9 +106,12 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
   const int N = p.N;
   const int K = p.K;
   const int KT = K / GBK;
+  const int64_t arows = (M - m0) < GBM ? (M - m0) : GBM;
 
-  // byte -> (table[low nibble], table[high nibble]): element 2t sits in the low nibble
-  ptab[tid] = make_float2(cst.table[tid & 15], cst.table[tid >> 4]);
+  if (tid < 256) ptab[tid] = make_float2(cst.table[tid & 15], cst.table[tid >> 4]);
+
+  auto abuf = [&](int b) -> uint8_t* { return b == 0 ? As0 : b == 1 ? As1 : As2; };
+  auto bbuf = [&](int b) -> uint8_t* { return b == 0 ? Bs0 : b == 1 ? Bs1 : Bs2; };
 
   floatx16 acc[4][2];
 #pragma unroll
@@ -110,206 +121,228 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // ---- A: direct global -> LDS, 8 x 1 KiB per wave per K step ----
-  const int64_t arows = (M - m0) < GBM ? (M - m0) : GBM;
-  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.A + m0 * K, (uint32_t)(arows * K * 2));
-  // lane l of the wave's i-th instruction fills LDS row r = (wave*8+i)*8 + l/8,
-  // physical chunk l%8, i.e. logical chunk (l%8) ^ swz(r)
-  uint32_t a_voff[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = (wave * 8 + i) * 8 + (lane >> 3);
-    a_voff[i] = (uint32_t)(r * K * 2 + (((lane & 7) ^ swz(r)) << 4));
-  }
-  auto issue_A = [&](int kt, int buf) {
+  if (producer) {
+    // ================= producer waves =================
+    const int pw = wave - 4;
+    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.A + m0 * K, (uint32_t)(arows * K * 2));
+    uint32_t a_voff[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      uint8_t* dst = (buf ? As1 : As0) + (wave * 8 + i) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)dst, 16, a_voff[i] + kt * 128, 0, 0, 0);
+      const int r = (pw * 8 + i) * 8 + (lane >> 3);
+      a_voff[i] = (uint32_t)(r * K * 2 + (((lane & 7) ^ swz(r)) << 4));
     }
-  };
+    auto issue_A = [&](int kt, int b) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint8_t* dst = abuf(b) + (pw * 8 + i) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)dst, 16, a_voff[i] + kt * 128, 0, 0, 0);
+      }
+    };
+    // FWD: (n = ptid>>1, half = ptid&1): 32 consecutive codes of W row n0+n.
+    // DX : (og = ptid>>4, hc = ptid&15): W rows 4*og .. 4*og+3 of the step, columns n0+hc*8 .. +8.
+    __amdgpu_buffer_rsrc_t c_rsrc;
+    uint32_t c_voff[4], s_voff[4];
+    if constexpr (MODE == MODE_FWD) {
+      const int n = ptid >> 1;
+      const int nrows = (N - n0) < GBN ? (N - n0) : GBN;
+      c_rsrc = make_rsrc(p.codes + (int64_t)n0 * (K >> 1), (uint32_t)((int64_t)nrows * (K >> 1)));
+      c_voff[0] = (uint32_t)(n * (K >> 1) + (ptid & 1) * 16);
+      s_voff[0] = (uint32_t)(n0 + n) * (uint32_t)(K >> 6);
+    } else {
+      const int og = ptid >> 4;
+      const int hc = ptid & 15;
+      const bool ok = n0 + hc * 8 < N;
+      c_rsrc = make_rsrc(p.codes, (uint32_t)(p.nblocks * 32));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c_voff[i] = ok ? (uint32_t)((og * 4 + i) * (N >> 1) + ((n0 + hc * 8) >> 1)) : kOOB;
+        s_voff[i] = ok ? (uint32_t)((og * 4 + i) * (N >> 6) + ((n0 + hc * 8) >> 6)) : kOOB;
+      }
+    }
+    const __amdgpu_buffer_rsrc_t s_rsrc = make_rsrc(p.absmax, (uint32_t)(p.nblocks * (DQ ? 1 : 4)));
+    const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(p.dqs, (uint32_t)(DQ ? ((p.nblocks + 255) / 256) * 4 : 0));
 
-  // ---- W codes + scales into registers (two register sets, two steps ahead) ----
-  __amdgpu_buffer_rsrc_t c_rsrc, s_rsrc, q_rsrc;
-  uint32_t c_voff[4], s_voff[4];
-  if constexpr (MODE == MODE_FWD) {
-    // thread (n = tid>>1, half = tid&1): 32 consecutive codes of W row n0+n
-    const int n = tid >> 1;
-    const int nrows = (N - n0) < GBN ? (N - n0) : GBN;
-    c_rsrc = make_rsrc(p.codes + (int64_t)n0 * (K >> 1), (uint32_t)((int64_t)nrows * (K >> 1)));
-    c_voff[0] = (uint32_t)(n * (K >> 1) + (tid & 1) * 16);
-    s_voff[0] = (uint32_t)(n0 + n) * (uint32_t)(K >> 6);  // block index at kt = 0
+    u32x4 creg[2];
+    uint32_t sraw[2][4];
+    float sstep[2][4];
+    auto load_scale = [&](uint32_t blk, int set, int i) {
+      if constexpr (DQ) {
+        sraw[set][i] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, blk, 0, 0);
+        sstep[set][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(q_rsrc, (blk >> 8) * 4, 0, 0));
+      } else {
+        sraw[set][i] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, blk * 4, 0, 0);
+      }
+    };
+    auto scale = [&](int set, int i) -> float {
+      if constexpr (DQ) {
+        return (float)sraw[set][i] * sstep[set][i];
+      } else {
+        return __builtin_bit_cast(float, sraw[set][i]);
+      }
+    };
+    auto issue_W = [&](int kt, int set) {
+      if constexpr (MODE == MODE_FWD) {
+        creg[set] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, c_voff[0] + kt * 32, 0, 0);
+        load_scale(s_voff[0] + kt, set, 0);
+      } else {
+        const uint32_t drow = (uint32_t)kt * 64u * (uint32_t)(N >> 1);
+        const uint32_t dblk = (uint32_t)kt * 64u * (uint32_t)(N >> 6);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          creg[set][i] = __builtin_amdgcn_raw_buffer_load_b32(c_rsrc, c_voff[i] + drow, 0, 0);
+          load_scale(s_voff[i] + dblk, set, i);
+        }
+      }
+    };
+    constexpr int kWLoads = (MODE == MODE_FWD) ? (DQ ? 3 : 2) : (DQ ? 12 : 8);
+    constexpr int kWaitW = (kWLoads & 15) | ((kWLoads >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+    auto dequant = [&](int set, int b) {
+      uint8_t* dst = bbuf(b);
+      if constexpr (MODE == MODE_FWD) {
+        const float sc = scale(set, 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w = creg[set][q];
+          const float2 t0 = ptab[w & 0xFFu], t1 = ptab[(w >> 8) & 0xFFu], t2 = ptab[(w >> 16) & 0xFFu],
+                       t3 = ptab[w >> 24];
+          uint4 o;
+          o.x = pack_bf16x2(t0.x * sc, t0.y * sc);
+          o.y = pack_bf16x2(t1.x * sc, t1.y * sc);
+          o.z = pack_bf16x2(t2.x * sc, t2.y * sc);
+          o.w = pack_bf16x2(t3.x * sc, t3.y * sc);
+          *(uint4*)(dst + lds_off(ptid >> 1, (ptid & 1) * 4 + q)) = o;
+        }
+      } else {
+        const int og = ptid >> 4;
+        const int hc = ptid & 15;
+        float sc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] = scale(set, i);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float2 v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float2 t = ptab[(creg[set][i] >> (8 * q)) & 0xFFu];
+            v[i] = make_float2(t.x * sc[i], t.y * sc[i]);
+          }
+          const int row0 = hc * 8 + 2 * q;
+          uint2 e0, e1;
+          e0.x = pack_bf16x2(v[0].x, v[1].x);
+          e0.y = pack_bf16x2(v[2].x, v[3].x);
+          e1.x = pack_bf16x2(v[0].y, v[1].y);
+          e1.y = pack_bf16x2(v[2].y, v[3].y);
+          *(uint2*)(dst + row0 * 128 + (((og >> 1) ^ swz(row0)) << 4) + (og & 1) * 8) = e0;
+          *(uint2*)(dst + (row0 + 1) * 128 + (((og >> 1) ^ swz(row0 + 1)) << 4) + (og & 1) * 8) = e1;
+        }
+      }
+    };
+    // prologue: tiles 0 and 1 into buffers 0 and 1; W(2) into set 0
+    issue_A(0, 0);
+    issue_A(1, 1);
+    issue_W(0, 0);
+    issue_W(1, 1);
+    __syncthreads();  // (1) ptab
+    dequant(0, 0);
+    dequant(1, 1);
+    issue_W(2, 0);
+    __builtin_amdgcn_s_waitcnt(kWaitW);
+    __syncthreads();  // (2) tiles 0, 1 published
+    // step s: produce tile s+2 (A DMA into buffer (s+2)%3, dequant from set s%2),
+    // fetch the codes of tile s+3 into set (s+1)%2, then the step's barrier.
+    // Buffer (s+2)%3 held tile s-1, fully consumed before the previous barrier.
+    auto pstep = [&](int s, int j) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue_A(s + 2, (j + 2) % 3);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_W(s + 3, (j + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      dequant(j & 1, (j + 2) % 3);
+      __builtin_amdgcn_s_waitcnt(kWaitW);
+      __syncthreads();
+    };
+    int s = 0;
+    for (; s + 6 <= KT; s += 6) {
+      pstep(s, 0); pstep(s + 1, 1); pstep(s + 2, 2); pstep(s + 3, 3); pstep(s + 4, 4); pstep(s + 5, 5);
+    }
+    if (s < KT) pstep(s, 0);
+    if (s + 1 < KT) pstep(s + 1, 1);
+    if (s + 2 < KT) pstep(s + 2, 2);
+    if (s + 3 < KT) pstep(s + 3, 3);
+    if (s + 4 < KT) pstep(s + 4, 4);
+    __builtin_amdgcn_s_waitcnt(0);
   } else {
-    // thread (og = tid>>4, hc = tid&15): rows kt*64 + og*4 + i (i < 4), columns n0 + hc*8 .. +8
-    const int og = tid >> 4;
-    const int hc = tid & 15;
-    const bool ok = n0 + hc * 8 < N;
-    c_rsrc = make_rsrc(p.codes, (uint32_t)(p.nblocks * 32));
+    // ================= consumer waves: fragment reads and MFMAs only =================
+    struct Frags {
+      bf16x8 a[4], b[2];
+    };
+    auto load_frags = [&](int b, int kk, Frags& f) {
+      const uint8_t* Ab = abuf(b);
+      const uint8_t* Bb = bbuf(b);
+      const int chunk = kk * 2 + (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      c_voff[i] = ok ? (uint32_t)((og * 4 + i) * (N >> 1) + ((n0 + hc * 8) >> 1)) : kOOB;
-      s_voff[i] = ok ? (uint32_t)((og * 4 + i) * (N >> 6) + ((n0 + hc * 8) >> 6)) : kOOB;
-    }
-  }
-  s_rsrc = make_rsrc(p.absmax, (uint32_t)(p.nblocks * (DQ ? 1 : 4)));
-  q_rsrc = make_rsrc(p.dqs, (uint32_t)(DQ ? ((p.nblocks + 255) / 256) * 4 : 0));
-
-  u32x4 creg[2];
-  uint32_t sraw[2][4];   // fp32 absmax bits, or the 8-bit scale code
-  float sstep[2][4];     // double quant: the group's fp32 step
-  // The scale is formed where it is used (in the dequant), not here, so that
-  // nothing waits on these loads before the step that consumes them.
-  auto load_scale = [&](uint32_t blk, int set, int i) {
-    if constexpr (DQ) {
-      sraw[set][i] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, blk, 0, 0);
-      sstep[set][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(q_rsrc, (blk >> 8) * 4, 0, 0));
-    } else {
-      sraw[set][i] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, blk * 4, 0, 0);
-    }
-  };
-  auto scale = [&](int set, int i) -> float {
-    if constexpr (DQ) {
-      return (float)sraw[set][i] * sstep[set][i];
-    } else {
-      return __builtin_bit_cast(float, sraw[set][i]);
-    }
-  };
-  // Out-of-range rows/columns carry offsets >= 2^31, past every descriptor's
-  // range (all buffers are < 2 GiB), so their codes and scales read as 0.
-  auto issue_W = [&](int kt, int set) {
-    if constexpr (MODE == MODE_FWD) {
-      creg[set] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, c_voff[0] + kt * 32, 0, 0);
-      load_scale(s_voff[0] + kt, set, 0);
-    } else {
-      const uint32_t drow = (uint32_t)kt * 64u * (uint32_t)(N >> 1);
-      const uint32_t dblk = (uint32_t)kt * 64u * (uint32_t)(N >> 6);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        creg[set][i] = __builtin_amdgcn_raw_buffer_load_b32(c_rsrc, c_voff[i] + drow, 0, 0);
-        load_scale(s_voff[i] + dblk, set, i);
-      }
-    }
-  };
-  // vector-memory instructions issue_W emits (what may stay in flight at a step's end)
-  constexpr int kWLoads = (MODE == MODE_FWD) ? (DQ ? 3 : 2) : (DQ ? 12 : 8);
-  constexpr int kWaitW = (kWLoads & 15) | ((kWLoads >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-
-  // dequantize quarter q (0..3) of the B tile held in register set `set` into LDS buffer `buf`
-  auto dequant_quarter = [&](int set, int buf, int q) {
-    uint8_t* dst = buf ? Bs1 : Bs0;
-    if constexpr (MODE == MODE_FWD) {
-      const uint32_t w = creg[set][q];
-      const float sc = scale(set, 0);
-      const float2 t0 = ptab[w & 0xFFu], t1 = ptab[(w >> 8) & 0xFFu], t2 = ptab[(w >> 16) & 0xFFu],
-                   t3 = ptab[w >> 24];
-      uint4 o;
-      o.x = pack_bf16x2(t0.x * sc, t0.y * sc);
-      o.y = pack_bf16x2(t1.x * sc, t1.y * sc);
-      o.z = pack_bf16x2(t2.x * sc, t2.y * sc);
-      o.w = pack_bf16x2(t3.x * sc, t3.y * sc);
-      *(uint4*)(dst + lds_off(tid >> 1, (tid & 1) * 4 + q)) = o;
-    } else {
-      // byte q of each of the 4 row words: columns hc*8 + 2q and +1
-      const int og = tid >> 4;
-      const int hc = tid & 15;
-      float2 v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float2 t = ptab[(creg[set][i] >> (8 * q)) & 0xFFu];
-        const float sc = scale(set, i);
-        v[i] = make_float2(t.x * sc, t.y * sc);
-      }
-      const int row0 = hc * 8 + 2 * q;
-      uint2 e0, e1;
-      e0.x = pack_bf16x2(v[0].x, v[1].x);
-      e0.y = pack_bf16x2(v[2].x, v[3].x);
-      e1.x = pack_bf16x2(v[0].y, v[1].y);
-      e1.y = pack_bf16x2(v[2].y, v[3].y);
-      *(uint2*)(dst + row0 * 128 + (((og >> 1) ^ swz(row0)) << 4) + (og & 1) * 8) = e0;
-      *(uint2*)(dst + (row0 + 1) * 128 + (((og >> 1) ^ swz(row0 + 1)) << 4) + (og & 1) * 8) = e1;
-    }
-  };
-
-  // ---- one K=16 MFMA group on LDS buffer `buf` ----
-  auto mfma16 = [&](int buf, int kk) {
-    const uint8_t* Ab = buf ? As1 : As0;
-    const uint8_t* Bb = buf ? Bs1 : Bs0;
-    const int chunk = kk * 2 + (lane >> 5);
-    bf16x8 af[4], bfr[2];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-      af[mi] = *(const bf16x8*)(Ab + lds_off(wm * 128 + mi * 32 + (lane & 31), chunk));
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-      bfr[ni] = *(const bf16x8*)(Bb + lds_off(wn * 64 + ni * 32 + (lane & 31), chunk));
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < 4; ++mi)
+        f.a[mi] = *(const bf16x8*)(Ab + lds_off(wm * 128 + mi * 32 + (lane & 31), chunk));
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
-  };
-
-  // Pipeline: tile t of A is in LDS buffer t%2 during step t; the codes of
-  // tile t are loaded into register set t%2 during step t-2 and dequantized
-  // into B buffer t%2 during step t-1, between that step's MFMA groups.
-  // Step kt (cur = kt%2): issue A(kt+1) -> LDS cur^1 and W(kt+2) -> set cur,
-  // run the MFMAs on buffer cur while dequantizing set cur^1 (tile kt+1) into
-  // B buffer cur^1, wait for A(kt+1) only, barrier.
-  auto step_full = [&](int kt, int cur) {
-    // A's loads must be the oldest in flight: the wait at the end of the step
-    // leaves only issue_W's kWLoads younger loads outstanding, so every row of
-    // A(kt+1) has landed in LDS before the barrier that publishes it
-    __builtin_amdgcn_sched_barrier(0);
-    issue_A(kt + 1, cur ^ 1);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_W(kt + 2, cur);
-    __builtin_amdgcn_sched_barrier(0);
+        f.b[ni] = *(const bf16x8*)(Bb + lds_off(wn * 64 + ni * 32 + (lane & 31), chunk));
+    };
+    auto mma = [&](const Frags& f) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      mfma16(cur, kk);
-      dequant_quarter(cur ^ 1, cur ^ 1, kk);
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0);
+    };
+    auto interleave = [&]() {
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one fragment read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    };
+    Frags f0, f1;
+    __syncthreads();  // (1)
+    __syncthreads();  // (2)
+    load_frags(0, 0, f0);
+    // step s: tile s (buffer s%3) is published and f0 holds its first K16
+    // fragments; the next group's reads are issued during the current group's
+    // MFMAs, the last one being the first group of tile s+1 (published one
+    // step earlier), so no step starts by waiting on LDS.
+    auto cstep = [&](int j) {
+      const int b = j % 3, bn = (j + 1) % 3;
+      load_frags(b, 1, f1);
+      mma(f0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      load_frags(b, 2, f0);
+      mma(f1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      load_frags(b, 3, f1);
+      mma(f0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      load_frags(bn, 0, f0);
+      mma(f1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+    };
+    int s = 0;
+    for (; s + 6 <= KT; s += 6) {
+      cstep(0); cstep(1); cstep(2); cstep(3); cstep(4); cstep(5);
     }
-    __builtin_amdgcn_s_waitcnt(kWaitW);
-    __syncthreads();
-  };
-  auto step_tail = [&](int kt, int cur) {  // last steps: no W(kt+2), maybe no A(kt+1)
-    const bool more = kt + 1 < KT;
-    if (more) issue_A(kt + 1, cur ^ 1);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      mfma16(cur, kk);
-      if (more) dequant_quarter(cur ^ 1, cur ^ 1, kk);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  };
-
-  // prologue: A(0) -> LDS 0, W(0) -> set 0, W(1) -> set 1, B(0) dequantized
-  issue_A(0, 0);
-  issue_W(0, 0);
-  if (KT > 1) issue_W(1, 1);
-  __syncthreads();  // ptab
-#pragma unroll
-  for (int q = 0; q < 4; ++q) dequant_quarter(0, 0, q);
-  __builtin_amdgcn_s_waitcnt(0);
+    if (s < KT) cstep(0);
+    if (s + 1 < KT) cstep(1);
+    if (s + 2 < KT) cstep(2);
+    if (s + 3 < KT) cstep(3);
+    if (s + 4 < KT) cstep(4);
+  }
   __syncthreads();
 
-  int kt = 0;
-  for (; kt + 3 < KT; kt += 2) {  // both steps of the pair have kt+2 < KT
-    step_full(kt, 0);
-    step_full(kt + 1, 1);
-  }
-  // at most three steps remain; kt is even here
-  if (kt + 2 < KT) {
-    step_full(kt, 0);
-    step_tail(kt + 1, 1);
-    step_tail(kt + 2, 0);
-  } else {
-    if (kt < KT) step_tail(kt, 0);
-    if (kt + 1 < KT) step_tail(kt + 1, 1);
-  }
-
-  // ---- adapter tail: R extra K columns from A2 [M][R] and B2 [N][R] ----
+  // ---- adapter tail: R extra K columns from A2 [M][R] and B2 [N][R] (loads by all waves) ----
   if (p.R > 0) {
     const __amdgpu_buffer_rsrc_t a2 = make_rsrc(p.A2 + m0 * p.R, (uint32_t)(arows * p.R * 2));
     const int nrows = (N - n0) < GBN ? (N - n0) : GBN;
@@ -317,40 +350,58 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
     for (int c0 = 0; c0 < p.R; c0 += GBK) {
       const int width = min(GBK, p.R - c0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = (tid >> 3) + 32 * i;
+      for (int i = 0; i < 4; ++i) {
+        const int r = (tid >> 3) + 64 * i;
         const int kc = tid & 7;
         const uint32_t off = kc * 8 < width ? (uint32_t)((r * p.R + c0 + kc * 8) * 2) : kOOB;
         *(u32x4*)(As0 + lds_off(r, kc)) = __builtin_amdgcn_raw_buffer_load_b128(a2, off, 0, 0);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = tid >> 1;
-        const int kc = (tid & 1) * 4 + j;
+      for (int jj = 0; jj < 2; ++jj) {
+        const int r = tid >> 2;
+        const int kc = (tid & 3) * 2 + jj;
         const uint32_t off = kc * 8 < width ? (uint32_t)((r * p.R + c0 + kc * 8) * 2) : kOOB;
         *(u32x4*)(Bs0 + lds_off(r, kc)) = __builtin_amdgcn_raw_buffer_load_b128(b2, off, 0, 0);
       }
       __syncthreads();
-      for (int kk = 0; kk < (width >> 4); ++kk) mfma16(0, kk);
+      if (!producer) {
+        for (int kk = 0; kk < (width >> 4); ++kk) {
+          const int chunk = kk * 2 + (lane >> 5);
+          bf16x8 fa[4], fb[2];
+#pragma unroll
+          for (int mi = 0; mi < 4; ++mi)
+            fa[mi] = *(const bf16x8*)(As0 + lds_off(wm * 128 + mi * 32 + (lane & 31), chunk));
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni)
+            fb[ni] = *(const bf16x8*)(Bs0 + lds_off(wn * 64 + ni * 32 + (lane & 31), chunk));
+#pragma unroll
+          for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ni], fa[mi], acc[mi][ni], 0, 0, 0);
+        }
+      }
       __syncthreads();
     }
   }
 
-  // ---- epilogue: D[n][m] per MFMA; lane holds m = l%32 and n = 8*(v/4) + 4*(l/32) + v%4 ----
+  // ---- epilogue (consumers): D[n][m]; lane holds m = l%32, n = 8*(v/4) + 4*(l/32) + v%4 ----
+  if (!producer) {
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    const int64_t m = m0 + wm * 128 + mi * 32 + (lane & 31);
-    if (m < M) {
+    for (int mi = 0; mi < 4; ++mi) {
+      const int64_t m = m0 + wm * 128 + mi * 32 + (lane & 31);
+      if (m < M) {
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
+        for (int ni = 0; ni < 2; ++ni) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * 64 + ni * 32 + 8 * g + 4 * (lane >> 5);
-          if (n < N) {
-            uint2 o;
-            o.x = pack_bf16x2(acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1]);
-            o.y = pack_bf16x2(acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]);
-            *(uint2*)(p.C + m * N + n) = o;
+          for (int gg = 0; gg < 4; ++gg) {
+            const int n = n0 + wn * 64 + ni * 32 + 8 * gg + 4 * (lane >> 5);
+            if (n < N) {
+              uint2 o;
+              o.x = pack_bf16x2(acc[mi][ni][4 * gg + 0], acc[mi][ni][4 * gg + 1]);
+              o.y = pack_bf16x2(acc[mi][ni][4 * gg + 2], acc[mi][ni][4 * gg + 3]);
+              *(uint2*)(p.C + m * N + n) = o;
+            }
           }
         }
       }
