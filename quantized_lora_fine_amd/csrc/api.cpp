@@ -79,13 +79,15 @@ nf4_status check_tensor(const nf4_tensor* q) {
 struct FwdPlan {
   int32_t RP;
   int ks, kr;
-  size_t off_l1t, off_l2t, off_ts, off_part, total;
+  size_t off_l1t, off_l2t, off_ts, off_part, off_cnt, total;
+  int64_t ncnt;  // 32-bit counters
 };
 
 FwdPlan plan_fwd(int64_t M, int64_t o, int64_t h, int32_t r) {
   FwdPlan p;
   p.RP = round16(r);
   plan_nt(M, (int)h, &p.ks, &p.kr);
+  p.ncnt = (M + 63) / 64;
   size_t off = 0;
   p.off_l1t = off;
   off += align256((size_t)p.RP * h * 2);
@@ -95,6 +97,8 @@ FwdPlan plan_fwd(int64_t M, int64_t o, int64_t h, int32_t r) {
   off += align256((size_t)M * p.RP * 2);
   p.off_part = off;
   off += align256((size_t)p.ks * M * p.RP * 4);
+  p.off_cnt = off;
+  off += align256((size_t)p.ncnt * 4);
   p.total = off;
   return p;
 }
@@ -103,7 +107,9 @@ struct BwdPlan {
   int32_t RP;
   int ks_t, kr_t, ks_g, kr_g, ms2, ms1;
   int64_t mr2, mr1;
-  size_t off_l1t, off_l1p, off_l2p, off_tb, off_g, off_pnt, off_p2, off_p1, total;
+  size_t off_l1t, off_l1p, off_l2p, off_tb, off_g, off_pnt, off_p2, off_p1, off_cnt, total;
+  // counters (32-bit) at off_cnt: T recompute [mb], G [mb], dL2 [o/64], dL1 [h/64]
+  int64_t cnt_t, cnt_g, cnt_2, cnt_1, ncnt;
 };
 
 BwdPlan plan_bwd(int64_t M, int64_t o, int64_t h, int32_t r) {
@@ -114,6 +120,12 @@ BwdPlan plan_bwd(int64_t M, int64_t o, int64_t h, int32_t r) {
   plan_tn(M, (int)o, &p.ms2, &p.mr2);
   plan_tn(M, (int)h, &p.ms1, &p.mr1);
   const int ksmax = p.ks_t > p.ks_g ? p.ks_t : p.ks_g;
+  const int64_t mb = (M + 63) / 64;
+  p.cnt_t = 0;
+  p.cnt_g = mb;
+  p.cnt_2 = 2 * mb;
+  p.cnt_1 = 2 * mb + (o + 63) / 64;
+  p.ncnt = p.cnt_1 + (h + 63) / 64;
   size_t off = 0;
   p.off_l1t = off;
   off += align256((size_t)p.RP * h * 2);
@@ -131,8 +143,24 @@ BwdPlan plan_bwd(int64_t M, int64_t o, int64_t h, int32_t r) {
   off += align256((size_t)p.ms2 * p.RP * o * 4);
   p.off_p1 = off;
   off += align256((size_t)p.ms1 * p.RP * h * 4);
+  p.off_cnt = off;
+  off += align256((size_t)p.ncnt * 4);
   p.total = off;
   return p;
+}
+
+PadJob pad_job(const uint16_t* in, int64_t si, int64_t sj, int64_t irows, int64_t jcols, uint16_t* out,
+               int64_t orows, int64_t ocols) {
+  PadJob j;
+  j.in = in;
+  j.out = out;
+  j.si = si;
+  j.sj = sj;
+  j.irows = irows;
+  j.jcols = jcols;
+  j.orows = orows;
+  j.ocols = ocols;
+  return j;
 }
 
 size_t error_ws(int64_t rows, int64_t cols) {
@@ -268,12 +296,16 @@ nf4_status nf4lora_fwd(const nf4_tensor* W, const uint16_t* X, int64_t M, const 
   uint16_t* l2t = (uint16_t*)(w + p.off_l2t);
   uint16_t* ts = (uint16_t*)(w + p.off_ts);
   float* part = (float*)(w + p.off_part);
-  // L1^T [RP][h] (rows >= r zero) and L2^T [o][RP] (columns >= r zero)
-  NF4_TRY(launch_pad_transpose(L1, 1, r, r, h, l1t, p.RP, h, hs));
-  NF4_TRY(launch_pad_transpose(L2, 1, o, o, r, l2t, o, p.RP, hs));
-  // T = X L1 (split K, fixed-order reduce) -> T_out (bf16) and s*T (bf16, padded)
-  NF4_TRY(launch_skinny_nt(X, l1t, M, (int)h, p.RP, part, p.ks, p.kr, hs));
-  NF4_TRY(launch_reduce_nt(part, M, p.RP, r, p.ks, 1.0f, T_out, r, s, ts, hs));
+  unsigned* cnt = (unsigned*)(w + p.off_cnt);
+  // one prep launch: L1^T [RP][h] (rows >= r zero), L2^T [o][RP] (columns >= r zero), counters
+  PrepArgs pa{};
+  pa.pad[0] = pad_job(L1, 1, r, r, h, l1t, p.RP, h);
+  pa.pad[1] = pad_job(L2, 1, o, o, r, l2t, o, p.RP);
+  pa.zero[0] = ZeroJob{cnt, p.ncnt};
+  NF4_TRY(launch_prep(pa, hs));
+  // T = X L1 (split K, fixed-order reduction) -> T_out (bf16) and s*T (bf16, padded)
+  NtArgs nt{X, l1t, M, (int)h, p.ks, p.kr, part, cnt, r, 1.0f, T_out, r, s, ts};
+  NF4_TRY(launch_skinny_nt(nt, p.RP, hs));
   // Y = X w_hat^T + (s T) L2
   NF4_TRY(launch_nf4_gemm(MODE_FWD, W->dq_group != 0, X, W->codes, W->absmax, W->dq_scale, ts, l2t, p.RP, Y, M,
                           (int)o, (int)h, nf4_consts(), hs));
@@ -313,10 +345,13 @@ nf4_status nf4lora_bwd(const nf4_tensor* W, const uint16_t* X, const uint16_t* d
 
   hipStream_t hs = (hipStream_t)stream;
   uint8_t* w = (uint8_t*)ws;
+  unsigned* cnt = (unsigned*)(w + p.off_cnt);
   if (M == 0) {
     // empty token set: both adapter gradients are exactly zero
-    NF4_TRY(launch_reduce_tn((const float*)(w + p.off_p2), p.RP, r, (int)o, 0, s, 0, dL2, hs));
-    NF4_TRY(launch_reduce_tn((const float*)(w + p.off_p1), p.RP, r, (int)h, 0, 1.0f, 1, dL1, hs));
+    PrepArgs pa{};
+    pa.zero[0] = ZeroJob{(uint32_t*)dL2, (int64_t)r * o};
+    pa.zero[1] = ZeroJob{(uint32_t*)dL1, (int64_t)h * r};
+    NF4_TRY(launch_prep(pa, hs));
     return NF4_OK;
   }
   uint16_t* l1t = (uint16_t*)(w + p.off_l1t);
@@ -328,26 +363,34 @@ nf4_status nf4lora_bwd(const nf4_tensor* W, const uint16_t* X, const uint16_t* d
   float* p2 = (float*)(w + p.off_p2);
   float* p1 = (float*)(w + p.off_p1);
 
-  // adapters in the layouts the products read: L1 [h][RP], L2 [RP][o]
-  NF4_TRY(launch_pad_transpose(L1, r, 1, h, r, l1p, h, p.RP, hs));
-  NF4_TRY(launch_pad_transpose(L2, o, 1, r, o, l2p, p.RP, o, hs));
+  // one prep launch: L1 [h][RP], L2 [RP][o], counters, and L1^T [RP][h] when T is recomputed
+  // or T [M][RP] when the given T has rows that are not whole 16-byte chunks
+  PrepArgs pa{};
+  pa.pad[0] = pad_job(L1, r, 1, h, r, l1p, h, p.RP);
+  pa.pad[1] = pad_job(L2, o, 1, r, o, l2p, p.RP, o);
+  if (!T) pa.pad[2] = pad_job(L1, 1, r, r, h, l1t, p.RP, h);
+  else if (r % 8 != 0) pa.pad[2] = pad_job(T, r, 1, M, r, tb, M, p.RP);
+  pa.zero[0] = ZeroJob{cnt, p.ncnt};
+  NF4_TRY(launch_prep(pa, hs));
   const uint16_t* tsrc = T;
   int ldt = r;
   if (!T) {
-    NF4_TRY(launch_pad_transpose(L1, 1, r, r, h, l1t, p.RP, h, hs));
-    NF4_TRY(launch_skinny_nt(X, l1t, M, (int)h, p.RP, pnt, p.ks_t, p.kr_t, hs));
-    NF4_TRY(launch_reduce_nt(pnt, M, p.RP, r, p.ks_t, 1.0f, nullptr, 0, 1.0f, tb, hs));
+    NtArgs nt{X, l1t, M, (int)h, p.ks_t, p.kr_t, pnt, cnt + p.cnt_t, r, 1.0f, nullptr, 0, 1.0f, tb};
+    NF4_TRY(launch_skinny_nt(nt, p.RP, hs));
     tsrc = tb;
     ldt = p.RP;
+  } else if (r % 8 != 0) {
+    tsrc = tb;  // padded by the prep launch: the TN product reads rows in 16-byte chunks
+    ldt = p.RP;
   }
-  // G = s dY L2^T  (bf16 [M][RP])
-  NF4_TRY(launch_skinny_nt(dY, l2p, M, (int)o, p.RP, pnt, p.ks_g, p.kr_g, hs));
-  NF4_TRY(launch_reduce_nt(pnt, M, p.RP, r, p.ks_g, 1.0f, nullptr, 0, s, g, hs));
+  // G = s dY L2^T  (bf16 [M][RP], columns >= r zero)
+  NtArgs ng{dY, l2p, M, (int)o, p.ks_g, p.kr_g, pnt, cnt + p.cnt_g, r, 1.0f, nullptr, 0, s, g};
+  NF4_TRY(launch_skinny_nt(ng, p.RP, hs));
   // dL2 = s T^T dY  ([r][o]),  dL1 = X^T G  (stored [h][r])
-  NF4_TRY(launch_skinny_tn(tsrc, ldt, r, dY, M, (int)o, p.RP, p2, p.ms2, p.mr2, hs));
-  NF4_TRY(launch_reduce_tn(p2, p.RP, r, (int)o, p.ms2, s, 0, dL2, hs));
-  NF4_TRY(launch_skinny_tn(g, p.RP, r, X, M, (int)h, p.RP, p1, p.ms1, p.mr1, hs));
-  NF4_TRY(launch_reduce_tn(p1, p.RP, r, (int)h, p.ms1, 1.0f, 1, dL1, hs));
+  TnArgs t2{tsrc, ldt, r, dY, M, (int)o, p.ms2, p.mr2, p2, cnt + p.cnt_2, s, 0, dL2};
+  NF4_TRY(launch_skinny_tn(t2, p.RP, hs));
+  TnArgs t1{g, p.RP, r, X, M, (int)h, p.ms1, p.mr1, p1, cnt + p.cnt_1, 1.0f, 1, dL1};
+  NF4_TRY(launch_skinny_tn(t1, p.RP, hs));
   // dX = dY w_hat + G L1^T
   if (dX) {
     NF4_TRY(launch_nf4_gemm(MODE_DX, W->dq_group != 0, dY, W->codes, W->absmax, W->dq_scale, g, l1p, p.RP, dX, M,

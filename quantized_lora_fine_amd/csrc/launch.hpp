@@ -22,17 +22,59 @@ hipError_t launch_nf4_gemm(int mode, bool dq, const uint16_t* A, const uint8_t* 
                            const float* dqs, const uint16_t* A2, const uint16_t* B2, int R, uint16_t* C, int64_t M,
                            int N, int K, const NF4Consts& c, hipStream_t st);
 
-hipError_t launch_pad_transpose(const uint16_t* in, int64_t si, int64_t sj, int64_t irows, int64_t jcols,
-                                uint16_t* out, int64_t orows, int64_t ocols, hipStream_t st);
+// One launch of k_prep: up to kPrepPads layout copies and kPrepZeros clears.
+// Unused jobs have orows * ocols == 0 / n == 0.
+constexpr int kPrepPads = 3;
+constexpr int kPrepZeros = 2;
+struct PadJob {  // out[i][j] = (i < irows && j < jcols) ? in[i*si + j*sj] : 0, out is [orows][ocols]
+  const uint16_t* in;
+  uint16_t* out;
+  int64_t si, sj, irows, jcols, orows, ocols;
+};
+struct ZeroJob {
+  uint32_t* p;
+  int64_t n;  // 32-bit words
+};
+struct PrepArgs {
+  PadJob pad[kPrepPads];
+  ZeroJob zero[kPrepZeros];
+};
+hipError_t launch_prep(const PrepArgs& a, hipStream_t st);
+
+// NT skinny product with its split reduction: out = alpha * A[M][K] B[RP][K]^T.
+struct NtArgs {
+  const uint16_t* A;
+  const uint16_t* B;
+  int64_t M;
+  int K;
+  int ksplit, krange;
+  float* part;      // [ksplit][M][RP] fp32 (unused if ksplit == 1)
+  unsigned* cnt;    // [ceil(M/64)] zeroed counters
+  int r;
+  float alpha1;
+  uint16_t* out1;   // [M][ld1], columns < r, or NULL
+  int ld1;
+  float alpha2;
+  uint16_t* out2;   // [M][RP], or NULL
+};
+// TN skinny product with its split reduction: out = alpha * P[M][:r]^T Q[M][N].
+struct TnArgs {
+  const uint16_t* P;  // [M][ldp], 16-byte aligned, ldp % 8 == 0, columns r .. ceil8(r)-1 zero
+  int ldp, r;
+  const uint16_t* Q;
+  int64_t M;
+  int N;
+  int msplit;
+  int64_t mrange;
+  float* part;      // [msplit][RP][N] fp32 (unused if msplit == 1)
+  unsigned* cnt;    // [ceil(N/64)] zeroed counters
+  float alpha;
+  int trans;        // 0: out [r][N]; 1: out [N][r]
+  float* out;
+};
 void plan_nt(int64_t M, int K, int* ksplit, int* krange);
 void plan_tn(int64_t M, int N, int* msplit, int64_t* mrange);
-hipError_t launch_skinny_nt(const uint16_t* A, const uint16_t* B, int64_t M, int K, int RP, float* part, int ksplit,
-                            int krange, hipStream_t st);
-hipError_t launch_reduce_nt(const float* part, int64_t M, int RP, int r, int ksplit, float alpha1, uint16_t* out1,
-                            int ld1, float alpha2, uint16_t* out2, hipStream_t st);
-hipError_t launch_skinny_tn(const uint16_t* P, int ldp, int r, const uint16_t* Q, int64_t M, int N, int RP,
-                            float* part, int msplit, int64_t mrange, hipStream_t st);
-hipError_t launch_reduce_tn(const float* part, int RP, int r, int N, int msplit, float alpha, int trans, float* out,
-                            hipStream_t st);
+hipError_t launch_skinny_nt(const NtArgs& a, int RP, hipStream_t st);
+hipError_t launch_skinny_tn(const TnArgs& a, int RP, hipStream_t st);
 
 }  // namespace nf4k
