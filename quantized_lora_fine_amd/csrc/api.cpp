@@ -231,7 +231,7 @@ nf4_status nf4_quantize(const float* W, const nf4_tensor* q, void* stream) {
       (db && overlap(in, rng(q->dq_scale, db))) || overlap(rng(q->codes, cb), rng(q->absmax, ab)))
     return NF4_ERR_ALIAS;
   return hip_status(launch_quantize(W, n / kBlock, q->dq_group != 0, q->codes, q->absmax, q->dq_scale,
-                                    nf4_consts(), (hipStream_t)stream));
+                                    nf4_enc(), (hipStream_t)stream));
 }
 
 nf4_status nf4_dequantize(const nf4_tensor* q, void* W_out, int32_t out_is_bf16, void* stream) {
@@ -437,7 +437,7 @@ nf4_status nf4_layer_error(const float* W, int64_t rows, int64_t cols, int32_t b
   const Range in = rng(W, (size_t)n * 4);
   if (overlap(in, rng(ws, need)) || overlap(in, rng(err_dev, 8)) || overlap(rng(ws, need), rng(err_dev, 8)))
     return NF4_ERR_ALIAS;
-  return hip_status(launch_error(W, n / kBlock, dq_group != 0, (double*)ws, err_dev, nf4_consts(),
+  return hip_status(launch_error(W, n / kBlock, dq_group != 0, (double*)ws, err_dev, nf4_enc(),
                                  (hipStream_t)stream));
 }
 

@@ -29,24 +29,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
-// Nearest code of an fp32 x in [-1, 1]: the number of thresholds below x,
-// found by a 4-level binary search over the 15 ordered thresholds.
-__device__ __forceinline__ uint32_t nf4_encode(float x, const NF4Consts& c) {
-  const bool b3 = x > c.thr[7];
-  const float t2 = b3 ? c.thr[11] : c.thr[3];
-  const bool b2 = x > t2;
-  const float t1 = b3 ? (b2 ? c.thr[13] : c.thr[9]) : (b2 ? c.thr[5] : c.thr[1]);
-  const bool b1 = x > t1;
-  float t0;
-  if (b3) {
-    t0 = b2 ? (b1 ? c.thr[14] : c.thr[12]) : (b1 ? c.thr[10] : c.thr[8]);
-  } else {
-    t0 = b2 ? (b1 ? c.thr[6] : c.thr[4]) : (b1 ? c.thr[2] : c.thr[0]);
-  }
-  const bool b0 = x > t0;
-  return (uint32_t)b3 * 8u + (uint32_t)b2 * 4u + (uint32_t)b1 * 2u + (uint32_t)b0;
-}
-
 // Max over the 16 lanes of a DPP row (lanes 16k .. 16k+15); every lane of the
 // row receives the result.
 __device__ __forceinline__ float row16_max(float v) {

@@ -11,10 +11,10 @@ namespace nf4k {
 enum { MODE_FWD = 0, MODE_DX = 1 };
 
 hipError_t launch_quantize(const float* W, int64_t nblocks, bool dq, uint8_t* codes, void* absmax, float* dqs,
-                           const NF4Consts& c, hipStream_t st);
+                           const NF4Enc& c, hipStream_t st);
 hipError_t launch_dequantize(const uint8_t* codes, const void* absmax, const float* dqs, int64_t nweights, bool dq,
                              bool bf16, void* out, const NF4Consts& c, hipStream_t st);
-hipError_t launch_error(const float* W, int64_t nblocks, bool dq, double* part, double* err, const NF4Consts& c,
+hipError_t launch_error(const float* W, int64_t nblocks, bool dq, double* part, double* err, const NF4Enc& c,
                         hipStream_t st);
 hipError_t launch_topk(const double* e, int n, int k, int* idx, hipStream_t st);
 

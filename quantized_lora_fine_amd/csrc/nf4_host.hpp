@@ -1,6 +1,8 @@
 // Host-visible constants of the NF4 format (no HIP dependency).
 #pragma once
 
+#include <stdint.h>
+
 namespace nf4k {
 
 // NF4 code values and the fp32 decision thresholds between neighbours,
@@ -15,5 +17,22 @@ struct NF4Consts {
 
 // The table, built once on first use (thread-safe static initialisation).
 const NF4Consts& nf4_consts();
+
+// Bucket table of the encoder.  For an fp32 x in [-1, 1] the bucket is
+// k = trunc(fl(16 x + 16)) in 0..32 (one rounding; 16 x is exact), a
+// monotone function of x whose buckets are 1/16 wide, narrower than the
+// smallest gap between two thresholds, so a bucket holds at most one
+// threshold.  With base[k] = number of thresholds in buckets below k and
+// thr[k] the threshold inside bucket k (+inf if none):
+//   code(x) = #{j : x > thr_j} = base[k] + (x > thr[k]),
+// and the dequantized value of that code is (x > thr[k]) ? qhi[k] : qlo[k].
+constexpr int kBuckets = 33;
+struct NF4Enc {
+  float thr[kBuckets];
+  uint32_t base[kBuckets];
+  float qlo[kBuckets];
+  float qhi[kBuckets];
+};
+const NF4Enc& nf4_enc();
 
 }  // namespace nf4k

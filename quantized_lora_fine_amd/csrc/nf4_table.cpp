@@ -15,6 +15,7 @@
 // fixes its float exactly.
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "nf4_host.hpp"
@@ -62,6 +63,38 @@ static NF4Consts build_consts() {
 const NF4Consts& nf4_consts() {
   static const NF4Consts c = build_consts();
   return c;
+}
+
+static uint32_t bucket_of(float x) { return (uint32_t)std::fmaf(x, 16.0f, 16.0f); }
+
+static NF4Enc build_enc() {
+  const NF4Consts& c = nf4_consts();
+  NF4Enc e;
+  for (int k = 0; k < kBuckets; ++k) {
+    e.thr[k] = INFINITY;
+    e.base[k] = 0;
+  }
+  int owner[kBuckets];
+  for (int k = 0; k < kBuckets; ++k) owner[k] = -1;
+  for (int j = 0; j < 15; ++j) {
+    const uint32_t k = bucket_of(c.thr[j]);
+    if (k >= (uint32_t)kBuckets || owner[k] >= 0) std::abort();  // two thresholds in one bucket
+    owner[k] = j;
+    e.thr[k] = c.thr[j];
+  }
+  uint32_t below = 0;
+  for (int k = 0; k < kBuckets; ++k) {
+    e.base[k] = below;
+    if (owner[k] >= 0) ++below;
+    e.qlo[k] = c.table[e.base[k]];
+    e.qhi[k] = c.table[owner[k] >= 0 ? e.base[k] + 1 : e.base[k]];
+  }
+  return e;
+}
+
+const NF4Enc& nf4_enc() {
+  static const NF4Enc e = build_enc();
+  return e;
 }
 
 }  // namespace nf4k

@@ -21,75 +21,115 @@ namespace nf4k {
 // ---------------------------------------------------------------------------
 // quantize
 // ---------------------------------------------------------------------------
+constexpr uint32_t kRsrcFlags = 0x00020000u;  // raw buffer, gfx9-family dword3
+constexpr int kNT = 2;                        // cache policy: streaming (nt)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcFlags);
+}
+
+// The 16 rounds of one wave: round i covers blocks lb = wave*64 + 4i + sub of
+// the group (sub = lane/16), lane l16 of the DPP row holding elements
+// 4*l16 .. 4*l16+3.  Reads past the group's last block return zero.
+__device__ __forceinline__ void load_group(__amdgpu_buffer_rsrc_t wr, int wave, int sub, int l16, floatx4 v[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int lb = wave * 64 + 4 * i + sub;
+    v[i] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(wr, (lb * 64 + l16 * 4) * 4, 0, kNT));
+  }
+}
+
+// Encoder tables in LDS (see NF4Enc): ea[k] = {threshold inside bucket k,
+// bit pattern of the number of thresholds below bucket k}, eq[k] = {value of
+// the lower code, value of the upper code}.  8-byte entries: the 33 buckets
+// span 66 consecutive banks, so lookups rarely conflict.
+__device__ __forceinline__ void enc_to_lds(const NF4Enc& e, float2* ea, float2* eq, int tid) {
+  if (tid < kBuckets) {
+    ea[tid] = make_float2(e.thr[tid], __builtin_bit_cast(float, e.base[tid]));
+    eq[tid] = make_float2(e.qlo[tid], e.qhi[tid]);
+  }
+}
+__device__ __forceinline__ uint32_t bucket_of(float x) { return (uint32_t)__builtin_fmaf(x, 16.f, 16.f); }
+__device__ __forceinline__ uint32_t encode1(float x, const float2* ea) {
+  const float2 t = ea[bucket_of(x)];
+  return __builtin_bit_cast(uint32_t, t.y) + (x > t.x ? 1u : 0u);
+}
+
+// codes of 4 weights normalised by the block absmax m (m == 0: every weight of
+// the block is +-0 and divides by 1 to +-0, code 7), packed into 16 bits.
+__device__ __forceinline__ uint32_t encode4(floatx4 v, float m, const float2* ea) {
+  const float d = (m > 0.f) ? m : 1.f;
+  return encode1(v.x / d, ea) | (encode1(v.y / d, ea) << 4) | (encode1(v.z / d, ea) << 8) |
+         (encode1(v.w / d, ea) << 12);
+}
+
+__device__ __forceinline__ float abs_max4(floatx4 v) {
+  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+// max over the 256 threads of the workgroup (every thread gets it)
+__device__ __forceinline__ float group_max(float gm, int lane, int wave) {
+  __shared__ float red[4];
+  gm = fmaxf(gm, __shfl_xor(gm, 16));
+  gm = fmaxf(gm, __shfl_xor(gm, 32));
+  if (lane == 0) red[wave] = gm;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
 template <bool DQ>
 __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, int64_t nblocks,
                                                   uint8_t* __restrict__ codes,
                                                   float* __restrict__ absmax,
                                                   uint8_t* __restrict__ c8,
-                                                  float* __restrict__ dqs, NF4Consts cst) {
+                                                  float* __restrict__ dqs, NF4Enc enc) {
+  __shared__ float2 ea[kBuckets], eq[kBuckets];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int sub = lane >> 4;   // block slot within a round (DPP row)
-  const int l16 = lane & 15;   // lane within the row: elements 4*l16 .. 4*l16+3
+  const int sub = lane >> 4;
+  const int l16 = lane & 15;
   const int64_t g = blockIdx.x;
-  const int64_t b0 = g * 256 + wave * 64;
+  const int64_t gb0 = g * 256;
+  const uint32_t nb = (uint32_t)min((int64_t)256, nblocks - gb0);  // blocks in this group
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(W + gb0 * 64, nb * 256);
+  const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes + gb0 * 32, nb * 32);
+  enc_to_lds(enc, ea, eq, tid);
 
   floatx4 v[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t blk = b0 + i * 4 + sub;
-    if (blk < nblocks) {
-      v[i] = __builtin_nontemporal_load((const floatx4*)(W + blk * 64 + l16 * 4));
-    } else {
-      v[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
+  load_group(wr, wave, sub, l16, v);
+  __syncthreads();  // encoder tables
 
   float amax[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    float m = fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w)));
-    m = row16_max(m);
+    const float m = row16_max(abs_max4(v[i]));
     amax[i] = m;
-    uint32_t p;
-    if (m > 0.f) {
-      p = nf4_encode(v[i].x / m, cst) | (nf4_encode(v[i].y / m, cst) << 4) |
-          (nf4_encode(v[i].z / m, cst) << 8) | (nf4_encode(v[i].w / m, cst) << 12);
-    } else {
-      p = 0x7777u;  // all-zero block: every element takes the exact-zero code
-    }
-    const int64_t blk = b0 + i * 4 + sub;
-    if (blk < nblocks) *(uint16_t*)(codes + blk * 32 + l16 * 2) = (uint16_t)p;
+    const int lb = wave * 64 + 4 * i + sub;
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)encode4(v[i], m, ea), cr, lb * 32 + l16 * 2, 0, kNT);
   }
-
-  // lane l16 of row `sub` owns the block of round l16: blk = b0 + 4*l16 + sub
+  // lane l16 of row `sub` owns the block of round l16: lb = wave*64 + 4*l16 + sub
   float mine = amax[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) mine = (l16 == i) ? amax[i] : mine;
-  const int64_t myblk = b0 + l16 * 4 + sub;
+  const int mylb = wave * 64 + 4 * l16 + sub;
 
   if constexpr (!DQ) {
-    if (myblk < nblocks) absmax[myblk] = mine;
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(absmax + gb0, nb * 4);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, mine), ar, mylb * 4, 0, 0);
   } else {
-    __shared__ float red[4];
+    // group max of 256 absmax values: the 16 rows of this lane's round, then lanes, then waves
     float gm = mine;
     gm = fmaxf(gm, __shfl_xor(gm, 1));
     gm = fmaxf(gm, __shfl_xor(gm, 2));
     gm = fmaxf(gm, __shfl_xor(gm, 4));
     gm = fmaxf(gm, __shfl_xor(gm, 8));
-    gm = fmaxf(gm, __shfl_xor(gm, 16));
-    gm = fmaxf(gm, __shfl_xor(gm, 32));
-    if (lane == 0) red[wave] = gm;
-    __syncthreads();
-    gm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    gm = group_max(gm, lane, wave);
     const float S = gm / 255.0f;
     if (tid == 0) dqs[g] = S;
-    if (myblk < nblocks) {
-      uint8_t q = 0;
-      if (S > 0.f) q = (uint8_t)fminf(255.f, rintf(mine / S));
-      c8[myblk] = q;
-    }
+    const uint32_t q = (S > 0.f) ? (uint32_t)fminf(255.f, rintf(mine / S)) : 0u;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(c8 + gb0, nb);
+    __builtin_amdgcn_raw_buffer_store_b8((unsigned char)q, qr, mylb, 0, 0);
   }
 }
 
@@ -138,9 +178,8 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
 // ---------------------------------------------------------------------------
 template <bool DQ>
 __global__ __launch_bounds__(256) void k_error_partial(const float* __restrict__ W, int64_t nblocks,
-                                                       double* __restrict__ part, NF4Consts cst) {
-  __shared__ float tab[16];
-  __shared__ float redf[4];
+                                                       double* __restrict__ part, NF4Enc enc) {
+  __shared__ float2 ea[kBuckets], eq[kBuckets];
   __shared__ double redd[2][4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -148,38 +187,24 @@ __global__ __launch_bounds__(256) void k_error_partial(const float* __restrict__
   const int sub = lane >> 4;
   const int l16 = lane & 15;
   const int64_t g = blockIdx.x;
-  const int64_t b0 = g * 256 + wave * 64;
-  if (tid < 16) tab[tid] = cst.table[tid];
+  const int64_t gb0 = g * 256;
+  const uint32_t nb = (uint32_t)min((int64_t)256, nblocks - gb0);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(W + gb0 * 64, nb * 256);
+  enc_to_lds(enc, ea, eq, tid);
 
   floatx4 v[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t blk = b0 + i * 4 + sub;
-    if (blk < nblocks) {
-      v[i] = __builtin_nontemporal_load((const floatx4*)(W + blk * 64 + l16 * 4));
-    } else {
-      v[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
+  load_group(wr, wave, sub, l16, v);
   float amax[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float m = fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w)));
-    amax[i] = row16_max(m);
-  }
+  for (int i = 0; i < 16; ++i) amax[i] = row16_max(abs_max4(v[i]));
   float S = 0.f;
   if constexpr (DQ) {
     float gm = amax[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) gm = fmaxf(gm, amax[i]);
-    gm = fmaxf(gm, __shfl_xor(gm, 16));
-    gm = fmaxf(gm, __shfl_xor(gm, 32));
-    if (lane == 0) redf[wave] = gm;
-  }
-  __syncthreads();  // also publishes tab[]
-  if constexpr (DQ) {
-    const float gm = fmaxf(fmaxf(redf[0], redf[1]), fmaxf(redf[2], redf[3]));
-    S = gm / 255.0f;
+    S = group_max(gm, lane, wave) / 255.0f;  // its barrier also publishes the encoder tables
+  } else {
+    __syncthreads();  // publishes the encoder tables
   }
 
   double dsum = 0.0, wsum = 0.0;
@@ -189,10 +214,13 @@ __global__ __launch_bounds__(256) void k_error_partial(const float* __restrict__
     float sc = m;
     if constexpr (DQ) sc = (S > 0.f) ? fminf(255.f, rintf(m / S)) * S : 0.f;
     const float w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    const float dv = (m > 0.f) ? m : 1.f;  // m == 0: all weights are +-0 -> code 7
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t c = (m > 0.f) ? nf4_encode(w4[e] / m, cst) : 7u;
-      const float wh = tab[c] * sc;
+      const float x = w4[e] / dv;
+      const uint32_t k = bucket_of(x);
+      const float2 t = ea[k], q = eq[k];
+      const float wh = ((x > t.x) ? q.y : q.x) * sc;
       // fp64 from here on: squares of fp32 weights can leave the fp32 range
       const double wd = (double)w4[e];
       const double d = wd - (double)wh;
@@ -269,7 +297,7 @@ __global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ e, int
 // host-side launchers (called from the C ABI layer)
 // ---------------------------------------------------------------------------
 hipError_t launch_quantize(const float* W, int64_t nblocks, bool dq, uint8_t* codes, void* absmax,
-                           float* dqs, const NF4Consts& c, hipStream_t st) {
+                           float* dqs, const NF4Enc& c, hipStream_t st) {
   const int64_t ng = (nblocks + 255) / 256;
   if (ng == 0) return hipSuccess;
   if (dq) {
@@ -297,7 +325,7 @@ hipError_t launch_dequantize(const uint8_t* codes, const void* absmax, const flo
 }
 
 hipError_t launch_error(const float* W, int64_t nblocks, bool dq, double* part, double* err,
-                        const NF4Consts& c, hipStream_t st) {
+                        const NF4Enc& c, hipStream_t st) {
   const int64_t ng = (nblocks + 255) / 256;
   if (ng > 0) {
     if (dq) {
