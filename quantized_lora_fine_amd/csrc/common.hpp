@@ -29,22 +29,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
-// Max over the 16 lanes of a DPP row (lanes 16k .. 16k+15); every lane of the
-// row receives the result.
-__device__ __forceinline__ float row16_max(float v) {
-  int x = __builtin_bit_cast(int, v);
-  // quad_perm [1,0,3,2] and [2,3,0,1]: max over each quad
-  x = __builtin_bit_cast(int, fmaxf(__builtin_bit_cast(float, x),
-      __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false))));
-  x = __builtin_bit_cast(int, fmaxf(__builtin_bit_cast(float, x),
-      __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false))));
-  // row_half_mirror: lane i <-> 7-i inside each 8 -> max over 8
-  x = __builtin_bit_cast(int, fmaxf(__builtin_bit_cast(float, x),
-      __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false))));
-  // row_mirror: lane i <-> 15-i inside each 16 -> max over 16
-  x = __builtin_bit_cast(int, fmaxf(__builtin_bit_cast(float, x),
-      __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false))));
-  return __builtin_bit_cast(float, x);
+// Max over the 16 lanes of a DPP row (lanes 16k .. 16k+15) of non-negative
+// fp32 values given as bit patterns (for which unsigned order is float order);
+// every lane of the row receives the result.  bound_ctrl reads 0 (the
+// identity) outside the row, and each step fuses into one v_max_u32_dpp.
+__device__ __forceinline__ uint32_t row16_max_bits(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, true));  // row_half_mirror
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, true));  // row_mirror
+  return x;
+}
+
+// Max over the 16 lanes of a DPP row of |v| (every lane of the row receives it).
+__device__ __forceinline__ float row16_absmax(float v) {
+  return __builtin_bit_cast(float, row16_max_bits(__builtin_bit_cast(uint32_t, v) & 0x7FFFFFFFu));
 }
 
 // Sum over the 16 lanes of a DPP row, same pattern as row16_max (fixed order,

@@ -70,17 +70,23 @@ static uint32_t bucket_of(float x) { return (uint32_t)std::fmaf(x, 16.0f, 16.0f)
 static NF4Enc build_enc() {
   const NF4Consts& c = nf4_consts();
   NF4Enc e;
-  for (int k = 0; k < kBuckets; ++k) {
-    e.thr[k] = INFINITY;
-    e.base[k] = 0;
-  }
   int owner[kBuckets];
-  for (int k = 0; k < kBuckets; ++k) owner[k] = -1;
+  for (int k = 0; k < kBuckets; ++k) {
+    e.bound[k] = INFINITY;
+    owner[k] = -1;
+  }
+  const float margin = 1e-5f;
   for (int j = 0; j < 15; ++j) {
-    const uint32_t k = bucket_of(c.thr[j]);
-    if (k >= (uint32_t)kBuckets || owner[k] >= 0) std::abort();  // two thresholds in one bucket
+    const float t = c.thr[j];
+    const uint32_t k = bucket_of(t);
+    // one threshold per bucket, none near a bucket edge
+    if (k >= (uint32_t)kBuckets || owner[k] >= 0) std::abort();
+    if (bucket_of(t - margin) != k || bucket_of(t + margin) != k) std::abort();
     owner[k] = j;
-    e.thr[k] = c.thr[j];
+    const float succ = std::nextafter(t, INFINITY);
+    double u = 0.5 * ((double)t + (double)succ);  // exact: the rounding boundary above t
+    if ((float)u == succ) u = std::nextafter(u, -INFINITY);  // a tie rounds up to succ: w on u counts
+    e.bound[k] = u;
   }
   uint32_t below = 0;
   for (int k = 0; k < kBuckets; ++k) {

@@ -39,32 +39,70 @@ __device__ __forceinline__ void load_group(__amdgpu_buffer_rsrc_t wr, int wave, 
   }
 }
 
-// Encoder tables in LDS (see NF4Enc): ea[k] = {threshold inside bucket k,
-// bit pattern of the number of thresholds below bucket k}, eq[k] = {value of
-// the lower code, value of the upper code}.  8-byte entries: the 33 buckets
-// span 66 consecutive banks, so lookups rarely conflict.
-__device__ __forceinline__ void enc_to_lds(const NF4Enc& e, float2* ea, float2* eq, int tid) {
+// Encoder table in LDS, one 16-byte entry per bucket (see NF4Enc):
+// {fp64 bound, base code (quantize) or lower value, upper value}.
+struct EncEntry {
+  double bound;
+  uint32_t lo;  // base code, or bit pattern of the lower code's value
+  float hi;     // value of the upper code
+};
+template <bool VALUES>
+__device__ __forceinline__ void enc_to_lds(const NF4Enc& e, EncEntry* t, int tid) {
   if (tid < kBuckets) {
-    ea[tid] = make_float2(e.thr[tid], __builtin_bit_cast(float, e.base[tid]));
-    eq[tid] = make_float2(e.qlo[tid], e.qhi[tid]);
+    EncEntry x;
+    x.bound = e.bound[tid];
+    x.lo = VALUES ? __builtin_bit_cast(uint32_t, e.qlo[tid]) : e.base[tid];
+    x.hi = e.qhi[tid];
+    t[tid] = x;
   }
 }
-__device__ __forceinline__ uint32_t bucket_of(float x) { return (uint32_t)__builtin_fmaf(x, 16.f, 16.f); }
-__device__ __forceinline__ uint32_t encode1(float x, const float2* ea) {
-  const float2 t = ea[bucket_of(x)];
-  return __builtin_bit_cast(uint32_t, t.y) + (x > t.x ? 1u : 0u);
+
+// Per-block setup of the division-free encoder: m' = m (or 1 for an all-zero
+// block, whose weights are all +-0 and take code 7), an approximate 1/m' and
+// a power-of-two prescale keeping that reciprocal in the normal range.
+struct BlockEnc {
+  float s, y;
+  double md;
+};
+__device__ __forceinline__ BlockEnc block_enc(float m) {
+  BlockEnc b;
+  const float mp = (m > 0.f) ? m : 1.f;
+  b.s = (mp < 0x1p-64f) ? 0x1p64f : ((mp > 0x1p64f) ? 0x1p-64f : 1.f);
+  b.y = __builtin_amdgcn_rcpf(mp * b.s);
+  b.md = (double)mp;
+  return b;
+}
+// x > t for the threshold t of the bucket of x = fl32(w / m'), decided
+// exactly; returns the table entry through `en`.
+__device__ __forceinline__ bool above(float w, const BlockEnc& b, const EncEntry* tab, EncEntry& en) {
+  // xq is within 2e-7 of w / m' and |xq| <= 1 + 2e-7, so k is in 0..32
+  // (a NaN weight converts to bucket 0)
+  const float xq = (w * b.s) * b.y;
+  const uint32_t k = (uint32_t)__builtin_fmaf(xq, 16.f, 16.f);
+  en = tab[k];
+  return fma(-en.bound, b.md, (double)w) > 0.0;
 }
 
-// codes of 4 weights normalised by the block absmax m (m == 0: every weight of
-// the block is +-0 and divides by 1 to +-0, code 7), packed into 16 bits.
-__device__ __forceinline__ uint32_t encode4(floatx4 v, float m, const float2* ea) {
-  const float d = (m > 0.f) ? m : 1.f;
-  return encode1(v.x / d, ea) | (encode1(v.y / d, ea) << 4) | (encode1(v.z / d, ea) << 8) |
-         (encode1(v.w / d, ea) << 12);
+// codes of 4 weights of a block, packed into 16 bits
+__device__ __forceinline__ uint32_t encode4(floatx4 v, const BlockEnc& b, const EncEntry* tab) {
+  const float w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t p = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    EncEntry en;
+    const bool up = above(w[e], b, tab, en);
+    p |= (en.lo + (up ? 1u : 0u)) << (4 * e);
+  }
+  return p;
 }
 
-__device__ __forceinline__ float abs_max4(floatx4 v) {
-  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+// block absmax: |w| of the 4 weights of this lane as bit patterns (unsigned
+// order = float order for non-negative values), then the 16 lanes of the row
+// (The whole vector is reinterpreted: a bit cast of a single ext_vector
+// element is not reliable with this compiler.)
+__device__ __forceinline__ float block_absmax(floatx4 v) {
+  const u32x4 u = __builtin_bit_cast(u32x4, v) & 0x7FFFFFFFu;
+  return __builtin_bit_cast(float, row16_max_bits(max(max(u.x, u.y), max(u.z, u.w))));
 }
 
 // max over the 256 threads of the workgroup (every thread gets it)
@@ -83,7 +121,7 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
                                                   float* __restrict__ absmax,
                                                   uint8_t* __restrict__ c8,
                                                   float* __restrict__ dqs, NF4Enc enc) {
-  __shared__ float2 ea[kBuckets], eq[kBuckets];
+  __shared__ EncEntry etab[kBuckets];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -94,19 +132,19 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
   const uint32_t nb = (uint32_t)min((int64_t)256, nblocks - gb0);  // blocks in this group
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(W + gb0 * 64, nb * 256);
   const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes + gb0 * 32, nb * 32);
-  enc_to_lds(enc, ea, eq, tid);
+  enc_to_lds<false>(enc, etab, tid);
 
   floatx4 v[16];
   load_group(wr, wave, sub, l16, v);
-  __syncthreads();  // encoder tables
+  __syncthreads();  // encoder table
 
   float amax[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float m = row16_max(abs_max4(v[i]));
+    const float m = block_absmax(v[i]);
     amax[i] = m;
     const int lb = wave * 64 + 4 * i + sub;
-    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)encode4(v[i], m, ea), cr, lb * 32 + l16 * 2, 0, kNT);
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)encode4(v[i], block_enc(m), etab), cr, lb * 32 + l16 * 2, 0, kNT);
   }
   // lane l16 of row `sub` owns the block of round l16: lb = wave*64 + 4*l16 + sub
   float mine = amax[0];
@@ -179,7 +217,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
 template <bool DQ>
 __global__ __launch_bounds__(256) void k_error_partial(const float* __restrict__ W, int64_t nblocks,
                                                        double* __restrict__ part, NF4Enc enc) {
-  __shared__ float2 ea[kBuckets], eq[kBuckets];
+  __shared__ EncEntry etab[kBuckets];
   __shared__ double redd[2][4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -190,43 +228,52 @@ __global__ __launch_bounds__(256) void k_error_partial(const float* __restrict__
   const int64_t gb0 = g * 256;
   const uint32_t nb = (uint32_t)min((int64_t)256, nblocks - gb0);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(W + gb0 * 64, nb * 256);
-  enc_to_lds(enc, ea, eq, tid);
+  enc_to_lds<true>(enc, etab, tid);
 
   floatx4 v[16];
   load_group(wr, wave, sub, l16, v);
   float amax[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) amax[i] = row16_max(abs_max4(v[i]));
+  for (int i = 0; i < 16; ++i) amax[i] = block_absmax(v[i]);
   float S = 0.f;
   if constexpr (DQ) {
     float gm = amax[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) gm = fmaxf(gm, amax[i]);
-    S = group_max(gm, lane, wave) / 255.0f;  // its barrier also publishes the encoder tables
+    S = group_max(gm, lane, wave) / 255.0f;  // its barrier also publishes the encoder table
   } else {
-    __syncthreads();  // publishes the encoder tables
+    __syncthreads();  // publishes the encoder table
   }
 
+  // dequantization scale of each round's block
+  float sc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    sc[i] = amax[i];
+    if constexpr (DQ) sc[i] = (S > 0.f) ? fminf(255.f, rintf(amax[i] / S)) * S : 0.f;
+  }
   double dsum = 0.0, wsum = 0.0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float m = amax[i];
-    float sc = m;
-    if constexpr (DQ) sc = (S > 0.f) ? fminf(255.f, rintf(m / S)) * S : 0.f;
+    // one round at a time; the 4 squares of a round are added pairwise before
+    // joining the running sums, so the serial chain is 16 steps, not 64
+    __builtin_amdgcn_sched_barrier(0);
     const float w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-    const float dv = (m > 0.f) ? m : 1.f;  // m == 0: all weights are +-0 -> code 7
+    const BlockEnc be = block_enc(amax[i]);
+    double d2[4], w2[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float x = w4[e] / dv;
-      const uint32_t k = bucket_of(x);
-      const float2 t = ea[k], q = eq[k];
-      const float wh = ((x > t.x) ? q.y : q.x) * sc;
+      EncEntry en;
+      const bool up = above(w4[e], be, etab, en);
+      const float wh = (up ? en.hi : __builtin_bit_cast(float, en.lo)) * sc[i];
       // fp64 from here on: squares of fp32 weights can leave the fp32 range
       const double wd = (double)w4[e];
       const double d = wd - (double)wh;
-      dsum = fma(d, d, dsum);
-      wsum = fma(wd, wd, wsum);
+      d2[e] = d * d;
+      w2[e] = wd * wd;
     }
+    dsum += (d2[0] + d2[1]) + (d2[2] + d2[3]);
+    wsum += (w2[0] + w2[1]) + (w2[2] + w2[3]);
   }
   // fixed-order reduction: xor tree inside the wave, then waves 0..3 in order
 #pragma unroll
