@@ -36,8 +36,8 @@ reading and pinned only by the closed forms and invariants in the tests.
 from .nf4 import (nf4_table, quantize, dequantize, dequantize_bf16_bits, pack_codes,
                   unpack_codes, layer_error, storage_bytes, protect_count, topk,
                   NF4Quant)
-from .lora import fwd, bwd, merge
+from .lora import fwd, bwd, adapter_grads, merge
 
 __all__ = ["nf4_table", "quantize", "dequantize", "dequantize_bf16_bits", "pack_codes",
            "unpack_codes", "layer_error", "storage_bytes", "protect_count", "topk",
-           "NF4Quant", "fwd", "bwd", "merge"]
+           "NF4Quant", "fwd", "bwd", "adapter_grads", "merge"]

@@ -34,24 +34,37 @@ def fwd(X, W_hat, L1, L2, s: float):
     return Y, T
 
 
+def adapter_grads(X, dY, L1, L2, s: float):
+    """Adapter part of the backward pass of equation (3) (no dX).
+
+    Chain rule on Y = X W_st^T + s (X L1) L2 for the two adapter factors:
+        G   = s dY L2^T          [M][r]
+        dL2 = s (X L1)^T dY      [r][o]
+        dL1 = X^T G              [h][r]
+    Every token contributes a separate term to dL1 and dL2, so the gradients
+    of a batch are the sums of the gradients of any split of its tokens.
+    Returns (G, dL1, dL2) in fp64.
+    """
+    X, dY, A, B = _f64(X), _f64(dY), _f64(L1), _f64(L2)
+    T = X @ A
+    G = s * (dY @ B.T)
+    dL2 = s * (T.T @ dY)
+    dL1 = X.T @ G
+    return G, dL1, dL2
+
+
 def bwd(X, dY, W_hat, L1, L2, s: float):
     """Backward pass of equation (3) for the adapters and the input.
 
     The frozen base gets no gradient: it is read at high precision to carry
     the gradient to X ("Lesson 17. What QLoRA Actually Costs", Warm-up; the
-    QLoRA blog's "One training step" section).  Chain rule on
-    Y = X W_st^T + s (X L1) L2:
-        G   = s dY L2^T          [M][r]
-        dL2 = s (X L1)^T dY      [r][o]
-        dL1 = X^T G              [h][r]
+    QLoRA blog's "One training step" section).  With G, dL1, dL2 from
+    adapter_grads:
         dX  = dY W_st + G L1^T   [M][h]
     Returns (dX, dL1, dL2, G) in fp64.
     """
-    X, dY, W, A, B = _f64(X), _f64(dY), _f64(W_hat), _f64(L1), _f64(L2)
-    T = X @ A
-    G = s * (dY @ B.T)
-    dL2 = s * (T.T @ dY)
-    dL1 = X.T @ G
+    G, dL1, dL2 = adapter_grads(X, dY, L1, L2, s)
+    dY, W, A = _f64(dY), _f64(W_hat), _f64(L1)
     dX = dY @ W + G @ A.T
     return dX, dL1, dL2, G
 
