@@ -177,6 +177,73 @@ nf4_status nf4lora_bwd(const nf4_tensor *W, const uint16_t *X, const uint16_t *d
                        void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The same layer with the frozen weight kept in bf16 instead of NF4: the
+ * protected linears of AQLoRA (section 3.2 Precision allocation: the K
+ * linears with the largest NF4 reconstruction error stay in 16-bit and skip
+ * the per-step dequantization).  W is bf16 [rows = o][cols = h] with rows and
+ * cols multiples of 64 and rows * cols < 2^31; it feeds the same fused
+ * kernels (no dequantization step).  Every other argument, the workspace
+ * (nf4_workspace_bytes with the same rows and cols), the outputs and the
+ * errors are those of nf4lora_fwd / nf4lora_bwd.
+ */
+nf4_status bf16lora_fwd(const uint16_t *W, int64_t rows, int64_t cols, const uint16_t *X, int64_t M,
+                        const uint16_t *L1, const uint16_t *L2, int32_t r, float s,
+                        uint16_t *Y, uint16_t *T_out,
+                        void *ws, size_t ws_bytes, void *stream);
+nf4_status bf16lora_bwd(const uint16_t *W, int64_t rows, int64_t cols, const uint16_t *X,
+                        const uint16_t *dY, int64_t M,
+                        const uint16_t *L1, const uint16_t *L2, int32_t r, float s,
+                        const uint16_t *T, uint16_t *dX, float *dL1, float *dL2,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * One linear of a stack run by nf4_stack_fwd / nf4_stack_bwd.  The frozen
+ * weight is either NF4 (q) or a protected bf16 weight (w_bf16, [rows][cols]);
+ * exactly one of the two is set.  r > 0 gives the linear an adapter (L1, L2,
+ * s as in nf4lora_fwd); r == 0 means no adapter (AQLoRA's adapter placement,
+ * section 3.3, leaves some linears without one): the forward is Y = X W^T
+ * and the backward only carries dX.
+ *   X  [M][h], Y [M][o], T [M][r] (saved by the forward when non-NULL and
+ *   handed to the backward), dY [M][o], dX [M][h] or NULL, dL1 [h][r],
+ *   dL2 [r][o].  All device pointers, caller-owned.
+ */
+typedef struct {
+    const nf4_tensor *q;
+    const uint16_t *w_bf16;
+    int64_t rows, cols;
+    int32_t r;
+    float s;
+    const uint16_t *L1, *L2;
+    const uint16_t *X;
+    uint16_t *Y, *T;
+    const uint16_t *dY;
+    uint16_t *dX;
+    float *dL1, *dL2;
+} nf4_linear;
+
+/* Workspace bytes for running any linear of the stack (host output). */
+nf4_status nf4_stack_workspace_bytes(const nf4_linear *layers, int32_t n, int64_t M, size_t *bytes);
+
+/*
+ * Forward over layers[0 .. n) in order, each as nf4lora_fwd / bf16lora_fwd
+ * (or the plain product when r == 0), sharing one workspace.  Stops at the
+ * first failing linear and returns its status.
+ */
+nf4_status nf4_stack_fwd(const nf4_linear *layers, int32_t n, int64_t M, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/*
+ * Backward over layers[n-1] down to layers[cut] (0 <= cut <= n): the early
+ * backward stop of AQLoRA's speed setting (section 3.3 Adapter placement and
+ * section 6: no computation below the cutoff).  Linears below cut are not
+ * touched; a linear whose dX is NULL gets no input gradient (the lowest
+ * adapted linears need none).  Each linear runs as nf4lora_bwd /
+ * bf16lora_bwd, or as the plain input-gradient product when r == 0.
+ */
+nf4_status nf4_stack_bwd(const nf4_linear *layers, int32_t n, int32_t cut, int64_t M, void *ws,
+                         size_t ws_bytes, void *stream);
+
+/*
  * The fused NF4 matmul on its own (the base product inside nf4lora_fwd and
  * nf4lora_bwd), with an optional low-rank term in the same output tile:
  *   transpose = 0:  C [M][o] = A [M][h] * W_hat^T + A2 [M][R] * B2 [o][R]^T

@@ -35,9 +35,18 @@ class _NF4Tensor(ctypes.Structure):
                 ("dq_scale", ctypes.c_void_p)]
 
 
+class _NF4Linear(ctypes.Structure):
+    _fields_ = [("q", ctypes.POINTER(_NF4Tensor)), ("w_bf16", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("r", ctypes.c_int32), ("s", ctypes.c_float), ("L1", ctypes.c_void_p),
+                ("L2", ctypes.c_void_p), ("X", ctypes.c_void_p), ("Y", ctypes.c_void_p), ("T", ctypes.c_void_p),
+                ("dY", ctypes.c_void_p), ("dX", ctypes.c_void_p), ("dL1", ctypes.c_void_p),
+                ("dL2", ctypes.c_void_p)]
+
+
 _vp, _i64, _i32, _sz, _f32, _f64 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t,
                                     ctypes.c_float, ctypes.c_double)
 _T = ctypes.POINTER(_NF4Tensor)
+_LP = ctypes.POINTER(_NF4Linear)
 _SIGS = {
     "nf4_abi_version": ([], ctypes.c_int),
     "nf4_status_str": ([ctypes.c_int], ctypes.c_char_p),
@@ -49,10 +58,16 @@ _SIGS = {
     "nf4_workspace_bytes": ([_i32, _i64, _i64, _i64, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
     "nf4lora_fwd": ([_T, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "nf4lora_bwd": ([_T, _vp, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "bf16lora_fwd": ([_vp, _i64, _i64, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "bf16lora_bwd": ([_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+                     ctypes.c_int),
     "nf4_matmul": ([_T, _i32, _vp, _i64, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
     "nf4_layer_error": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _sz, _vp], ctypes.c_int),
     "nf4_topk": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
     "nf4_protect_count": ([_f64, _i32], _i32),
+    "nf4_stack_workspace_bytes": ([_LP, _i32, _i64, ctypes.POINTER(_sz)], ctypes.c_int),
+    "nf4_stack_fwd": ([_LP, _i32, _i64, _vp, _sz, _vp], ctypes.c_int),
+    "nf4_stack_bwd": ([_LP, _i32, _i32, _i64, _vp, _sz, _vp], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -198,6 +213,47 @@ def bwd(q: NF4Weight, X: torch.Tensor, dY: torch.Tensor, L1: torch.Tensor, L2: t
     return dX, dL1, dL2
 
 
+def bf16_workspace(op: int, M: int, W: torch.Tensor, r: int) -> torch.Tensor:
+    """Workspace for bf16lora_fwd / bf16lora_bwd on a bf16 weight [o][h]."""
+    return torch.empty(workspace_bytes(op, M, W.shape[0], W.shape[1], r), dtype=torch.uint8, device=W.device)
+
+
+def bf16_fwd(W: torch.Tensor, X: torch.Tensor, L1: torch.Tensor, L2: torch.Tensor, s: float, want_T: bool = True,
+             ws: torch.Tensor | None = None, out: torch.Tensor | None = None, T_out: torch.Tensor | None = None):
+    """bf16lora_fwd (a protected linear, bf16 W [o][h]): returns (Y, T or None)."""
+    assert W.dtype == torch.bfloat16 and W.is_cuda and W.is_contiguous() and W.dim() == 2
+    o, h = W.shape
+    M, r = X.shape[0], L1.shape[1]
+    Y = out if out is not None else torch.empty(M, o, dtype=torch.bfloat16, device=X.device)
+    T = T_out if T_out is not None else (
+        torch.empty(M, r, dtype=torch.bfloat16, device=X.device) if want_T else None)
+    if ws is None:
+        ws = bf16_workspace(NF4_OP_FWD, M, W, r)
+    _check(_lib.bf16lora_fwd(_ptr(W), o, h, _ptr(_u16(X)), M, _ptr(_u16(L1)), _ptr(_u16(L2)), r, float(s),
+                             _ptr(Y), _ptr(T), _ptr(ws), ws.numel(), _stream()), "bf16lora_fwd")
+    return Y, T
+
+
+def bf16_bwd(W: torch.Tensor, X: torch.Tensor, dY: torch.Tensor, L1: torch.Tensor, L2: torch.Tensor, s: float,
+             T: torch.Tensor | None = None, want_dX: bool = True, ws: torch.Tensor | None = None, outs=None):
+    """bf16lora_bwd: returns (dX or None, dL1, dL2)."""
+    assert W.dtype == torch.bfloat16 and W.is_cuda and W.is_contiguous() and W.dim() == 2
+    o, h = W.shape
+    M, r = X.shape[0], L1.shape[1]
+    if outs is None:
+        dX = torch.empty(M, h, dtype=torch.bfloat16, device=X.device) if want_dX else None
+        dL1 = torch.empty(h, r, dtype=torch.float32, device=X.device)
+        dL2 = torch.empty(r, o, dtype=torch.float32, device=X.device)
+    else:
+        dX, dL1, dL2 = outs
+    if ws is None:
+        ws = bf16_workspace(NF4_OP_BWD, M, W, r)
+    _check(_lib.bf16lora_bwd(_ptr(W), o, h, _ptr(_u16(X)), _ptr(_u16(dY)), M, _ptr(_u16(L1)), _ptr(_u16(L2)),
+                             r, float(s), _ptr(T), _ptr(dX), _ptr(dL1), _ptr(dL2), _ptr(ws), ws.numel(), _stream()),
+           "bf16lora_bwd")
+    return dX, dL1, dL2
+
+
 def layer_error(W: torch.Tensor, dq_group: int = 0, out: torch.Tensor | None = None,
                 ws: torch.Tensor | None = None) -> torch.Tensor:
     """nf4_layer_error: a cuda float64 tensor of shape [1] (no host sync)."""
@@ -230,3 +286,46 @@ def topk(errors: torch.Tensor, k: int, out: torch.Tensor | None = None) -> torch
     idx = out if out is not None else torch.empty(max(k, 1), dtype=torch.int32, device=errors.device)
     _check(_lib.nf4_topk(_ptr(errors), errors.numel(), k, _ptr(idx), _stream()), "nf4_topk")
     return idx[:k]
+
+
+# ---------------------------------------------------------------------------
+# stack runner
+# ---------------------------------------------------------------------------
+
+class Stack:
+    """A list of linears for nf4_stack_fwd / nf4_stack_bwd.
+
+    Each linear is a dict: weight ("q": NF4Weight or "w": bf16 tensor [o][h]),
+    optional adapter ("r", "s", "L1", "L2"; r = 0 or absent: none) and the
+    buffers "X", "Y", "T", "dY", "dX", "dL1", "dL2" (tensors or None).  The
+    tensors must stay alive as long as the Stack is used.
+    """
+
+    def __init__(self, linears, M: int):
+        self.M = M
+        self.linears = linears
+        self.arr = (_NF4Linear * len(linears))()
+        for i, L in enumerate(linears):
+            e = self.arr[i]
+            if L.get("q") is not None:
+                e.q = ctypes.pointer(L["q"].desc)
+            else:
+                W = L["w"]
+                assert W.dtype == torch.bfloat16 and W.is_contiguous()
+                e.w_bf16, e.rows, e.cols = _ptr(W), W.shape[0], W.shape[1]
+            e.r, e.s = int(L.get("r", 0)), float(L.get("s", 0.0))
+            for k in ("L1", "L2", "X", "Y", "T", "dY", "dX", "dL1", "dL2"):
+                setattr(e, k, _ptr(L.get(k)))
+        n = _sz()
+        _check(_lib.nf4_stack_workspace_bytes(self.arr, len(linears), M, ctypes.byref(n)),
+               "nf4_stack_workspace_bytes")
+        self.ws = torch.empty(max(int(n.value), 16), dtype=torch.uint8, device="cuda")
+
+    def fwd(self):
+        _check(_lib.nf4_stack_fwd(self.arr, len(self.linears), self.M, _ptr(self.ws), self.ws.numel(), _stream()),
+               "nf4_stack_fwd")
+
+    def bwd(self, cut: int = 0):
+        _check(_lib.nf4_stack_bwd(self.arr, len(self.linears), cut, self.M, _ptr(self.ws), self.ws.numel(),
+                                  _stream()), "nf4_stack_bwd")
+

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -169,14 +170,223 @@ size_t error_ws(int64_t rows, int64_t cols) {
   return align256((size_t)(ng > 0 ? ng : 1) * 16);
 }
 
-nf4_status check_layer(const nf4_tensor* W, int64_t M, int32_t r) {
+// The frozen weight of a layer as the fused GEMM reads it: NF4 (with fp32 or
+// double-quantized scales) or bf16.  rows = o, cols = h.
+struct WSrc {
+  int src;
+  int64_t rows, cols;
+  const uint16_t* wb;
+  const uint8_t* codes;
+  const void* absmax;
+  const float* dqs;
+  Range buf[3];  // the weight's buffers, for the aliasing checks
+};
+
+nf4_status layer_shape(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0 || rows % kBlock != 0 || cols % kBlock != 0) return NF4_ERR_SHAPE;
+  if (rows > INT32_MAX / 2 || cols > INT32_MAX / 2) return NF4_ERR_SHAPE;
+  return NF4_OK;
+}
+
+nf4_status wsrc_nf4(const nf4_tensor* W, WSrc* w) {
   nf4_status st = check_tensor(W);
   if (st != NF4_OK) return st;
-  if (W->rows % kBlock != 0 || W->rows <= 0 || W->cols <= 0) return NF4_ERR_SHAPE;
-  if (W->rows > INT32_MAX / 2 || W->cols > INT32_MAX / 2) return NF4_ERR_SHAPE;
+  st = layer_shape(W->rows, W->cols);
+  if (st != NF4_OK) return st;
+  size_t cb, ab, db;
+  tensor_sizes(W->rows, W->cols, W->dq_group, &cb, &ab, &db);
+  w->src = W->dq_group ? kSrcNF4DQ : kSrcNF4;
+  w->rows = W->rows;
+  w->cols = W->cols;
+  w->wb = nullptr;
+  w->codes = W->codes;
+  w->absmax = W->absmax;
+  w->dqs = W->dq_scale;
+  w->buf[0] = rng(W->codes, cb);
+  w->buf[1] = rng(W->absmax, ab);
+  w->buf[2] = rng(W->dq_scale, db);
+  return NF4_OK;
+}
+
+nf4_status wsrc_bf16(const uint16_t* W, int64_t rows, int64_t cols, WSrc* w) {
+  nf4_status st = layer_shape(rows, cols);
+  if (st != NF4_OK) return st;
+  if (rows * cols > (int64_t)INT32_MAX) return NF4_ERR_SHAPE;  // byte offsets stay below 4 GiB
+  if (!W) return NF4_ERR_NULL;
+  if (!aligned16(W)) return NF4_ERR_ALIGN;
+  w->src = kSrcBF16;
+  w->rows = rows;
+  w->cols = cols;
+  w->wb = W;
+  w->codes = nullptr;
+  w->absmax = nullptr;
+  w->dqs = nullptr;
+  w->buf[0] = rng(W, (size_t)(rows * cols * 2));
+  w->buf[1] = rng(nullptr, 0);
+  w->buf[2] = rng(nullptr, 0);
+  return NF4_OK;
+}
+
+nf4_status check_batch(int64_t M, int32_t r) {
   if (M < 0 || M > ((int64_t)1 << 31)) return NF4_ERR_SHAPE;
   if (r < 1 || r > 256) return NF4_ERR_SHAPE;
   return NF4_OK;
+}
+
+hipError_t gemm(int mode, const WSrc& w, const uint16_t* A, const uint16_t* A2, const uint16_t* B2, int R,
+                uint16_t* C, int64_t M, hipStream_t st) {
+  const int64_t N = mode == MODE_FWD ? w.rows : w.cols;
+  const int64_t K = mode == MODE_FWD ? w.cols : w.rows;
+  return launch_nf4_gemm(mode, w.src, A, w.wb, w.codes, w.absmax, w.dqs, A2, B2, R, C, M, (int)N, (int)K,
+                         nf4_consts(), st);
+}
+
+nf4_status layer_fwd(const WSrc& W, const uint16_t* X, int64_t M, const uint16_t* L1, const uint16_t* L2,
+                            int32_t r, float s, uint16_t* Y, uint16_t* T_out, void* ws, size_t ws_bytes,
+                            void* stream) {
+  nf4_status st = check_batch(M, r);
+  if (st != NF4_OK) return st;
+  if (M == 0) return NF4_OK;
+  if (!X || !L1 || !L2 || !Y) return NF4_ERR_NULL;
+  if (!aligned16(X) || !aligned16(L1) || !aligned16(L2) || !aligned16(Y) || (T_out && !aligned16(T_out)))
+    return NF4_ERR_ALIGN;
+  const int64_t o = W.rows, h = W.cols;
+  const FwdPlan p = plan_fwd(M, o, h, r);
+  if (!ws) return NF4_ERR_WORKSPACE;
+  if (ws_bytes < p.total) return NF4_ERR_WORKSPACE;
+  if (!aligned16(ws)) return NF4_ERR_ALIGN;
+  const Range ins[] = {rng(X, (size_t)M * h * 2), rng(L1, (size_t)h * r * 2), rng(L2, (size_t)r * o * 2),
+                       W.buf[0], W.buf[1], W.buf[2]};
+  const Range outs[] = {rng(Y, (size_t)M * o * 2), rng(T_out, T_out ? (size_t)M * r * 2 : 0),
+                        rng(ws, p.total)};
+  for (const Range& a : outs) {
+    for (const Range& b : ins)
+      if (overlap(a, b)) return NF4_ERR_ALIAS;
+  }
+  if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2])) return NF4_ERR_ALIAS;
+
+  hipStream_t hs = (hipStream_t)stream;
+  uint8_t* w = (uint8_t*)ws;
+  uint16_t* l1t = (uint16_t*)(w + p.off_l1t);
+  uint16_t* l2t = (uint16_t*)(w + p.off_l2t);
+  uint16_t* ts = (uint16_t*)(w + p.off_ts);
+  float* part = (float*)(w + p.off_part);
+  unsigned* cnt = (unsigned*)(w + p.off_cnt);
+  // one prep launch: L1^T [RP][h] (rows >= r zero), L2^T [o][RP] (columns >= r zero), counters
+  PrepArgs pa{};
+  pa.pad[0] = pad_job(L1, 1, r, r, h, l1t, p.RP, h);
+  pa.pad[1] = pad_job(L2, 1, o, o, r, l2t, o, p.RP);
+  pa.zero[0] = ZeroJob{cnt, p.ncnt};
+  NF4_TRY(launch_prep(pa, hs));
+  // T = X L1 (split K, fixed-order reduction) -> T_out (bf16) and s*T (bf16, padded)
+  NtArgs nt{X, l1t, M, (int)h, p.ks, p.kr, part, cnt, r, 1.0f, T_out, r, s, ts};
+  NF4_TRY(launch_skinny_nt(nt, p.RP, hs));
+  // Y = X w_hat^T + (s T) L2
+  NF4_TRY(gemm(MODE_FWD, W, X, ts, l2t, p.RP, Y, M, hs));
+  return NF4_OK;
+}
+
+nf4_status layer_bwd(const WSrc& W, const uint16_t* X, const uint16_t* dY, int64_t M, const uint16_t* L1,
+                            const uint16_t* L2, int32_t r, float s, const uint16_t* T, uint16_t* dX, float* dL1,
+                            float* dL2, void* ws, size_t ws_bytes, void* stream) {
+  nf4_status st = check_batch(M, r);
+  if (st != NF4_OK) return st;
+  if (!dL1 || !dL2) return NF4_ERR_NULL;
+  if (M > 0 && (!X || !dY || !L1 || !L2)) return NF4_ERR_NULL;
+  const int64_t o = W.rows, h = W.cols;
+  const BwdPlan p = plan_bwd(M, o, h, r);
+  if (!ws) return NF4_ERR_WORKSPACE;
+  if (ws_bytes < p.total) return NF4_ERR_WORKSPACE;
+  if (!aligned16(ws) || !aligned16(dL1) || !aligned16(dL2)) return NF4_ERR_ALIGN;
+  if (M > 0 && (!aligned16(X) || !aligned16(dY) || !aligned16(L1) || !aligned16(L2) || (T && !aligned16(T)) ||
+                (dX && !aligned16(dX))))
+    return NF4_ERR_ALIGN;
+  const Range ins[] = {rng(X, (size_t)M * h * 2),     rng(dY, (size_t)M * o * 2),
+                       rng(L1, (size_t)h * r * 2),    rng(L2, (size_t)r * o * 2),
+                       rng(T, T ? (size_t)M * r * 2 : 0), W.buf[0],
+                       W.buf[1],                      W.buf[2]};
+  const Range outs[] = {rng(dX, dX ? (size_t)M * h * 2 : 0), rng(dL1, (size_t)h * r * 4),
+                        rng(dL2, (size_t)r * o * 4), rng(ws, p.total)};
+  for (const Range& a : outs) {
+    for (const Range& b : ins)
+      if (overlap(a, b)) return NF4_ERR_ALIAS;
+  }
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return NF4_ERR_ALIAS;
+
+  hipStream_t hs = (hipStream_t)stream;
+  uint8_t* w = (uint8_t*)ws;
+  unsigned* cnt = (unsigned*)(w + p.off_cnt);
+  if (M == 0) {
+    // empty token set: both adapter gradients are exactly zero
+    PrepArgs pa{};
+    pa.zero[0] = ZeroJob{(uint32_t*)dL2, (int64_t)r * o};
+    pa.zero[1] = ZeroJob{(uint32_t*)dL1, (int64_t)h * r};
+    NF4_TRY(launch_prep(pa, hs));
+    return NF4_OK;
+  }
+  uint16_t* l1t = (uint16_t*)(w + p.off_l1t);
+  uint16_t* l1p = (uint16_t*)(w + p.off_l1p);
+  uint16_t* l2p = (uint16_t*)(w + p.off_l2p);
+  uint16_t* tb = (uint16_t*)(w + p.off_tb);
+  uint16_t* g = (uint16_t*)(w + p.off_g);
+  float* pnt = (float*)(w + p.off_pnt);
+  float* p2 = (float*)(w + p.off_p2);
+  float* p1 = (float*)(w + p.off_p1);
+
+  // one prep launch: L1 [h][RP], L2 [RP][o], counters, and L1^T [RP][h] when T is recomputed
+  // or T [M][RP] when the given T has rows that are not whole 16-byte chunks
+  PrepArgs pa{};
+  pa.pad[0] = pad_job(L1, r, 1, h, r, l1p, h, p.RP);
+  pa.pad[1] = pad_job(L2, o, 1, r, o, l2p, p.RP, o);
+  if (!T) pa.pad[2] = pad_job(L1, 1, r, r, h, l1t, p.RP, h);
+  else if (r % 8 != 0) pa.pad[2] = pad_job(T, r, 1, M, r, tb, M, p.RP);
+  pa.zero[0] = ZeroJob{cnt, p.ncnt};
+  NF4_TRY(launch_prep(pa, hs));
+  const uint16_t* tsrc = T;
+  int ldt = r;
+  if (!T) {
+    NtArgs nt{X, l1t, M, (int)h, p.ks_t, p.kr_t, pnt, cnt + p.cnt_t, r, 1.0f, nullptr, 0, 1.0f, tb};
+    NF4_TRY(launch_skinny_nt(nt, p.RP, hs));
+    tsrc = tb;
+    ldt = p.RP;
+  } else if (r % 8 != 0) {
+    tsrc = tb;  // padded by the prep launch: the TN product reads rows in 16-byte chunks
+    ldt = p.RP;
+  }
+  // G = s dY L2^T  (bf16 [M][RP], columns >= r zero)
+  NtArgs ng{dY, l2p, M, (int)o, p.ks_g, p.kr_g, pnt, cnt + p.cnt_g, r, 1.0f, nullptr, 0, s, g};
+  NF4_TRY(launch_skinny_nt(ng, p.RP, hs));
+  // dL2 = s T^T dY  ([r][o]),  dL1 = X^T G  (stored [h][r])
+  TnArgs t2{tsrc, ldt, r, dY, M, (int)o, p.ms2, p.mr2, p2, cnt + p.cnt_2, s, 0, dL2};
+  NF4_TRY(launch_skinny_tn(t2, p.RP, hs));
+  TnArgs t1{g, p.RP, r, X, M, (int)h, p.ms1, p.mr1, p1, cnt + p.cnt_1, 1.0f, 1, dL1};
+  NF4_TRY(launch_skinny_tn(t1, p.RP, hs));
+  // dX = dY w_hat + G L1^T
+  if (dX) {
+    NF4_TRY(gemm(MODE_DX, W, dY, g, l1p, p.RP, dX, M, hs));
+  }
+  return NF4_OK;
+}
+
+nf4_status wsrc_linear(const nf4_linear& L, WSrc* w) {
+  if ((L.q != nullptr) == (L.w_bf16 != nullptr)) return NF4_ERR_ARG;  // exactly one weight
+  return L.q ? wsrc_nf4(L.q, w) : wsrc_bf16(L.w_bf16, L.rows, L.cols, w);
+}
+
+// the base product alone (a linear without adapter): Y = X W^T, or dX = dY W
+nf4_status plain_product(int mode, const WSrc& w, const uint16_t* A, uint16_t* C, int64_t M, void* stream) {
+  if (M < 0 || M > ((int64_t)1 << 31)) return NF4_ERR_SHAPE;
+  if (M == 0) return NF4_OK;
+  if (!A || !C) return NF4_ERR_NULL;
+  if (!aligned16(A) || !aligned16(C)) return NF4_ERR_ALIGN;
+  const int64_t K = mode == MODE_FWD ? w.cols : w.rows, N = mode == MODE_FWD ? w.rows : w.cols;
+  const Range out = rng(C, (size_t)M * N * 2);
+  if (overlap(out, rng(A, (size_t)M * K * 2)) || overlap(out, w.buf[0]) || overlap(out, w.buf[1]) ||
+      overlap(out, w.buf[2]))
+    return NF4_ERR_ALIAS;
+  return hip_status(gemm(mode, w, A, nullptr, nullptr, 0, C, M, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -267,136 +477,37 @@ nf4_status nf4_workspace_bytes(int32_t op, int64_t M, int64_t rows, int64_t cols
 
 nf4_status nf4lora_fwd(const nf4_tensor* W, const uint16_t* X, int64_t M, const uint16_t* L1, const uint16_t* L2,
                        int32_t r, float s, uint16_t* Y, uint16_t* T_out, void* ws, size_t ws_bytes, void* stream) {
-  nf4_status st = check_layer(W, M, r);
+  WSrc w;
+  nf4_status st = wsrc_nf4(W, &w);
   if (st != NF4_OK) return st;
-  if (M == 0) return NF4_OK;
-  if (!X || !L1 || !L2 || !Y) return NF4_ERR_NULL;
-  if (!aligned16(X) || !aligned16(L1) || !aligned16(L2) || !aligned16(Y) || (T_out && !aligned16(T_out)))
-    return NF4_ERR_ALIGN;
-  const int64_t o = W->rows, h = W->cols;
-  const FwdPlan p = plan_fwd(M, o, h, r);
-  if (!ws) return NF4_ERR_WORKSPACE;
-  if (ws_bytes < p.total) return NF4_ERR_WORKSPACE;
-  if (!aligned16(ws)) return NF4_ERR_ALIGN;
-  size_t cb, ab, db;
-  tensor_sizes(o, h, W->dq_group, &cb, &ab, &db);
-  const Range ins[] = {rng(X, (size_t)M * h * 2), rng(L1, (size_t)h * r * 2), rng(L2, (size_t)r * o * 2),
-                       rng(W->codes, cb), rng(W->absmax, ab), rng(W->dq_scale, db)};
-  const Range outs[] = {rng(Y, (size_t)M * o * 2), rng(T_out, T_out ? (size_t)M * r * 2 : 0),
-                        rng(ws, p.total)};
-  for (const Range& a : outs) {
-    for (const Range& b : ins)
-      if (overlap(a, b)) return NF4_ERR_ALIAS;
-  }
-  if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2])) return NF4_ERR_ALIAS;
-
-  hipStream_t hs = (hipStream_t)stream;
-  uint8_t* w = (uint8_t*)ws;
-  uint16_t* l1t = (uint16_t*)(w + p.off_l1t);
-  uint16_t* l2t = (uint16_t*)(w + p.off_l2t);
-  uint16_t* ts = (uint16_t*)(w + p.off_ts);
-  float* part = (float*)(w + p.off_part);
-  unsigned* cnt = (unsigned*)(w + p.off_cnt);
-  // one prep launch: L1^T [RP][h] (rows >= r zero), L2^T [o][RP] (columns >= r zero), counters
-  PrepArgs pa{};
-  pa.pad[0] = pad_job(L1, 1, r, r, h, l1t, p.RP, h);
-  pa.pad[1] = pad_job(L2, 1, o, o, r, l2t, o, p.RP);
-  pa.zero[0] = ZeroJob{cnt, p.ncnt};
-  NF4_TRY(launch_prep(pa, hs));
-  // T = X L1 (split K, fixed-order reduction) -> T_out (bf16) and s*T (bf16, padded)
-  NtArgs nt{X, l1t, M, (int)h, p.ks, p.kr, part, cnt, r, 1.0f, T_out, r, s, ts};
-  NF4_TRY(launch_skinny_nt(nt, p.RP, hs));
-  // Y = X w_hat^T + (s T) L2
-  NF4_TRY(launch_nf4_gemm(MODE_FWD, W->dq_group != 0, X, W->codes, W->absmax, W->dq_scale, ts, l2t, p.RP, Y, M,
-                          (int)o, (int)h, nf4_consts(), hs));
-  return NF4_OK;
+  return layer_fwd(w, X, M, L1, L2, r, s, Y, T_out, ws, ws_bytes, stream);
 }
 
 nf4_status nf4lora_bwd(const nf4_tensor* W, const uint16_t* X, const uint16_t* dY, int64_t M, const uint16_t* L1,
                        const uint16_t* L2, int32_t r, float s, const uint16_t* T, uint16_t* dX, float* dL1,
                        float* dL2, void* ws, size_t ws_bytes, void* stream) {
-  nf4_status st = check_layer(W, M, r);
+  WSrc w;
+  nf4_status st = wsrc_nf4(W, &w);
   if (st != NF4_OK) return st;
-  if (!dL1 || !dL2) return NF4_ERR_NULL;
-  if (M > 0 && (!X || !dY || !L1 || !L2)) return NF4_ERR_NULL;
-  const int64_t o = W->rows, h = W->cols;
-  const BwdPlan p = plan_bwd(M, o, h, r);
-  if (!ws) return NF4_ERR_WORKSPACE;
-  if (ws_bytes < p.total) return NF4_ERR_WORKSPACE;
-  if (!aligned16(ws) || !aligned16(dL1) || !aligned16(dL2)) return NF4_ERR_ALIGN;
-  if (M > 0 && (!aligned16(X) || !aligned16(dY) || !aligned16(L1) || !aligned16(L2) || (T && !aligned16(T)) ||
-                (dX && !aligned16(dX))))
-    return NF4_ERR_ALIGN;
-  size_t cb, ab, db;
-  tensor_sizes(o, h, W->dq_group, &cb, &ab, &db);
-  const Range ins[] = {rng(X, (size_t)M * h * 2),     rng(dY, (size_t)M * o * 2),
-                       rng(L1, (size_t)h * r * 2),    rng(L2, (size_t)r * o * 2),
-                       rng(T, T ? (size_t)M * r * 2 : 0), rng(W->codes, cb),
-                       rng(W->absmax, ab),            rng(W->dq_scale, db)};
-  const Range outs[] = {rng(dX, dX ? (size_t)M * h * 2 : 0), rng(dL1, (size_t)h * r * 4),
-                        rng(dL2, (size_t)r * o * 4), rng(ws, p.total)};
-  for (const Range& a : outs) {
-    for (const Range& b : ins)
-      if (overlap(a, b)) return NF4_ERR_ALIAS;
-  }
-  for (int i = 0; i < 4; ++i)
-    for (int j = i + 1; j < 4; ++j)
-      if (overlap(outs[i], outs[j])) return NF4_ERR_ALIAS;
+  return layer_bwd(w, X, dY, M, L1, L2, r, s, T, dX, dL1, dL2, ws, ws_bytes, stream);
+}
 
-  hipStream_t hs = (hipStream_t)stream;
-  uint8_t* w = (uint8_t*)ws;
-  unsigned* cnt = (unsigned*)(w + p.off_cnt);
-  if (M == 0) {
-    // empty token set: both adapter gradients are exactly zero
-    PrepArgs pa{};
-    pa.zero[0] = ZeroJob{(uint32_t*)dL2, (int64_t)r * o};
-    pa.zero[1] = ZeroJob{(uint32_t*)dL1, (int64_t)h * r};
-    NF4_TRY(launch_prep(pa, hs));
-    return NF4_OK;
-  }
-  uint16_t* l1t = (uint16_t*)(w + p.off_l1t);
-  uint16_t* l1p = (uint16_t*)(w + p.off_l1p);
-  uint16_t* l2p = (uint16_t*)(w + p.off_l2p);
-  uint16_t* tb = (uint16_t*)(w + p.off_tb);
-  uint16_t* g = (uint16_t*)(w + p.off_g);
-  float* pnt = (float*)(w + p.off_pnt);
-  float* p2 = (float*)(w + p.off_p2);
-  float* p1 = (float*)(w + p.off_p1);
+nf4_status bf16lora_fwd(const uint16_t* W, int64_t rows, int64_t cols, const uint16_t* X, int64_t M,
+                        const uint16_t* L1, const uint16_t* L2, int32_t r, float s, uint16_t* Y, uint16_t* T_out,
+                        void* ws, size_t ws_bytes, void* stream) {
+  WSrc w;
+  nf4_status st = wsrc_bf16(W, rows, cols, &w);
+  if (st != NF4_OK) return st;
+  return layer_fwd(w, X, M, L1, L2, r, s, Y, T_out, ws, ws_bytes, stream);
+}
 
-  // one prep launch: L1 [h][RP], L2 [RP][o], counters, and L1^T [RP][h] when T is recomputed
-  // or T [M][RP] when the given T has rows that are not whole 16-byte chunks
-  PrepArgs pa{};
-  pa.pad[0] = pad_job(L1, r, 1, h, r, l1p, h, p.RP);
-  pa.pad[1] = pad_job(L2, o, 1, r, o, l2p, p.RP, o);
-  if (!T) pa.pad[2] = pad_job(L1, 1, r, r, h, l1t, p.RP, h);
-  else if (r % 8 != 0) pa.pad[2] = pad_job(T, r, 1, M, r, tb, M, p.RP);
-  pa.zero[0] = ZeroJob{cnt, p.ncnt};
-  NF4_TRY(launch_prep(pa, hs));
-  const uint16_t* tsrc = T;
-  int ldt = r;
-  if (!T) {
-    NtArgs nt{X, l1t, M, (int)h, p.ks_t, p.kr_t, pnt, cnt + p.cnt_t, r, 1.0f, nullptr, 0, 1.0f, tb};
-    NF4_TRY(launch_skinny_nt(nt, p.RP, hs));
-    tsrc = tb;
-    ldt = p.RP;
-  } else if (r % 8 != 0) {
-    tsrc = tb;  // padded by the prep launch: the TN product reads rows in 16-byte chunks
-    ldt = p.RP;
-  }
-  // G = s dY L2^T  (bf16 [M][RP], columns >= r zero)
-  NtArgs ng{dY, l2p, M, (int)o, p.ks_g, p.kr_g, pnt, cnt + p.cnt_g, r, 1.0f, nullptr, 0, s, g};
-  NF4_TRY(launch_skinny_nt(ng, p.RP, hs));
-  // dL2 = s T^T dY  ([r][o]),  dL1 = X^T G  (stored [h][r])
-  TnArgs t2{tsrc, ldt, r, dY, M, (int)o, p.ms2, p.mr2, p2, cnt + p.cnt_2, s, 0, dL2};
-  NF4_TRY(launch_skinny_tn(t2, p.RP, hs));
-  TnArgs t1{g, p.RP, r, X, M, (int)h, p.ms1, p.mr1, p1, cnt + p.cnt_1, 1.0f, 1, dL1};
-  NF4_TRY(launch_skinny_tn(t1, p.RP, hs));
-  // dX = dY w_hat + G L1^T
-  if (dX) {
-    NF4_TRY(launch_nf4_gemm(MODE_DX, W->dq_group != 0, dY, W->codes, W->absmax, W->dq_scale, g, l1p, p.RP, dX, M,
-                            (int)h, (int)o, nf4_consts(), hs));
-  }
-  return NF4_OK;
+nf4_status bf16lora_bwd(const uint16_t* W, int64_t rows, int64_t cols, const uint16_t* X, const uint16_t* dY,
+                        int64_t M, const uint16_t* L1, const uint16_t* L2, int32_t r, float s, const uint16_t* T,
+                        uint16_t* dX, float* dL1, float* dL2, void* ws, size_t ws_bytes, void* stream) {
+  WSrc w;
+  nf4_status st = wsrc_bf16(W, rows, cols, &w);
+  if (st != NF4_OK) return st;
+  return layer_bwd(w, X, dY, M, L1, L2, r, s, T, dX, dL1, dL2, ws, ws_bytes, stream);
 }
 
 nf4_status nf4_matmul(const nf4_tensor* W, int32_t transpose, const uint16_t* A, int64_t M, const uint16_t* A2,
@@ -419,8 +530,10 @@ nf4_status nf4_matmul(const nf4_tensor* W, int32_t transpose, const uint16_t* A,
                        rng(W->codes, cb), rng(W->absmax, ab), rng(W->dq_scale, db)};
   for (const Range& b : ins)
     if (overlap(out, b)) return NF4_ERR_ALIAS;
-  return hip_status(launch_nf4_gemm(transpose ? MODE_DX : MODE_FWD, W->dq_group != 0, A, W->codes, W->absmax,
-                                    W->dq_scale, A2, B2, R, C, M, (int)N, (int)K, nf4_consts(), (hipStream_t)stream));
+  WSrc w;
+  st = wsrc_nf4(W, &w);
+  if (st != NF4_OK) return st;
+  return hip_status(gemm(transpose ? MODE_DX : MODE_FWD, w, A, A2, B2, R, C, M, (hipStream_t)stream));
 }
 
 nf4_status nf4_layer_error(const float* W, int64_t rows, int64_t cols, int32_t block, int32_t dq_group,
@@ -453,6 +566,61 @@ nf4_status nf4_topk(const double* err_dev, int32_t n, int32_t k, int32_t* idx_de
 int32_t nf4_protect_count(double rho, int32_t n) {
   if (!(rho >= 0.0 && rho <= 1.0) || n < 0) return -1;
   return (int32_t)std::floor(rho * (double)n + 0.5);
+}
+
+
+nf4_status nf4_stack_workspace_bytes(const nf4_linear* layers, int32_t n, int64_t M, size_t* bytes) {
+  if (!bytes || (n > 0 && !layers)) return NF4_ERR_NULL;
+  if (n < 0 || M < 0) return NF4_ERR_SHAPE;
+  size_t most = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const nf4_linear& L = layers[i];
+    WSrc w;
+    nf4_status st = wsrc_linear(L, &w);
+    if (st != NF4_OK) return st;
+    if (L.r == 0) continue;
+    if (L.r < 0 || L.r > 256) return NF4_ERR_SHAPE;
+    const size_t f = plan_fwd(M, w.rows, w.cols, L.r).total, b = plan_bwd(M, w.rows, w.cols, L.r).total;
+    most = std::max(most, std::max(f, b));
+  }
+  *bytes = most;
+  return NF4_OK;
+}
+
+nf4_status nf4_stack_fwd(const nf4_linear* layers, int32_t n, int64_t M, void* ws, size_t ws_bytes, void* stream) {
+  if (n > 0 && !layers) return NF4_ERR_NULL;
+  if (n < 0) return NF4_ERR_SHAPE;
+  for (int32_t i = 0; i < n; ++i) {
+    const nf4_linear& L = layers[i];
+    WSrc w;
+    nf4_status st = wsrc_linear(L, &w);
+    if (st == NF4_OK) {
+      st = L.r == 0 ? plain_product(MODE_FWD, w, L.X, L.Y, M, stream)
+                    : layer_fwd(w, L.X, M, L.L1, L.L2, L.r, L.s, L.Y, L.T, ws, ws_bytes, stream);
+    }
+    if (st != NF4_OK) return st;
+  }
+  return NF4_OK;
+}
+
+nf4_status nf4_stack_bwd(const nf4_linear* layers, int32_t n, int32_t cut, int64_t M, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (n > 0 && !layers) return NF4_ERR_NULL;
+  if (n < 0 || cut < 0 || cut > n) return NF4_ERR_SHAPE;
+  for (int32_t i = n - 1; i >= cut; --i) {
+    const nf4_linear& L = layers[i];
+    WSrc w;
+    nf4_status st = wsrc_linear(L, &w);
+    if (st == NF4_OK) {
+      if (L.r == 0) {
+        if (L.dX) st = plain_product(MODE_DX, w, L.dY, L.dX, M, stream);
+      } else {
+        st = layer_bwd(w, L.X, L.dY, M, L.L1, L.L2, L.r, L.s, L.T, L.dX, L.dL1, L.dL2, ws, ws_bytes, stream);
+      }
+    }
+    if (st != NF4_OK) return st;
+  }
+  return NF4_OK;
 }
 
 }  // extern "C"

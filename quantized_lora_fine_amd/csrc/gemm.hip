@@ -53,6 +53,7 @@ constexpr uint32_t kOOB = 0x80000000u;        // an offset past every buffer's r
 
 struct GemmArgs {
   const uint16_t* A;
+  const uint16_t* Wb;  // bf16 weight [o][h] (SRC == kSrcBF16)
   const uint8_t* codes;
   const void* absmax;
   const float* dqs;
@@ -76,8 +77,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcFlags);
 }
 
-template <int MODE, bool DQ>
+template <int MODE, int SRC>
 __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
+  constexpr bool DQ = SRC == kSrcNF4DQ;
+  constexpr bool BF = SRC == kSrcBF16;
   // three buffers each for A and the dequantized B: tile t lives in buffer t%3
   __shared__ __attribute__((aligned(16))) uint8_t As0[GBM * 128];
   __shared__ __attribute__((aligned(16))) uint8_t As1[GBM * 128];
@@ -138,11 +141,23 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)dst, 16, a_voff[i] + kt * 128, 0, 0, 0);
       }
     };
-    // FWD: (n = ptid>>1, half = ptid&1): 32 consecutive codes of W row n0+n.
+    // FWD: (n = ptid>>1, half = ptid&1): 32 consecutive codes (or bf16) of W row n0+n.
     // DX : (og = ptid>>4, hc = ptid&15): W rows 4*og .. 4*og+3 of the step, columns n0+hc*8 .. +8.
     __amdgpu_buffer_rsrc_t c_rsrc;
     uint32_t c_voff[4], s_voff[4];
-    if constexpr (MODE == MODE_FWD) {
+    if constexpr (BF && MODE == MODE_FWD) {
+      const int n = ptid >> 1;
+      const int nrows = (N - n0) < GBN ? (N - n0) : GBN;
+      c_rsrc = make_rsrc(p.Wb + (int64_t)n0 * K, (uint32_t)((int64_t)nrows * K * 2));
+      c_voff[0] = (uint32_t)(n * K * 2 + (ptid & 1) * 64);
+    } else if constexpr (BF) {
+      const int og = ptid >> 4;
+      const int hc = ptid & 15;
+      const bool ok = n0 + hc * 8 < N;
+      c_rsrc = make_rsrc(p.Wb, (uint32_t)((int64_t)K * N * 2));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c_voff[i] = ok ? (uint32_t)(((og * 4 + i) * N + n0 + hc * 8) * 2) : kOOB;
+    } else if constexpr (MODE == MODE_FWD) {
       const int n = ptid >> 1;
       const int nrows = (N - n0) < GBN ? (N - n0) : GBN;
       c_rsrc = make_rsrc(p.codes + (int64_t)n0 * (K >> 1), (uint32_t)((int64_t)nrows * (K >> 1)));
@@ -180,8 +195,17 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
         return __builtin_bit_cast(float, sraw[set][i]);
       }
     };
+    u32x4 wreg[2][4];  // bf16 weight chunks (SRC == kSrcBF16)
     auto issue_W = [&](int kt, int set) {
-      if constexpr (MODE == MODE_FWD) {
+      if constexpr (BF && MODE == MODE_FWD) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          wreg[set][q] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, c_voff[0] + kt * 128 + q * 16, 0, 0);
+      } else if constexpr (BF) {
+        const uint32_t drow = (uint32_t)kt * 128u * (uint32_t)N;  // 64 rows of N bf16
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wreg[set][i] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, c_voff[i] + drow, 0, 0);
+      } else if constexpr (MODE == MODE_FWD) {
         creg[set] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, c_voff[0] + kt * 32, 0, 0);
         load_scale(s_voff[0] + kt, set, 0);
       } else {
@@ -194,11 +218,32 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
         }
       }
     };
-    constexpr int kWLoads = (MODE == MODE_FWD) ? (DQ ? 3 : 2) : (DQ ? 12 : 8);
+    constexpr int kWLoads = BF ? 4 : (MODE == MODE_FWD) ? (DQ ? 3 : 2) : (DQ ? 12 : 8);
     constexpr int kWaitW = (kWLoads & 15) | ((kWLoads >> 4) << 14) | (0x7 << 4) | (0xF << 8);
     auto dequant = [&](int set, int b) {
       uint8_t* dst = bbuf(b);
-      if constexpr (MODE == MODE_FWD) {
+      if constexpr (BF && MODE == MODE_FWD) {
+        // bf16 source: the 4 chunks go to the tile as they are
+#pragma unroll
+        for (int q = 0; q < 4; ++q) *(u32x4*)(dst + lds_off(ptid >> 1, (ptid & 1) * 4 + q)) = wreg[set][q];
+      } else if constexpr (BF) {
+        // bf16 source, transposed: dword q of row i holds columns 2q (low half) and 2q+1 (high half);
+        // B row n gets the 4 rows' values of column n as one 8-byte chunk
+        const int og = ptid >> 4;
+        const int hc = ptid & 15;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t a0 = wreg[set][0][q], a1 = wreg[set][1][q], a2 = wreg[set][2][q], a3 = wreg[set][3][q];
+          const int row0 = hc * 8 + 2 * q;
+          uint2 e0, e1;
+          e0.x = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+          e0.y = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+          e1.x = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+          e1.y = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
+          *(uint2*)(dst + row0 * 128 + (((og >> 1) ^ swz(row0)) << 4) + (og & 1) * 8) = e0;
+          *(uint2*)(dst + (row0 + 1) * 128 + (((og >> 1) ^ swz(row0 + 1)) << 4) + (og & 1) * 8) = e1;
+        }
+      } else if constexpr (MODE == MODE_FWD) {
         const float sc = scale(set, 0);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -409,12 +454,13 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
   }
 }
 
-hipError_t launch_nf4_gemm(int mode, bool dq, const uint16_t* A, const uint8_t* codes, const void* absmax,
-                           const float* dqs, const uint16_t* A2, const uint16_t* B2, int R, uint16_t* C,
-                           int64_t M, int N, int K, const NF4Consts& c, hipStream_t st) {
+hipError_t launch_nf4_gemm(int mode, int src, const uint16_t* A, const uint16_t* Wb, const uint8_t* codes,
+                           const void* absmax, const float* dqs, const uint16_t* A2, const uint16_t* B2, int R,
+                           uint16_t* C, int64_t M, int N, int K, const NF4Consts& c, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   GemmArgs p;
   p.A = A;
+  p.Wb = Wb;
   p.codes = codes;
   p.absmax = absmax;
   p.dqs = dqs;
@@ -430,13 +476,17 @@ hipError_t launch_nf4_gemm(int mode, bool dq, const uint16_t* A, const uint8_t* 
   p.tiles_n = (N + GBN - 1) / GBN;
   const int64_t nwg = tiles_m * p.tiles_n;
   const dim3 gr((unsigned)nwg), bl(GNT);
+#define NF4K_GEMM(MD, SR) hipLaunchKernelGGL((k_nf4_gemm<MD, SR>), gr, bl, 0, st, p, c)
   if (mode == MODE_FWD) {
-    if (dq) hipLaunchKernelGGL((k_nf4_gemm<MODE_FWD, true>), gr, bl, 0, st, p, c);
-    else hipLaunchKernelGGL((k_nf4_gemm<MODE_FWD, false>), gr, bl, 0, st, p, c);
+    if (src == kSrcNF4DQ) NF4K_GEMM(MODE_FWD, kSrcNF4DQ);
+    else if (src == kSrcNF4) NF4K_GEMM(MODE_FWD, kSrcNF4);
+    else NF4K_GEMM(MODE_FWD, kSrcBF16);
   } else {
-    if (dq) hipLaunchKernelGGL((k_nf4_gemm<MODE_DX, true>), gr, bl, 0, st, p, c);
-    else hipLaunchKernelGGL((k_nf4_gemm<MODE_DX, false>), gr, bl, 0, st, p, c);
+    if (src == kSrcNF4DQ) NF4K_GEMM(MODE_DX, kSrcNF4DQ);
+    else if (src == kSrcNF4) NF4K_GEMM(MODE_DX, kSrcNF4);
+    else NF4K_GEMM(MODE_DX, kSrcBF16);
   }
+#undef NF4K_GEMM
   return hipGetLastError();
 }
 

@@ -18,9 +18,12 @@ hipError_t launch_error(const float* W, int64_t nblocks, bool dq, double* part, 
                         hipStream_t st);
 hipError_t launch_topk(const double* e, int n, int k, int* idx, hipStream_t st);
 
-hipError_t launch_nf4_gemm(int mode, bool dq, const uint16_t* A, const uint8_t* codes, const void* absmax,
-                           const float* dqs, const uint16_t* A2, const uint16_t* B2, int R, uint16_t* C, int64_t M,
-                           int N, int K, const NF4Consts& c, hipStream_t st);
+// Weight source of the fused GEMM: NF4 with fp32 absmax, NF4 with 8-bit
+// double-quantized scales, or a bf16 weight (no quantization).
+enum { kSrcNF4 = 0, kSrcNF4DQ = 1, kSrcBF16 = 2 };
+hipError_t launch_nf4_gemm(int mode, int src, const uint16_t* A, const uint16_t* Wb, const uint8_t* codes,
+                           const void* absmax, const float* dqs, const uint16_t* A2, const uint16_t* B2, int R,
+                           uint16_t* C, int64_t M, int N, int K, const NF4Consts& c, hipStream_t st);
 
 // One launch of k_prep: up to kPrepPads layout copies and kPrepZeros clears.
 // Unused jobs have orows * ocols == 0 / n == 0.

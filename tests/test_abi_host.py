@@ -22,7 +22,7 @@ lib = nf4._lib
 def header_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    names = re.findall(r"^[A-Za-z_][\w \*]*?\b(nf4\w*)\s*\(", src, flags=re.M)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b((?:nf4|bf16lora)\w*)\s*\(", src, flags=re.M)
     return sorted(set(names))
 
 
@@ -166,6 +166,31 @@ def test_bwd_validation():
     assert bwd_call(desc(rows=128, cols=96)) == nf4.NF4_ERR_SHAPE
 
 
+def bf16_fwd_call(W=A, rows=128, cols=128, X=C, M=16, Y=F, ws=H, ws_bytes=1 << 30):
+    v = lambda p: ctypes.c_void_p(p) if p else None
+    return lib.bf16lora_fwd(v(W), rows, cols, v(X), M, v(D), v(E), 8, 2.0, v(Y), v(G), v(ws), ws_bytes, None)
+
+
+def bf16_bwd_call(W=A, rows=128, cols=128, dX=G, dL1=H, ws_bytes=1 << 30):
+    v = lambda p: ctypes.c_void_p(p) if p else None
+    return lib.bf16lora_bwd(v(W), rows, cols, v(C), v(D), 16, v(E), v(F), 8, 2.0, None, v(dX), v(dL1),
+                            v(H + 0x1000000), v(H + 0x2000000), ws_bytes, None)
+
+
+def test_bf16_layer_validation():
+    assert bf16_fwd_call(W=0) == nf4.NF4_ERR_NULL
+    assert bf16_fwd_call(W=A + 2) == nf4.NF4_ERR_ALIGN
+    assert bf16_fwd_call(rows=100) == nf4.NF4_ERR_SHAPE
+    assert bf16_fwd_call(cols=96) == nf4.NF4_ERR_SHAPE
+    assert bf16_fwd_call(rows=1 << 16, cols=1 << 16) == nf4.NF4_ERR_SHAPE   # 2^32 elements: too large
+    assert bf16_fwd_call(ws=0) == nf4.NF4_ERR_WORKSPACE
+    assert bf16_fwd_call(Y=A + 64) == nf4.NF4_ERR_ALIAS                  # Y inside W
+    assert bf16_fwd_call(M=0) == nf4.NF4_OK
+    assert bf16_bwd_call(dL1=0) == nf4.NF4_ERR_NULL
+    assert bf16_bwd_call(dX=A) == nf4.NF4_ERR_ALIAS                      # dX over W
+    assert bf16_bwd_call(ws_bytes=16) == nf4.NF4_ERR_WORKSPACE
+
+
 def test_error_and_topk_validation():
     v = ctypes.c_void_p
     assert lib.nf4_layer_error(v(C), 64, 64, 64, 0, None, v(D), 1 << 20, None) == nf4.NF4_ERR_NULL
@@ -178,3 +203,26 @@ def test_error_and_topk_validation():
     assert lib.nf4_topk(v(C), 10, 3, None, None) == nf4.NF4_ERR_NULL
     assert lib.nf4_topk(v(C), 10, 3, v(C + 16), None) == nf4.NF4_ERR_ALIAS
     assert lib.nf4_topk(v(C), 10, 0, None, None) == nf4.NF4_OK
+
+
+def test_stack_validation():
+    v = ctypes.c_void_p
+    d = desc(rows=128, cols=128)
+    L = (nf4._NF4Linear * 2)()
+    L[0].q = ctypes.pointer(d)
+    L[0].r = 8
+    L[1].w_bf16, L[1].rows, L[1].cols, L[1].r = v(C), 128, 128, 0
+    n = ctypes.c_size_t()
+    assert lib.nf4_stack_workspace_bytes(L, 2, 16, ctypes.byref(n)) == nf4.NF4_OK
+    assert n.value == max(nf4.workspace_bytes(nf4.NF4_OP_FWD, 16, 128, 128, 8),
+                          nf4.workspace_bytes(nf4.NF4_OP_BWD, 16, 128, 128, 8))
+    assert lib.nf4_stack_workspace_bytes(L, 2, 16, None) == nf4.NF4_ERR_NULL
+    assert lib.nf4_stack_bwd(L, 2, 3, 16, v(H), 1 << 30, None) == nf4.NF4_ERR_SHAPE    # cut > n
+    assert lib.nf4_stack_bwd(L, 2, -1, 16, v(H), 1 << 30, None) == nf4.NF4_ERR_SHAPE
+    assert lib.nf4_stack_bwd(L, 2, 2, 16, v(H), 1 << 30, None) == nf4.NF4_OK           # cut == n: nothing runs
+    L[1].q = ctypes.pointer(d)                                                          # both weights set
+    assert lib.nf4_stack_workspace_bytes(L, 2, 16, ctypes.byref(n)) == nf4.NF4_ERR_ARG
+    L[1].q = None
+    L[1].w_bf16 = None                                                                  # no weight
+    assert lib.nf4_stack_fwd(L, 2, 16, v(H), 1 << 30, None) != nf4.NF4_OK
+    assert lib.nf4_stack_fwd(None, 1, 16, v(H), 1 << 30, None) == nf4.NF4_ERR_NULL

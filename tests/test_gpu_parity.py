@@ -262,3 +262,115 @@ def test_layer_c2_full():
     say("c2 4096x4096 r=16 M=2048, double quant")
     d = synth.layer_inputs(synth.C2)
     check_layer(d, d["s"], d["dq_group"])
+
+
+# ---------------------------------------------------------------------------
+# protected (bf16) linears through the same fused kernels
+# ---------------------------------------------------------------------------
+
+def check_bf16_layer(d, s, use_T=True):
+    Wb = synth.bf16(d["W"])  # the protected weight, stored in bf16
+    W = dev(Wb)
+    X, L1, L2, dY = (dev(d[k]) for k in ("X", "L1", "L2", "dY"))
+    Y, T = nf4.bf16_fwd(W, X, L1, L2, s)
+    dX, dL1, dL2 = nf4.bf16_bwd(W, X, dY, L1, L2, s, T=T if use_T else None)
+    torch.cuda.synchronize()
+    Yr, Tr = oracle.fwd(d["X"], Wb, d["L1"], d["L2"], s)
+    dXr, dL1r, dL2r, _ = oracle.bwd(d["X"], d["dY"], Wb, d["L1"], d["L2"], s)
+    check_close("T", T, Tr)
+    check_close("Y", Y, Yr)
+    check_close("dX", dX, dXr)
+    check_close("dL1", dL1, dL1r)
+    check_close("dL2", dL2, dL2r)
+
+
+def test_bf16_layer_c1():
+    d = synth.layer_inputs(synth.C1)
+    check_bf16_layer(d, d["s"])
+
+
+@pytest.mark.parametrize("M,o,h,r,s", [
+    (1, 64, 64, 1, 2.0),
+    (37, 320, 192, 17, 0.5),
+    (300, 128, 576, 8, 2.0),
+    (513, 704, 640, 16, 2.0),
+])
+def test_bf16_layer_ragged(M, o, h, r, s):
+    say(f"bf16 layer M={M} o={o} h={h} r={r}")
+    d = synth.random_case(seed=M + o + h, rows=o, cols=h, M=M, r=r)
+    check_bf16_layer(d, s, use_T=(r % 2 == 0))
+
+
+def test_bf16_layer_c2_full():
+    say("bf16 layer 4096x4096 r=16 M=2048")
+    d = synth.layer_inputs(synth.C2)
+    check_bf16_layer(d, d["s"])
+
+
+# ---------------------------------------------------------------------------
+# stack runner: forward over every linear, backward down to a cut
+# ---------------------------------------------------------------------------
+
+def test_stack_runner_matches_layer_calls():
+    M = 96
+    spec = [  # (format, o, h, r, dq)
+        ("nf4", 128, 192, 8, 0), ("bf16", 192, 128, 8, 0), ("nf4", 256, 128, 0, 256),
+        ("nf4", 128, 256, 16, 0), ("bf16", 64, 128, 0, 0), ("nf4", 128, 64, 4, 256),
+    ]
+    cut = 1
+    lins, refs = [], []
+    sentinel = 7.0
+    for i, (fmt, o, h, r, dq) in enumerate(spec):
+        d = synth.random_case(seed=100 + i, rows=o, cols=h, M=M, r=max(r, 1))
+        L = {"X": dev(d["X"]), "dY": dev(d["dY"]), "r": r, "s": 2.0,
+             "Y": torch.empty(M, o, dtype=torch.bfloat16, device=DEV)}
+        if fmt == "nf4":
+            L["q"] = nf4.quantize(dev(d["W"]), dq)
+        else:
+            L["w"] = dev(synth.bf16(d["W"]))
+        if r:
+            L["L1"], L["L2"] = dev(d["L1"]), dev(d["L2"])
+            L["T"] = torch.empty(M, r, dtype=torch.bfloat16, device=DEV)
+            L["dL1"] = torch.full((h, r), sentinel, dtype=torch.float32, device=DEV)
+            L["dL2"] = torch.full((r, o), sentinel, dtype=torch.float32, device=DEV)
+        if i != cut:  # the lowest linear above the cut needs no input gradient
+            L["dX"] = torch.full((M, h), sentinel, dtype=torch.bfloat16, device=DEV)
+        lins.append(L)
+        refs.append(d)
+    st = nf4.Stack(lins, M)
+    st.fwd()
+    st.bwd(cut=cut)
+    torch.cuda.synchronize()
+    for i, (L, d, (fmt, o, h, r, dq)) in enumerate(zip(lins, refs, spec)):
+        say(f"  linear {i}: {fmt} {o}x{h} r={r}")
+        if r:
+            if fmt == "nf4":
+                Y, T = nf4.fwd(L["q"], L["X"], L["L1"], L["L2"], 2.0)
+                dX, dL1, dL2 = nf4.bwd(L["q"], L["X"], L["dY"], L["L1"], L["L2"], 2.0, T=T)
+            else:
+                Y, T = nf4.bf16_fwd(L["w"], L["X"], L["L1"], L["L2"], 2.0)
+                dX, dL1, dL2 = nf4.bf16_bwd(L["w"], L["X"], L["dY"], L["L1"], L["L2"], 2.0, T=T)
+            assert torch.equal(L["Y"], Y) and torch.equal(L["T"], T)
+            if i >= cut:
+                assert torch.equal(L["dL1"], dL1) and torch.equal(L["dL2"], dL2)
+            else:
+                assert bool((L["dL1"] == sentinel).all()) and bool((L["dL2"] == sentinel).all())
+            if "dX" in L:
+                if i >= cut:
+                    assert torch.equal(L["dX"], dX)
+                else:
+                    assert bool((L["dX"] == sentinel).all())
+        else:
+            # plain product: Y = X W^T (and dX = dY W above the cut), against the oracle
+            Wref = synth.bf16(d["W"]) if fmt == "bf16" else oracle.dequantize(oracle.quantize(d["W"], 64, dq))
+            z1, z2 = np.zeros((h, 1)), np.zeros((1, o))
+            Yr, _ = oracle.fwd(d["X"], Wref, z1, z2, 2.0)
+            check_close("Y", L["Y"], Yr)
+            if "dX" in L and i >= cut:
+                dXr, _, _, _ = oracle.bwd(d["X"], d["dY"], Wref, z1, z2, 2.0)
+                check_close("dX", L["dX"], dXr)
+    # one adapted linear against the oracle as well
+    d = refs[3]
+    wh = oracle.dequantize(oracle.quantize(d["W"], 64, 0))
+    Yr, _ = oracle.fwd(d["X"], wh, d["L1"], d["L2"], 2.0)
+    check_close("Y[3]", lins[3]["Y"], Yr)
