@@ -77,6 +77,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--workload", default="c2", choices=["c2", "c4-stack"],
+                    help="c2: the 4096x4096 layer (default); c4-stack: the 280-linear 14B-shaped stack with "
+                         "AQLoRA's allocation against QLoRA")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -90,6 +93,9 @@ def main():
 
     import quantized_lora_fine_amd as nf4
     import synth
+
+    if args.workload == "c4-stack":
+        return bench_stack(args)
 
     cfg = synth.C2
     M, o, h, r, s = cfg.M, cfg.rows, cfg.cols, cfg.r, cfg.s
@@ -230,6 +236,120 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_stack(args):
+    """The 14B-shaped stack: per-linear NF4 error, top-8 protection, then one
+    training step's linear work (forward over all 280 linears, backward down
+    to the cut) under three allocations:
+      qlora     every linear NF4, adapters everywhere, full backward;
+      aqlora-q  the 8 largest-error linears in bf16, adapters everywhere;
+      aqlora-s  the same protection, adapters on the top 85% of the blocks
+                (below them a plain forward), backward stopped at the lowest
+                adapted block, whose input-side linears need no dX.
+    Activations are synthetic and shared between linears of the same shape
+    (the linear work does not depend on their values)."""
+    import torch
+
+    import quantized_lora_fine_amd as nf4
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stack = synth.c4_stack()
+    n, M, r, s, K = len(stack), synth.C4_TOKENS, 16, 2.0, synth.C4_TOPK
+    nblk = synth.C4_LAYERS
+    print(f"# device {torch.cuda.get_device_name(0)}; 14B-shaped stack, {n} linears, M={M}", file=sys.stderr,
+          flush=True)
+    # profiling pass + NF4 storage
+    t0 = time.perf_counter()
+    slots = torch.empty(n, 2, dtype=torch.float64, device=dev)
+    qs = []
+    ws_e = torch.empty(nf4.workspace_bytes(nf4.NF4_OP_ERROR, 0, synth.C4_FFN, synth.C4_HIDDEN, 1),
+                       dtype=torch.uint8, device=dev)
+    e_ms = 0.0
+    for lin in stack:
+        W = synth.c4_weight(lin, device=dev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        nf4.layer_error(W, 0, out=slots[lin.index], ws=ws_e)
+        b.record()
+        qs.append(nf4.quantize(W, 256))
+        b.synchronize()
+        e_ms += a.elapsed_time(b)
+        del W
+    top = nf4.topk(slots[:, 0].contiguous(), K).cpu().numpy().tolist()
+    protected = {i: synth.c4_weight(stack[i], device=dev).to(torch.bfloat16).contiguous() for i in top}
+    print(f"# stack built in {time.perf_counter() - t0:.1f} s; top-{K} {top}", file=sys.stderr, flush=True)
+
+    g = torch.Generator(device=dev).manual_seed(7)
+    acts = {}
+    for width in (synth.C4_HIDDEN, synth.C4_FFN):
+        acts[("x", width)] = torch.randn(M, width, generator=g, device=dev).to(torch.bfloat16)
+        acts[("y", width)] = torch.empty(M, width, dtype=torch.bfloat16, device=dev)
+        acts[("dy", width)] = torch.randn(M, width, generator=g, device=dev).to(torch.bfloat16)
+        acts[("dx", width)] = torch.empty(M, width, dtype=torch.bfloat16, device=dev)
+    adapters = []
+    for lin in stack:
+        adapters.append({"L1": (torch.randn(lin.cols, r, generator=g, device=dev) * 0.02).to(torch.bfloat16),
+                         "L2": (torch.randn(r, lin.rows, generator=g, device=dev) * 0.02).to(torch.bfloat16),
+                         "T": torch.empty(M, r, dtype=torch.bfloat16, device=dev),
+                         "dL1": torch.empty(lin.cols, r, dtype=torch.float32, device=dev),
+                         "dL2": torch.empty(r, lin.rows, dtype=torch.float32, device=dev)})
+
+    def build(protect, alpha):
+        first_blk = nblk - int(round(alpha * nblk))  # lowest adapted block
+        cut = first_blk * len(synth.C4_LINEARS)
+        linears = []
+        for lin in stack:
+            L = {"X": acts[("x", lin.cols)], "Y": acts[("y", lin.rows)], "dY": acts[("dy", lin.rows)]}
+            if protect and lin.index in protected:
+                L["w"] = protected[lin.index]
+            else:
+                L["q"] = qs[lin.index]
+            if lin.index >= cut:
+                L.update(adapters[lin.index], r=r, s=s)
+                # the lowest adapted block's input-side linears feed nothing that needs a gradient
+                if not (lin.layer == first_blk and lin.kind in ("q", "k", "v", "gate", "up")):
+                    L["dX"] = acts[("dx", lin.cols)]
+            linears.append(L)
+        return nf4.Stack(linears, M), cut
+
+    flops_fwd = 2.0 * M * sum(l.rows * l.cols for l in stack)
+    res = {}
+    for name, protect, alpha in (("qlora", False, 1.0), ("aqlora-q", True, 1.0), ("aqlora-s", True, 0.85)):
+        st, cut = build(protect, alpha)
+
+        def step():
+            st.fwd()
+            st.bwd(cut)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        ms = 1e3 * (time.perf_counter() - t) / args.steps
+        res[name] = {"ms_per_step": round(ms, 3), "cut": cut, "bf16_linears": K if protect else 0}
+        print(f"# {name}: {ms:.2f} ms/step (backward cut at linear {cut})", file=sys.stderr, flush=True)
+    base = res["qlora"]["ms_per_step"]
+    for k in res:
+        res[k]["speedup_vs_qlora_pct"] = round(100.0 * (base / res[k]["ms_per_step"] - 1.0), 2)
+    out = {
+        "metric": "14B-shaped stack training-step linear work, AQLoRA allocation vs QLoRA",
+        "value": res["aqlora-s"]["speedup_vs_qlora_pct"], "unit": "% faster than QLoRA", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["aqlora-s"]["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "14B-shaped stack: 40 blocks x {q,k,v,o 5120^2; gate,up 5120->13824; down "
+                               "13824->5120}, Student-t weights, NF4 + DQ/256, top-8 bf16, M=4096, r=16",
+                   "forward_tflop": round(flops_fwd / 1e12, 2)},
+        "error_pass_ms": round(e_ms, 3), "error_pass_GBps": round(4.0 * sum(l.rows * l.cols for l in stack)
+                                                                   / (e_ms * 1e-3) / 1e9, 1),
+        "protected": top, "modes": res,
     }
     print(json.dumps(out), flush=True)
 
