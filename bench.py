@@ -273,6 +273,7 @@ def bench_stack(args):
     for lin in stack:
         W = synth.c4_weight(lin, device=dev)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()  # the events then bracket the error pass alone
         a.record()
         nf4.layer_error(W, 0, out=slots[lin.index], ws=ws_e)
         b.record()
