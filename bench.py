@@ -196,6 +196,21 @@ def main():
     kernels["layer_error"] = {"us": round(1e3 * op_ms["error"], 3),
                               "GBps": round(e_bytes / (op_ms["error"] * 1e-3) / 1e9, 1), "bytes": e_bytes}
 
+    # merge after training (not part of the step): NF4 base -> bf16, fp32 base -> bf16
+    Wm = torch.empty(o, h, dtype=torch.bfloat16, device=dev)
+    for name, src, nbytes in (("merge_nf4_to_bf16", q, n // 2 + n // 64 + 4 * (n // 64 // 256) + 2 * n),
+                              ("merge_fp32_to_bf16", W, 6 * n)):
+        for _ in range(args.warmup):
+            nf4.merge(src, L1, L2, s, bf16=True, out=Wm)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            nf4.merge(src, L1, L2, s, bf16=True, out=Wm)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / args.steps
+        kernels[name] = {"us": round(us, 3), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes": nbytes}
+
     dom = max(("nf4_gemm_fwd", "nf4_gemm_dx"), key=lambda k: kernels[k]["us"])
     ach = kernels[dom]["tflops"]
     traffic = None

@@ -197,6 +197,27 @@ nf4_status bf16lora_bwd(const uint16_t *W, int64_t rows, int64_t cols, const uin
                         void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Merge a trained adapter into the base ("LoRA: Fine-tuning a model by
+ * learning a small update", section "Serving models and switching tasks":
+ * W_merged = W0 + (alpha/r) B A; "Lesson 17. What QLoRA Actually Costs":
+ * merge into the full-precision base, quantise afterwards if needed).  In
+ * the storage layout [rows = o][cols = h]:
+ *     W_out[n][k] = base[n][k] + s * sum_j L2[j][n] * L1[k][j]
+ * computed in fp32 (fp32 sum of the r products, then s * sum + base).
+ *   base : W (fp32 [rows][cols]) when W != NULL, else q dequantized exactly
+ *          as nf4_dequantize does (q->rows, q->cols must equal rows, cols).
+ *   L1   : bf16 [cols][r];  L2 : bf16 [r][rows];  1 <= r <= 256.
+ *   W_out: fp32 [rows][cols] (out_is_bf16 == 0) or its bf16 rounding to
+ *          nearest even; for an NF4 re-quantization pass the fp32 form to
+ *          nf4_quantize.
+ * rows >= 0, cols % 64 == 0.  Errors: NF4_ERR_NULL, _SHAPE, _ARG, _ALIGN,
+ * _ALIAS, _HIP.
+ */
+nf4_status nf4lora_merge(const float *W, const nf4_tensor *q, int64_t rows, int64_t cols,
+                         const uint16_t *L1, const uint16_t *L2, int32_t r, float s,
+                         void *W_out, int32_t out_is_bf16, void *stream);
+
+/*
  * One linear of a stack run by nf4_stack_fwd / nf4_stack_bwd.  The frozen
  * weight is either NF4 (q) or a protected bf16 weight (w_bf16, [rows][cols]);
  * exactly one of the two is set.  r > 0 gives the linear an adapter (L1, L2,

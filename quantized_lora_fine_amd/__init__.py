@@ -65,6 +65,7 @@ _SIGS = {
     "nf4_layer_error": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _sz, _vp], ctypes.c_int),
     "nf4_topk": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
     "nf4_protect_count": ([_f64, _i32], _i32),
+    "nf4lora_merge": ([_vp, _T, _i64, _i64, _vp, _vp, _i32, _f32, _vp, _i32, _vp], ctypes.c_int),
     "nf4_stack_workspace_bytes": ([_LP, _i32, _i64, ctypes.POINTER(_sz)], ctypes.c_int),
     "nf4_stack_fwd": ([_LP, _i32, _i64, _vp, _sz, _vp], ctypes.c_int),
     "nf4_stack_bwd": ([_LP, _i32, _i32, _i64, _vp, _sz, _vp], ctypes.c_int),
@@ -286,6 +287,22 @@ def topk(errors: torch.Tensor, k: int, out: torch.Tensor | None = None) -> torch
     idx = out if out is not None else torch.empty(max(k, 1), dtype=torch.int32, device=errors.device)
     _check(_lib.nf4_topk(_ptr(errors), errors.numel(), k, _ptr(idx), _stream()), "nf4_topk")
     return idx[:k]
+
+
+def merge(base, L1: torch.Tensor, L2: torch.Tensor, s: float, bf16: bool = False,
+          out: torch.Tensor | None = None) -> torch.Tensor:
+    """nf4lora_merge: base (fp32 W tensor [o][h] or NF4Weight) + s (L1 L2)^T, fp32 or bf16 [o][h]."""
+    if isinstance(base, NF4Weight):
+        W, q, rows, cols, dev = None, ctypes.byref(base.desc), base.rows, base.cols, base.codes.device
+    else:
+        assert base.dtype == torch.float32 and base.is_contiguous() and base.dim() == 2
+        W, q, (rows, cols), dev = base, None, base.shape, base.device
+    r = L1.shape[1]
+    if out is None:
+        out = torch.empty(rows, cols, dtype=torch.bfloat16 if bf16 else torch.float32, device=dev)
+    _check(_lib.nf4lora_merge(_ptr(W), q, rows, cols, _ptr(_u16(L1)), _ptr(_u16(L2)), r, float(s), _ptr(out),
+                              1 if bf16 else 0, _stream()), "nf4lora_merge")
+    return out
 
 
 # ---------------------------------------------------------------------------

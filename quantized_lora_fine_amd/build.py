@@ -36,7 +36,7 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
 # statements)
 EXTRA = {"quant.hip": ["-ffp-contract=off"]}
 
-HIP_SOURCES = ["quant.hip", "gemm.hip", "skinny.hip"]
+HIP_SOURCES = ["quant.hip", "gemm.hip", "skinny.hip", "merge.hip"]
 CPP_SOURCES = ["api.cpp", "nf4_table.cpp"]
 
 

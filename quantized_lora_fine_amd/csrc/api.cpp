@@ -623,4 +623,41 @@ nf4_status nf4_stack_bwd(const nf4_linear* layers, int32_t n, int32_t cut, int64
   return NF4_OK;
 }
 
+
+nf4_status nf4lora_merge(const float* W, const nf4_tensor* q, int64_t rows, int64_t cols, const uint16_t* L1,
+                         const uint16_t* L2, int32_t r, float s, void* W_out, int32_t out_is_bf16, void* stream) {
+  nf4_status st = check_shape(rows, cols, (int32_t)kBlock, 0);
+  if (st != NF4_OK) return st;
+  if (r < 1 || r > 256) return NF4_ERR_SHAPE;
+  if (rows > INT32_MAX / 2 || cols > INT32_MAX / 2) return NF4_ERR_SHAPE;
+  const int64_t n = rows * cols;
+  Range wb[3] = {rng(nullptr, 0), rng(nullptr, 0), rng(nullptr, 0)};
+  int base = 0;
+  if (!W) {
+    if (!q) return NF4_ERR_NULL;
+    st = check_tensor(q);
+    if (st != NF4_OK) return st;
+    if (q->rows != rows || q->cols != cols) return NF4_ERR_SHAPE;
+    size_t cb, ab, db;
+    tensor_sizes(rows, cols, q->dq_group, &cb, &ab, &db);
+    wb[0] = rng(q->codes, cb);
+    wb[1] = rng(q->absmax, ab);
+    wb[2] = rng(q->dq_scale, db);
+    base = q->dq_group ? 2 : 1;
+  } else {
+    if (!aligned16(W)) return NF4_ERR_ALIGN;
+    wb[0] = rng(W, (size_t)n * 4);
+  }
+  if (n == 0) return NF4_OK;
+  if (!L1 || !L2 || !W_out) return NF4_ERR_NULL;
+  if (!aligned16(W_out)) return NF4_ERR_ALIGN;
+  const Range out = rng(W_out, (size_t)n * (out_is_bf16 ? 2 : 4));
+  if (overlap(out, wb[0]) || overlap(out, wb[1]) || overlap(out, wb[2]) ||
+      overlap(out, rng(L1, (size_t)cols * r * 2)) || overlap(out, rng(L2, (size_t)r * rows * 2)))
+    return NF4_ERR_ALIAS;
+  return hip_status(launch_merge(base, W, q && !W ? q->codes : nullptr, q && !W ? q->absmax : nullptr,
+                                 q && !W ? q->dq_scale : nullptr, L1, L2, r, s, rows, cols, out_is_bf16 != 0,
+                                 W_out, nf4_consts(), (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -25,6 +25,11 @@ hipError_t launch_nf4_gemm(int mode, int src, const uint16_t* A, const uint16_t*
                            const void* absmax, const float* dqs, const uint16_t* A2, const uint16_t* B2, int R,
                            uint16_t* C, int64_t M, int N, int K, const NF4Consts& c, hipStream_t st);
 
+// W' = base + s (L1 L2)^T into fp32 or bf16; base 0: fp32 W, 1: NF4, 2: NF4 with 8-bit scales.
+hipError_t launch_merge(int base, const float* W, const uint8_t* codes, const void* absmax, const float* dqs,
+                        const uint16_t* L1, const uint16_t* L2, int r, float s, int64_t rows, int64_t cols,
+                        bool out_bf16, void* out, const NF4Consts& c, hipStream_t st);
+
 // One launch of k_prep: up to kPrepPads layout copies and kPrepZeros clears.
 // Unused jobs have orows * ocols == 0 / n == 0.
 constexpr int kPrepPads = 3;

@@ -226,3 +226,20 @@ def test_stack_validation():
     L[1].w_bf16 = None                                                                  # no weight
     assert lib.nf4_stack_fwd(L, 2, 16, v(H), 1 << 30, None) != nf4.NF4_OK
     assert lib.nf4_stack_fwd(None, 1, 16, v(H), 1 << 30, None) == nf4.NF4_ERR_NULL
+
+
+def test_merge_validation():
+    v = ctypes.c_void_p
+    d = desc(rows=128, cols=128)
+    m = lambda W=C, q=None, rows=128, cols=128, L1=D, L2=E, r=8, out=F, bf=0: lib.nf4lora_merge(
+        v(W) if W else None, ctypes.byref(q) if q is not None else None, rows, cols, v(L1) if L1 else None,
+        v(L2) if L2 else None, r, 2.0, v(out) if out else None, bf, None)
+    assert m(W=None) == nf4.NF4_ERR_NULL                        # neither base
+    assert m(cols=100) == nf4.NF4_ERR_SHAPE
+    assert m(r=0) == nf4.NF4_ERR_SHAPE
+    assert m(W=None, q=d, rows=64) == nf4.NF4_ERR_SHAPE          # q shape differs
+    assert m(L1=None) == nf4.NF4_ERR_NULL
+    assert m(out=F + 8) == nf4.NF4_ERR_ALIGN
+    assert m(out=C + 64) == nf4.NF4_ERR_ALIAS                    # output inside W
+    assert m(W=None, q=d, out=A) == nf4.NF4_ERR_ALIAS            # output over the codes
+    assert m(rows=0) == nf4.NF4_OK

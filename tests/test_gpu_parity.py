@@ -374,3 +374,36 @@ def test_stack_runner_matches_layer_calls():
     wh = oracle.dequantize(oracle.quantize(d["W"], 64, 0))
     Yr, _ = oracle.fwd(d["X"], wh, d["L1"], d["L2"], 2.0)
     check_close("Y[3]", lins[3]["Y"], Yr)
+
+
+# ---------------------------------------------------------------------------
+# merge: W' = base + s (L1 L2)^T
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("o,h,r,base", [(512, 512, 8, "fp32"), (320, 192, 17, "nf4"), (4096, 4096, 16, "nf4dq"),
+                                        (192, 640, 100, "fp32"), (64, 64, 1, "nf4dq")])
+def test_merge(o, h, r, base):
+    d = synth.random_case(seed=o + r, rows=o, cols=h, M=1, r=r)
+    s = 2.0
+    if base == "fp32":
+        src, ref_base = dev(d["W"]), d["W"]
+    else:
+        dq = 256 if base == "nf4dq" else 0
+        src = nf4.quantize(dev(d["W"]), dq)
+        ref_base = oracle.dequantize(oracle.quantize(d["W"], 64, dq))
+    ref = oracle.merge(ref_base, d["L1"], d["L2"], s)
+    L1, L2 = dev(d["L1"]), dev(d["L2"])
+    got = nf4.merge(src, L1, L2, s).cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    say(f"  merge {o}x{h} r={r} {base}: max|err| {err.max():.2e}, max|ref| {np.abs(ref).max():.2e}")
+    # fp32 bound: bf16 x bf16 products are exact in fp32; the r-term FMA chain,
+    # the scaling by s and the final add each round to nearest (unit 2^-24)
+    u = 2.0 ** -24
+    terms = s * (np.abs(oracle.lora._f64(d["L1"])) @ np.abs(oracle.lora._f64(d["L2"]))).T
+    tol32 = (r + 2) * u * terms + 2 * u * np.abs(ref)
+    assert np.all(err <= tol32), float(np.max(err - tol32))
+    gotb = nf4.merge(src, L1, L2, s, bf16=True).cpu().float().numpy().astype(np.float64)
+    # bf16: round-to-nearest of the fp32 value v, within half a bf16 ulp of it:
+    # 2^(floor(log2|v|) - 8) <= 2^-8 |v|
+    tolb = 2.0 ** -8 * (np.abs(ref) + tol32) + tol32
+    assert np.all(np.abs(gotb - ref) <= tolb), float(np.max(np.abs(gotb - ref) - tolb))
