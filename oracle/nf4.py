@@ -41,6 +41,39 @@ def nf4_table() -> np.ndarray:
     return np.array(vals, dtype=np.float64).astype(np.float32)
 
 
+CODEBOOKS = ("nf4", "int4", "fp4")
+
+
+def codebook_table(codebook: str = "nf4") -> np.ndarray:
+    """The 16 code values of a 4-bit codebook, fp32, ascending (equal values keep their order).
+
+    nf4   the NormalFloat table above.
+    int4  the integer alternative ("Lesson 17. What QLoRA Actually Costs",
+          the "int4 rather than NF4" row of its comparison table): the pages
+          give no layout; the reading taken is the symmetric absmax int4 grid,
+          code c -> (c - 8) / 7, so that -1, 0 and +1 are codes 1, 8 and 15
+          (code 0, -8/7, lies outside [-1, 1] and is never chosen).
+    fp4   the ordinary 4-bit float of the QLoRA blog's figure 3 ("the blue
+          ordinary-float curve"): the reading taken is the E2M1 format (sign,
+          2 exponent bits, 1 mantissa bit: magnitudes 0, .5, 1, 1.5, 2, 3, 4,
+          6) divided by its largest value 6, with -0 before +0.  With the
+          lower code on a tie, an exact zero and the small positive values
+          nearest zero take -0; +0 is never chosen.
+    Values that are not binary fractions are the fp64 quotient rounded to fp32.
+    """
+    if codebook == "nf4":
+        return nf4_table()
+    if codebook == "int4":
+        return np.array([(c - 8) / 7.0 for c in range(16)], dtype=np.float64).astype(np.float32)
+    if codebook == "fp4":
+        mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+        neg = [-m / 6.0 for m in reversed(mags)]   # -1 .. -0
+        pos = [m / 6.0 for m in mags]              # +0 .. +1
+        neg[-1] = -0.0
+        return np.array(neg + pos, dtype=np.float64).astype(np.float32)
+    raise ValueError(f"unknown codebook {codebook!r}")
+
+
 def pack_codes(codes: np.ndarray) -> np.ndarray:
     """Two 4-bit codes per byte: element 2t in the low nibble, 2t+1 in the high."""
     c = np.asarray(codes, dtype=np.uint8).reshape(-1)
@@ -66,6 +99,7 @@ class NF4Quant:
     absmax: np.ndarray         # fp32 [nblocks], first-level scale per block
     c8: np.ndarray | None      # uint8 [nblocks] when double quantized
     dq_scale: np.ndarray | None  # fp32 [ngroups] step per group when double quantized
+    codebook: str = "nf4"
 
     @property
     def packed(self) -> np.ndarray:
@@ -102,13 +136,14 @@ def _encode(x: np.ndarray, table: np.ndarray) -> np.ndarray:
     return out
 
 
-def quantize(W, block: int = BLOCK, dq_group: int = 0) -> NF4Quant:
+def quantize(W, block: int = BLOCK, dq_group: int = 0, codebook: str = "nf4") -> NF4Quant:
     """Blockwise absmax NF4 quantization, optionally with double quantization.
 
     Steps ("1. NormalFloat" and "2. Double quantization" in the QLoRA blog):
       1. absmax a_b = max |w| over each block of `block` consecutive weights (fp32).
       2. x = w / a_b, IEEE fp32 division; x = 0 for an all-zero block.
-      3. code = index of the nearest NF4 value to x (lower index on a tie).
+      3. code = index of the nearest code value to x (lower index on a tie);
+         the NF4 table unless another codebook is named.
       4. double quant (dq_group > 0), run after encoding so codes do not change:
          per group of dq_group blocks, S_g = fl32(max a / 255) and
          c8_b = min(255, round-half-even(fl32(a_b / S_g))), c8 = 0 if S_g = 0.
@@ -124,7 +159,7 @@ def quantize(W, block: int = BLOCK, dq_group: int = 0) -> NF4Quant:
     safe = np.where(absmax == 0, np.float32(1), absmax).astype(np.float32)
     x = (blocks / safe[:, None]).astype(np.float32)          # fp32 / fp32: IEEE division
     x[absmax == 0, :] = np.float32(0)
-    codes = _encode(x, nf4_table()).reshape(-1)
+    codes = _encode(x, codebook_table(codebook)).reshape(-1)
     c8 = S = None
     if dq_group:
         nb = absmax.size
@@ -138,12 +173,12 @@ def quantize(W, block: int = BLOCK, dq_group: int = 0) -> NF4Quant:
         r = np.rint((absmax / safeS).astype(np.float32))
         c8 = np.minimum(np.float32(255), r).astype(np.uint8)
         c8[Sb == 0] = 0
-    return NF4Quant(rows, cols, block, dq_group, codes, absmax, c8, S)
+    return NF4Quant(rows, cols, block, dq_group, codes, absmax, c8, S, codebook)
 
 
 def dequantize(q: NF4Quant) -> np.ndarray:
     """w_hat = fl32(table[code] * scale_b), fp32 [rows][cols]."""
-    t = nf4_table()
+    t = codebook_table(q.codebook)
     sc = q.scales()
     w = t[q.codes].reshape(-1, q.block) * sc[:, None]
     return w.astype(np.float32).reshape(q.rows, q.cols)
@@ -155,7 +190,7 @@ def dequantize_bf16_bits(q: NF4Quant) -> np.ndarray:
     return w.view(torch.int16).numpy().view(np.uint16)
 
 
-def layer_error(W, block: int = BLOCK, dq_group: int = 0) -> float:
+def layer_error(W, block: int = BLOCK, dq_group: int = 0, codebook: str = "nf4") -> float:
     """Relative Frobenius NF4 reconstruction error ||W - W_hat||_F / ||W||_F, fp64.
 
     AQLoRA summary, section 3.1: each linear's weights are evaluated in
@@ -164,7 +199,7 @@ def layer_error(W, block: int = BLOCK, dq_group: int = 0) -> float:
     the reading taken).  0 for an all-zero W.
     """
     W = np.asarray(W, dtype=np.float32)
-    wh = dequantize(quantize(W, block, dq_group))
+    wh = dequantize(quantize(W, block, dq_group, codebook))
     d = W.astype(np.float64) - wh.astype(np.float64)
     num = float(np.sum(d * d))
     den = float(np.sum(W.astype(np.float64) ** 2))

@@ -494,10 +494,77 @@ def pin_topk(topk_fn=onf4.topk, seed=17):
     assert got == want
 
 
+# ---------------------------------------------------------------------------
+# other 4-bit codebooks (int4, fp4) through the same encoder and decoder
+# ---------------------------------------------------------------------------
+
+def _codebook_fns(cb, quantize_fn=onf4.quantize, table_fn=onf4.codebook_table):
+    return (lambda W, block=64, dq=0: quantize_fn(W, block, dq, cb)), (lambda: table_fn(cb))
+
+
+def pin_codebook_tables(table_fn=onf4.codebook_table):
+    """int4 = (c-8)/7 and fp4 = E2M1 / 6, each value the fp32 nearest to the exact rational."""
+    assert np.array_equal(table_fn("nf4").view(np.uint32), onf4.nf4_table().view(np.uint32))
+    t = table_fn("int4")
+    for c in range(16):
+        assert t[c] == f32_nearest(Fraction(c - 8, 7)), c
+    mags = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4),
+            Fraction(6)]
+    exact = [-m / 6 for m in reversed(mags)] + [m / 6 for m in mags]
+    f = table_fn("fp4")
+    for c in range(16):
+        assert fr(f[c]) == fr(f32_nearest(exact[c])), c
+    assert np.signbit(f[7]) and not np.signbit(f[8]) and f[7] == 0 and f[8] == 0
+    for tab in (t, f):
+        assert np.all(np.diff(tab.astype(np.float64)) >= 0)
+    assert t[1] == -1 and t[8] == 0 and t[15] == 1 and f[0] == -1 and f[15] == 1
+
+
+def pin_codebook_encoders(quantize_fn=onf4.quantize, table_fn=onf4.codebook_table):
+    """Exact brute force (nearest code, lower index on ties) for int4 and fp4, including
+    sweeps of +-16 fp32 steps around every midpoint and any fp32-exact midpoint."""
+    for cb in ("int4", "fp4"):
+        q, t = _codebook_fns(cb, quantize_fn, table_fn)
+        pin_encoder_bruteforce(q, t, seed=11, nblocks=12)
+        pin_midpoint_sweeps(q, t, seed=12, n_scales=2, ulps=16)
+        table = t()
+        for j in representable_midpoints(table):
+            m = np.float32(float((fr(table[j]) + fr(table[j + 1])) / 2))
+            blk = np.zeros(64, np.float32)
+            blk[0] = np.float32(1.0)
+            blk[1] = m
+            ref, _ = brute_codes(blk, table)
+            assert list(q(blk.reshape(1, 64)).codes) == ref, (cb, j)
+    # fp4 never produces +0 (code 8): it ties with -0 at every x and the lower code wins
+    q, _ = _codebook_fns("fp4", quantize_fn, table_fn)
+    W = np.random.default_rng(13).standard_normal((32, 64)).astype(np.float32)
+    W[:, 5] = 0.0
+    assert not np.any(q(W).codes == 8)
+
+
+def pin_codebook_roundtrip(quantize_fn=onf4.quantize, dequantize_fn=onf4.dequantize,
+                           table_fn=onf4.codebook_table, seed=14):
+    """Weights built from the reachable code values times 2^k come back exactly."""
+    rng = np.random.default_rng(seed)
+    for cb, unreachable, ends in (("int4", {0}, [1, 15]), ("fp4", {8}, [0, 15])):
+        table = table_fn(cb)
+        allowed = np.array([c for c in range(16) if c not in unreachable], np.uint8)
+        nb = 24
+        c = rng.choice(allowed, size=(nb, 64)).astype(np.uint8)
+        c[:, 0] = rng.choice(ends, size=nb)
+        k = rng.integers(-20, 6, size=nb)
+        W = (table[c] * np.float32(2.0) ** k[:, None].astype(np.float32)).astype(np.float32)
+        qq = quantize_fn(W.reshape(4, -1), 64, 0, cb)
+        assert np.array_equal(qq.codes, c.reshape(-1)), cb
+        wh = dequantize_fn(qq)
+        assert np.array_equal(wh.reshape(-1).view(np.uint32), W.reshape(-1).view(np.uint32)), cb
+
+
 ALL_PINS = [
     pin_table_structure, pin_table_independent, pin_encoder_bruteforce, pin_exact_ties,
     pin_midpoint_sweeps, pin_roundtrip, pin_absmax_exact, pin_scale_invariance,
     pin_dq_codes_unchanged, pin_dq_exact, pin_dq_bound, pin_pack, pin_storage,
     pin_fwd_bruteforce, pin_fwd_merge, pin_fwd_special, pin_bwd_finite_diff, pin_bwd_special,
     pin_error_bruteforce, pin_error_zero_on_grid, pin_error_tails, pin_counts, pin_topk,
+    pin_codebook_tables, pin_codebook_encoders, pin_codebook_roundtrip,
 ]

@@ -159,3 +159,33 @@ def test_mistake_topk_ties():
     def bad_topk(e, k):
         return list(np.argsort(-np.asarray(e), kind="stable")[::-1][:k][::-1])
     assert _fails(pins.pin_topk, bad_topk)
+
+
+def test_mistake_codebooks():
+    # int4 with the grid shifted by one code, fp4 with +0 before -0, fp4 divided by 4 instead of 6
+    def shifted(cb):
+        t = oracle.codebook_table(cb)
+        return (np.arange(16, dtype=np.float64) - 7.0).astype(np.float32) / np.float32(7) if cb == "int4" else t
+    assert _fails(pins.pin_codebook_tables, shifted)
+
+    def zero_order(cb):
+        t = oracle.codebook_table(cb).copy()
+        if cb == "fp4":
+            t[7], t[8] = np.float32(0.0), np.float32(-0.0)
+        return t
+    assert _fails(pins.pin_codebook_tables, zero_order)
+
+    def wrong_norm(cb):
+        t = oracle.codebook_table(cb)
+        return (t * np.float32(1.5)).astype(np.float32) if cb == "fp4" else t
+    assert _fails(pins.pin_codebook_tables, wrong_norm)
+    # an encoder that breaks ties toward the upper code fails the brute force
+    def upper_tie_quantize(W, block=64, dq=0, cb="nf4"):
+        q = oracle.nf4.quantize(W, block, dq, cb)
+        t = oracle.codebook_table(cb).astype(np.float64)
+        x = (np.asarray(W, np.float32).reshape(-1, block) /
+             np.where(q.absmax == 0, 1, q.absmax)[:, None].astype(np.float32)).astype(np.float32).reshape(-1)
+        d = np.abs(x.astype(np.float64)[:, None] - t[None, :])
+        q.codes = (15 - np.argmin(d[:, ::-1], axis=1)).astype(np.uint8)
+        return q
+    assert _fails(pins.pin_codebook_encoders, upper_tie_quantize)
