@@ -211,6 +211,21 @@ def main():
         us = 1e3 * e0.elapsed_time(e1) / args.steps
         kernels[name] = {"us": round(us, 3), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes": nbytes}
 
+    # the same weights at identical storage in the other 4-bit codebooks: reconstruction error and quantize time
+    codebooks = {}
+    for cbn in ("nf4", "int4", "fp4"):
+        qc = nf4.NF4Weight(o, h, 256, dev, cbn)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nf4.quantize(W, 256, out=qc)
+        e0.record(stream)
+        for _ in range(args.steps):
+            nf4.quantize(W, 256, out=qc)
+        e1.record(stream)
+        err_c = nf4.layer_error(W, 256, ws=ws_e, codebook=cbn)
+        torch.cuda.synchronize()
+        codebooks[cbn] = {"rel_frobenius_error": round(float(err_c.cpu()), 6),
+                          "quantize_us": round(1e3 * e0.elapsed_time(e1) / args.steps, 3)}
+
     dom = max(("nf4_gemm_fwd", "nf4_gemm_dx"), key=lambda k: kernels[k]["us"])
     ach = kernels[dom]["tflops"]
     traffic = None
@@ -249,6 +264,7 @@ def main():
         "fwd_bwd_pct_bf16_peak": round(100 * F / (fb_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "op_ms": {k: round(v, 5) for k, v in op_ms.items()},
         "kernels": kernels,
+        "codebooks": codebooks,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define NF4LORA_ABI_VERSION 1
+#define NF4LORA_ABI_VERSION 2
 
 typedef enum nf4_status {
   NF4_OK = 0,
@@ -69,6 +69,13 @@ typedef enum nf4_status {
  *                group of 256 blocks ("2. Double quantization").
  *   codes      : rows*cols/2 bytes; byte t holds element 2t in its low
  *                nibble and element 2t+1 in its high nibble (row-major order).
+ *   codebook   : the 16 code values (NF4_CODEBOOK_*, see nf4_codebook_values):
+ *                NF4 (the format of "1. NormalFloat"), or, for comparison
+ *                at identical storage, the symmetric int4 grid (c-8)/7
+ *                ("Lesson 17. What QLoRA Actually Costs": int4 rather than
+ *                NF4) or the E2M1 4-bit float / 6 (the ordinary-float curve of
+ *                the QLoRA blog's figure 3).  Zero-initialised descriptors
+ *                are NF4.
  * Dequantized weight: w_hat = fl32(table[code] * scale), scale = absmax
  * (fp32) or fl32(c8 * dq_scale[group]).  nblocks = rows*cols/64.
  */
@@ -80,7 +87,11 @@ typedef struct nf4_tensor {
   uint8_t *codes;
   void *absmax;
   float *dq_scale;
+  int32_t codebook;
 } nf4_tensor;
+
+/* Codebooks for nf4_tensor.codebook and nf4_layer_error. */
+enum { NF4_CODEBOOK_NF4 = 0, NF4_CODEBOOK_INT4 = 1, NF4_CODEBOOK_FP4 = 2 };
 
 /* Operation ids for nf4_workspace_bytes. */
 enum { NF4_OP_FWD = 1, NF4_OP_BWD = 2, NF4_OP_ERROR = 3 };
@@ -100,6 +111,19 @@ const char *nf4_status_str(int status);
  * own inverse normal CDF and rounded to nearest fp32.
  */
 void nf4_code_table(float out[16]);
+
+/*
+ * The 16 code values of a codebook (fp32, ascending; equal values keep their
+ * order), written to the HOST array out[16]:
+ *   NF4_CODEBOOK_NF4  : as nf4_code_table;
+ *   NF4_CODEBOOK_INT4 : (c - 8) / 7, the fp64 quotient rounded to fp32;
+ *   NF4_CODEBOOK_FP4  : -6 -4 -3 -2 -1.5 -1 -.5 -0 +0 .5 1 1.5 2 3 4 6, each / 6
+ *                       (fp64 quotient rounded to fp32).
+ * The encoder picks the nearest value to x = w / absmax, the lower code on a
+ * tie (so fp4 never yields +0 and int4 never its code 0, -8/7).
+ * Errors: NF4_ERR_NULL, _ARG (unknown codebook).
+ */
+nf4_status nf4_codebook_values(int32_t codebook, float out[16]);
 
 /*
  * Byte sizes of the three buffers of a quantized [rows][cols] weight
@@ -285,13 +309,14 @@ nf4_status nf4_matmul(const nf4_tensor *W, int32_t transpose, const uint16_t *A,
  * w_hat from 64-weight blocks (dq_group 0) or with double quantization
  * (dq_group 256).  This is the ranking quantity of AQLoRA's profiling pass
  * (section 3.1; the page's equation is missing, the relative Frobenius norm
- * is the reading).  fp32 per element, fp64 across blocks, fixed reduction
- * order.  err_dev: device double[1].  ws: nf4_workspace_bytes(NF4_OP_ERROR).
+ * is the reading).  codebook as in nf4_tensor (NF4 for the ranking; the
+ * others measure the comparison at identical storage).  fp32 per element,
+ * fp64 across blocks, fixed reduction order.  err_dev: device double[1].  ws: nf4_workspace_bytes(NF4_OP_ERROR).
  * Errors: NF4_ERR_NULL, _SHAPE, _ARG, _ALIGN, _WORKSPACE, _HIP.
  */
 nf4_status nf4_layer_error(const float *W, int64_t rows, int64_t cols, int32_t block,
-                           int32_t dq_group, double *err_dev, void *ws, size_t ws_bytes,
-                           void *stream);
+                           int32_t dq_group, int32_t codebook, double *err_dev, void *ws,
+                           size_t ws_bytes, void *stream);
 
 /*
  * The protected set of AQLoRA's precision allocation (section 3.2): indices

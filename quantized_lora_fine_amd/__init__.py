@@ -25,6 +25,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_WORKSPACE, NF4_ERR_ALIAS, NF4_ERR_HIP, NF4_ERR_ARG = range(8)
 NF4_OP_FWD, NF4_OP_BWD, NF4_OP_ERROR = 1, 2, 3
+CODEBOOKS = {"nf4": 0, "int4": 1, "fp4": 2}
 BLOCK = 64
 DQ_GROUP = 256
 
@@ -32,7 +33,7 @@ DQ_GROUP = 256
 class _NF4Tensor(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("block", ctypes.c_int32),
                 ("dq_group", ctypes.c_int32), ("codes", ctypes.c_void_p), ("absmax", ctypes.c_void_p),
-                ("dq_scale", ctypes.c_void_p)]
+                ("dq_scale", ctypes.c_void_p), ("codebook", ctypes.c_int32)]
 
 
 class _NF4Linear(ctypes.Structure):
@@ -62,7 +63,8 @@ _SIGS = {
     "bf16lora_bwd": ([_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                      ctypes.c_int),
     "nf4_matmul": ([_T, _i32, _vp, _i64, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
-    "nf4_layer_error": ([_vp, _i64, _i64, _i32, _i32, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "nf4_layer_error": ([_vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "nf4_codebook_values": ([_i32, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
     "nf4_topk": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
     "nf4_protect_count": ([_f64, _i32], _i32),
     "nf4lora_merge": ([_vp, _T, _i64, _i64, _vp, _vp, _i32, _f32, _vp, _i32, _vp], ctypes.c_int),
@@ -103,6 +105,13 @@ def code_table() -> torch.Tensor:
     return torch.tensor(list(out), dtype=torch.float32)
 
 
+def codebook_values(codebook: str = "nf4") -> torch.Tensor:
+    """nf4_codebook_values: the 16 code values of a codebook (CPU fp32)."""
+    out = (ctypes.c_float * 16)()
+    _check(_lib.nf4_codebook_values(CODEBOOKS[codebook], out), "nf4_codebook_values")
+    return torch.tensor(list(out), dtype=torch.float32)
+
+
 def tensor_bytes(rows: int, cols: int, dq_group: int = 0, block: int = BLOCK):
     c, a, d = _sz(), _sz(), _sz()
     _check(_lib.nf4_tensor_bytes(rows, cols, block, dq_group, ctypes.byref(c), ctypes.byref(a), ctypes.byref(d)),
@@ -136,14 +145,14 @@ def _u16(t: torch.Tensor) -> torch.Tensor:
 class NF4Weight:
     """A quantized weight: the three device buffers plus the C descriptor."""
 
-    def __init__(self, rows: int, cols: int, dq_group: int = 0, device="cuda"):
+    def __init__(self, rows: int, cols: int, dq_group: int = 0, device="cuda", codebook: str = "nf4"):
         cb, ab, db = tensor_bytes(rows, cols, dq_group)
-        self.rows, self.cols, self.dq_group = rows, cols, dq_group
+        self.rows, self.cols, self.dq_group, self.codebook = rows, cols, dq_group, codebook
         self.codes = torch.empty(max(cb, 1), dtype=torch.uint8, device=device)
         self.absmax = torch.empty(max(ab, 1), dtype=torch.uint8, device=device)
         self.dq_scale = torch.empty(max(db, 1), dtype=torch.uint8, device=device) if dq_group else None
         self.desc = _NF4Tensor(rows, cols, BLOCK, dq_group, self.codes.data_ptr(), self.absmax.data_ptr(),
-                               self.dq_scale.data_ptr() if dq_group else None)
+                               self.dq_scale.data_ptr() if dq_group else None, CODEBOOKS[codebook])
         self._cb, self._ab, self._db = cb, ab, db
 
     @property
@@ -163,10 +172,10 @@ class NF4Weight:
         return self.codes[:self._cb]
 
 
-def quantize(W: torch.Tensor, dq_group: int = 0, out: NF4Weight | None = None) -> NF4Weight:
-    """nf4_quantize of a cuda fp32 [rows][cols] tensor (into `out` when given)."""
+def quantize(W: torch.Tensor, dq_group: int = 0, out: NF4Weight | None = None, codebook: str = "nf4") -> NF4Weight:
+    """nf4_quantize of a cuda fp32 [rows][cols] tensor (into `out` when given; its codebook then applies)."""
     assert W.dtype == torch.float32 and W.is_cuda and W.is_contiguous() and W.dim() == 2
-    q = out if out is not None else NF4Weight(W.shape[0], W.shape[1], dq_group, W.device)
+    q = out if out is not None else NF4Weight(W.shape[0], W.shape[1], dq_group, W.device, codebook)
     _check(_lib.nf4_quantize(_ptr(W), ctypes.byref(q.desc), _stream()), "nf4_quantize")
     return q
 
@@ -256,7 +265,7 @@ def bf16_bwd(W: torch.Tensor, X: torch.Tensor, dY: torch.Tensor, L1: torch.Tenso
 
 
 def layer_error(W: torch.Tensor, dq_group: int = 0, out: torch.Tensor | None = None,
-                ws: torch.Tensor | None = None) -> torch.Tensor:
+                ws: torch.Tensor | None = None, codebook: str = "nf4") -> torch.Tensor:
     """nf4_layer_error: a cuda float64 tensor of shape [1] (no host sync)."""
     assert W.dtype == torch.float32 and W.is_cuda and W.is_contiguous() and W.dim() == 2
     rows, cols = W.shape
@@ -264,8 +273,8 @@ def layer_error(W: torch.Tensor, dq_group: int = 0, out: torch.Tensor | None = N
     if ws is None:
         n = workspace_bytes(NF4_OP_ERROR, 0, rows, cols, 1)
         ws = torch.empty(n, dtype=torch.uint8, device=W.device)
-    _check(_lib.nf4_layer_error(_ptr(W), rows, cols, BLOCK, dq_group, _ptr(err), _ptr(ws), ws.numel(), _stream()),
-           "nf4_layer_error")
+    _check(_lib.nf4_layer_error(_ptr(W), rows, cols, BLOCK, dq_group, CODEBOOKS[codebook], _ptr(err), _ptr(ws),
+                                ws.numel(), _stream()), "nf4_layer_error")
     return err
 
 

@@ -65,6 +65,7 @@ nf4_status check_tensor(const nf4_tensor* q) {
   if (!q) return NF4_ERR_NULL;
   nf4_status st = check_shape(q->rows, q->cols, q->block, q->dq_group);
   if (st != NF4_OK) return st;
+  if (q->codebook < 0 || q->codebook >= kCodebooks) return NF4_ERR_ARG;
   if (q->rows * q->cols > 0) {
     if (!q->codes || !q->absmax) return NF4_ERR_NULL;
     if (q->dq_group && !q->dq_scale) return NF4_ERR_NULL;
@@ -174,6 +175,7 @@ size_t error_ws(int64_t rows, int64_t cols) {
 // double-quantized scales) or bf16.  rows = o, cols = h.
 struct WSrc {
   int src;
+  int codebook;
   int64_t rows, cols;
   const uint16_t* wb;
   const uint8_t* codes;
@@ -196,6 +198,7 @@ nf4_status wsrc_nf4(const nf4_tensor* W, WSrc* w) {
   size_t cb, ab, db;
   tensor_sizes(W->rows, W->cols, W->dq_group, &cb, &ab, &db);
   w->src = W->dq_group ? kSrcNF4DQ : kSrcNF4;
+  w->codebook = W->codebook;
   w->rows = W->rows;
   w->cols = W->cols;
   w->wb = nullptr;
@@ -215,6 +218,7 @@ nf4_status wsrc_bf16(const uint16_t* W, int64_t rows, int64_t cols, WSrc* w) {
   if (!W) return NF4_ERR_NULL;
   if (!aligned16(W)) return NF4_ERR_ALIGN;
   w->src = kSrcBF16;
+  w->codebook = kCodebookNF4;
   w->rows = rows;
   w->cols = cols;
   w->wb = W;
@@ -238,7 +242,7 @@ hipError_t gemm(int mode, const WSrc& w, const uint16_t* A, const uint16_t* A2, 
   const int64_t N = mode == MODE_FWD ? w.rows : w.cols;
   const int64_t K = mode == MODE_FWD ? w.cols : w.rows;
   return launch_nf4_gemm(mode, w.src, A, w.wb, w.codes, w.absmax, w.dqs, A2, B2, R, C, M, (int)N, (int)K,
-                         nf4_consts(), st);
+                         codebook_consts(w.codebook), st);
 }
 
 nf4_status layer_fwd(const WSrc& W, const uint16_t* X, int64_t M, const uint16_t* L1, const uint16_t* L2,
@@ -409,6 +413,13 @@ const char* nf4_status_str(int s) {
   }
 }
 
+nf4_status nf4_codebook_values(int32_t codebook, float out[16]) {
+  if (!out) return NF4_ERR_NULL;
+  if (codebook < 0 || codebook >= kCodebooks) return NF4_ERR_ARG;
+  std::memcpy(out, codebook_consts(codebook).table, sizeof(float) * 16);
+  return NF4_OK;
+}
+
 void nf4_code_table(float out[16]) {
   if (!out) return;
   const NF4Consts& c = nf4_consts();
@@ -441,7 +452,7 @@ nf4_status nf4_quantize(const float* W, const nf4_tensor* q, void* stream) {
       (db && overlap(in, rng(q->dq_scale, db))) || overlap(rng(q->codes, cb), rng(q->absmax, ab)))
     return NF4_ERR_ALIAS;
   return hip_status(launch_quantize(W, n / kBlock, q->dq_group != 0, q->codes, q->absmax, q->dq_scale,
-                                    nf4_enc(), (hipStream_t)stream));
+                                    codebook_enc(q->codebook), (hipStream_t)stream));
 }
 
 nf4_status nf4_dequantize(const nf4_tensor* q, void* W_out, int32_t out_is_bf16, void* stream) {
@@ -458,7 +469,7 @@ nf4_status nf4_dequantize(const nf4_tensor* q, void* W_out, int32_t out_is_bf16,
       (db && overlap(out, rng(q->dq_scale, db))))
     return NF4_ERR_ALIAS;
   return hip_status(launch_dequantize(q->codes, q->absmax, q->dq_scale, n, q->dq_group != 0, out_is_bf16 != 0,
-                                      W_out, nf4_consts(), (hipStream_t)stream));
+                                      W_out, codebook_consts(q->codebook), (hipStream_t)stream));
 }
 
 nf4_status nf4_workspace_bytes(int32_t op, int64_t M, int64_t rows, int64_t cols, int32_t r, size_t* bytes) {
@@ -537,9 +548,10 @@ nf4_status nf4_matmul(const nf4_tensor* W, int32_t transpose, const uint16_t* A,
 }
 
 nf4_status nf4_layer_error(const float* W, int64_t rows, int64_t cols, int32_t block, int32_t dq_group,
-                           double* err_dev, void* ws, size_t ws_bytes, void* stream) {
+                           int32_t codebook, double* err_dev, void* ws, size_t ws_bytes, void* stream) {
   nf4_status st = check_shape(rows, cols, block, dq_group);
   if (st != NF4_OK) return st;
+  if (codebook < 0 || codebook >= kCodebooks) return NF4_ERR_ARG;
   if (!err_dev) return NF4_ERR_NULL;
   const int64_t n = rows * cols;
   if (n > 0 && !W) return NF4_ERR_NULL;
@@ -550,7 +562,7 @@ nf4_status nf4_layer_error(const float* W, int64_t rows, int64_t cols, int32_t b
   const Range in = rng(W, (size_t)n * 4);
   if (overlap(in, rng(ws, need)) || overlap(in, rng(err_dev, 8)) || overlap(rng(ws, need), rng(err_dev, 8)))
     return NF4_ERR_ALIAS;
-  return hip_status(launch_error(W, n / kBlock, dq_group != 0, (double*)ws, err_dev, nf4_enc(),
+  return hip_status(launch_error(W, n / kBlock, dq_group != 0, (double*)ws, err_dev, codebook_enc(codebook),
                                  (hipStream_t)stream));
 }
 
@@ -657,7 +669,7 @@ nf4_status nf4lora_merge(const float* W, const nf4_tensor* q, int64_t rows, int6
     return NF4_ERR_ALIAS;
   return hip_status(launch_merge(base, W, q && !W ? q->codes : nullptr, q && !W ? q->absmax : nullptr,
                                  q && !W ? q->dq_scale : nullptr, L1, L2, r, s, rows, cols, out_is_bf16 != 0,
-                                 W_out, nf4_consts(), (hipStream_t)stream));
+                                 W_out, codebook_consts(q && !W ? q->codebook : 0), (hipStream_t)stream));
 }
 
 }  // extern "C"

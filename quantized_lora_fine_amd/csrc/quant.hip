@@ -40,26 +40,25 @@ __device__ __forceinline__ void load_group(__amdgpu_buffer_rsrc_t wr, int wave, 
 }
 
 // Encoder table in LDS, one 16-byte entry per bucket (see NF4Enc):
-// {fp64 bound, base code (quantize) or lower value, upper value}.
+// {fp64 bound, code (quantize) or value bits (error) below / above the bound}.
 struct EncEntry {
   double bound;
-  uint32_t lo;  // base code, or bit pattern of the lower code's value
-  float hi;     // value of the upper code
+  uint32_t lo, hi;
 };
 template <bool VALUES>
 __device__ __forceinline__ void enc_to_lds(const NF4Enc& e, EncEntry* t, int tid) {
-  if (tid < kBuckets) {
+  if (tid < e.nb) {
     EncEntry x;
     x.bound = e.bound[tid];
-    x.lo = VALUES ? __builtin_bit_cast(uint32_t, e.qlo[tid]) : e.base[tid];
-    x.hi = e.qhi[tid];
+    x.lo = VALUES ? __builtin_bit_cast(uint32_t, e.qlo[tid]) : e.code_lo[tid];
+    x.hi = VALUES ? __builtin_bit_cast(uint32_t, e.qhi[tid]) : e.code_hi[tid];
     t[tid] = x;
   }
 }
 
 // Per-block setup of the division-free encoder: m' = m (or 1 for an all-zero
-// block, whose weights are all +-0 and take code 7), an approximate 1/m' and
-// a power-of-two prescale keeping that reciprocal in the normal range.
+// block, whose weights are all +-0 and take the code of 0), an approximate
+// 1/m' and a power-of-two prescale keeping that reciprocal in the normal range.
 struct BlockEnc {
   float s, y;
   double md;
@@ -74,32 +73,30 @@ __device__ __forceinline__ BlockEnc block_enc(float m) {
 }
 // x > t for the threshold t of the bucket of x = fl32(w / m'), decided
 // exactly; returns the table entry through `en`.
-__device__ __forceinline__ bool above(float w, const BlockEnc& b, const EncEntry* tab, EncEntry& en) {
-  // xq is within 2e-7 of w / m' and |xq| <= 1 + 2e-7, so k is in 0..32
+__device__ __forceinline__ bool above(float w, const BlockEnc& b, float bscale, float boffset, const EncEntry* tab,
+                                      EncEntry& en) {
+  // xq is within 2e-7 of w / m' and |xq| <= 1 + 2e-7, so k is in 0 .. nb-1
   // (a NaN weight converts to bucket 0)
   const float xq = (w * b.s) * b.y;
-  const uint32_t k = (uint32_t)__builtin_fmaf(xq, 16.f, 16.f);
+  const uint32_t k = (uint32_t)__builtin_fmaf(xq, bscale, boffset);
   en = tab[k];
   return fma(-en.bound, b.md, (double)w) > 0.0;
 }
 
 // codes of 4 weights of a block, packed into 16 bits
-__device__ __forceinline__ uint32_t encode4(floatx4 v, const BlockEnc& b, const EncEntry* tab) {
+__device__ __forceinline__ uint32_t encode4(floatx4 v, const BlockEnc& b, float bscale, float boffset,
+                                            const EncEntry* tab) {
   const float w[4] = {v.x, v.y, v.z, v.w};
   uint32_t p = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     EncEntry en;
-    const bool up = above(w[e], b, tab, en);
-    p |= (en.lo + (up ? 1u : 0u)) << (4 * e);
+    const bool up = above(w[e], b, bscale, boffset, tab, en);
+    p |= (up ? en.hi : en.lo) << (4 * e);
   }
   return p;
 }
 
-// block absmax: |w| of the 4 weights of this lane as bit patterns (unsigned
-// order = float order for non-negative values), then the 16 lanes of the row
-// (The whole vector is reinterpreted: a bit cast of a single ext_vector
-// element is not reliable with this compiler.)
 __device__ __forceinline__ float block_absmax(floatx4 v) {
   const u32x4 u = __builtin_bit_cast(u32x4, v) & 0x7FFFFFFFu;
   return __builtin_bit_cast(float, row16_max_bits(max(max(u.x, u.y), max(u.z, u.w))));
@@ -121,7 +118,7 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
                                                   float* __restrict__ absmax,
                                                   uint8_t* __restrict__ c8,
                                                   float* __restrict__ dqs, NF4Enc enc) {
-  __shared__ EncEntry etab[kBuckets];
+  __shared__ EncEntry etab[kMaxBuckets];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -144,7 +141,7 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
     const float m = block_absmax(v[i]);
     amax[i] = m;
     const int lb = wave * 64 + 4 * i + sub;
-    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)encode4(v[i], block_enc(m), etab), cr, lb * 32 + l16 * 2, 0, kNT);
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)encode4(v[i], block_enc(m), enc.bscale, enc.boffset, etab), cr, lb * 32 + l16 * 2, 0, kNT);
   }
   // lane l16 of row `sub` owns the block of round l16: lb = wave*64 + 4*l16 + sub
   float mine = amax[0];
@@ -217,7 +214,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
 template <bool DQ>
 __global__ __launch_bounds__(256) void k_error_partial(const float* __restrict__ W, int64_t nblocks,
                                                        double* __restrict__ part, NF4Enc enc) {
-  __shared__ EncEntry etab[kBuckets];
+  __shared__ EncEntry etab[kMaxBuckets];
   __shared__ double redd[2][4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -264,8 +261,8 @@ __global__ __launch_bounds__(256) void k_error_partial(const float* __restrict__
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       EncEntry en;
-      const bool up = above(w4[e], be, etab, en);
-      const float wh = (up ? en.hi : __builtin_bit_cast(float, en.lo)) * sc[i];
+      const bool up = above(w4[e], be, enc.bscale, enc.boffset, etab, en);
+      const float wh = __builtin_bit_cast(float, up ? en.hi : en.lo) * sc[i];
       // fp64 from here on: squares of fp32 weights can leave the fp32 range
       const double wd = (double)w4[e];
       const double d = wd - (double)wh;

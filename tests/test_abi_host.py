@@ -35,7 +35,7 @@ def test_exports_match_header():
 
 
 def test_abi_version_and_status_strings():
-    assert nf4.abi_version() == 1
+    assert nf4.abi_version() == 2
     for s in range(8):
         assert nf4.status_str(s)
     assert "unknown" in nf4.status_str(99)
@@ -193,12 +193,13 @@ def test_bf16_layer_validation():
 
 def test_error_and_topk_validation():
     v = ctypes.c_void_p
-    assert lib.nf4_layer_error(v(C), 64, 64, 64, 0, None, v(D), 1 << 20, None) == nf4.NF4_ERR_NULL
-    assert lib.nf4_layer_error(v(C), 64, 65, 64, 0, v(E), v(D), 1 << 20, None) == nf4.NF4_ERR_SHAPE
-    assert lib.nf4_layer_error(v(C), 64, 64, 64, 7, v(E), v(D), 1 << 20, None) == nf4.NF4_ERR_ARG
-    assert lib.nf4_layer_error(v(C), 64, 64, 64, 0, v(E), None, 0, None) == nf4.NF4_ERR_WORKSPACE
-    assert lib.nf4_layer_error(v(C), 64, 64, 64, 0, v(E), v(D), 8, None) == nf4.NF4_ERR_WORKSPACE
-    assert lib.nf4_layer_error(v(C), 64, 64, 64, 0, v(C + 16), v(D), 1 << 20, None) == nf4.NF4_ERR_ALIAS
+    assert lib.nf4_layer_error(v(C), 64, 64, 64, 0, 0, None, v(D), 1 << 20, None) == nf4.NF4_ERR_NULL
+    assert lib.nf4_layer_error(v(C), 64, 65, 64, 0, 0, v(E), v(D), 1 << 20, None) == nf4.NF4_ERR_SHAPE
+    assert lib.nf4_layer_error(v(C), 64, 64, 64, 7, 0, v(E), v(D), 1 << 20, None) == nf4.NF4_ERR_ARG
+    assert lib.nf4_layer_error(v(C), 64, 64, 64, 0, 0, v(E), None, 0, None) == nf4.NF4_ERR_WORKSPACE
+    assert lib.nf4_layer_error(v(C), 64, 64, 64, 0, 0, v(E), v(D), 8, None) == nf4.NF4_ERR_WORKSPACE
+    assert lib.nf4_layer_error(v(C), 64, 64, 64, 0, 0, v(C + 16), v(D), 1 << 20, None) == nf4.NF4_ERR_ALIAS
+    assert lib.nf4_layer_error(v(C), 64, 64, 64, 0, 3, v(E), v(D), 1 << 20, None) == nf4.NF4_ERR_ARG  # codebook
     assert lib.nf4_topk(v(C), 10, 11, v(D), None) == nf4.NF4_ERR_SHAPE
     assert lib.nf4_topk(v(C), 10, 3, None, None) == nf4.NF4_ERR_NULL
     assert lib.nf4_topk(v(C), 10, 3, v(C + 16), None) == nf4.NF4_ERR_ALIAS
@@ -243,3 +244,17 @@ def test_merge_validation():
     assert m(out=C + 64) == nf4.NF4_ERR_ALIAS                    # output inside W
     assert m(W=None, q=d, out=A) == nf4.NF4_ERR_ALIAS            # output over the codes
     assert m(rows=0) == nf4.NF4_OK
+
+
+def test_codebook_values_match_oracle():
+    for name in ("nf4", "int4", "fp4"):
+        got = nf4.codebook_values(name).numpy()
+        assert np.array_equal(got.view(np.uint32), oracle.codebook_table(name).view(np.uint32)), name
+    out = (ctypes.c_float * 16)()
+    assert lib.nf4_codebook_values(3, out) == nf4.NF4_ERR_ARG
+    assert lib.nf4_codebook_values(0, None) == nf4.NF4_ERR_NULL
+    # a descriptor naming an unknown codebook is rejected
+    d = desc()
+    d.codebook = 5
+    assert st_quant(d) == nf4.NF4_ERR_ARG
+

@@ -78,10 +78,10 @@ def test_quantize_dequantize_c2():
     assert np.array_equal(whb, oracle.dequantize_bf16_bits(ref))
 
 
-def edge_weights():
+def edge_weights(codebook="nf4"):
     """Blocks that stress the encoder: exact ties, zero/subnormal/huge blocks, spikes, ragged groups."""
     rng = np.random.default_rng(11)
-    t = oracle.nf4_table()
+    t = oracle.codebook_table(codebook)
     blocks = []
     # exact midpoints at several scales (ties take the lower code)
     for k in (0, -7, 9):
@@ -407,3 +407,48 @@ def test_merge(o, h, r, base):
     # 2^(floor(log2|v|) - 8) <= 2^-8 |v|
     tolb = 2.0 ** -8 * (np.abs(ref) + tol32) + tol32
     assert np.all(np.abs(gotb - ref) <= tolb), float(np.max(np.abs(gotb - ref) - tolb))
+
+
+# ---------------------------------------------------------------------------
+# other 4-bit codebooks (int4, fp4) through the same kernels
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("codebook", ["int4", "fp4"])
+@pytest.mark.parametrize("dq", [0, 256])
+def test_codebook_quantize(codebook, dq):
+    for W in (synth.layer_inputs(synth.C1)["W"], edge_weights(codebook)):
+        q = nf4.quantize(dev(W), dq, codebook=codebook)
+        ref = oracle.quantize(W, 64, dq, codebook)
+        check_quant(q, ref)
+        wh = nf4.dequantize(q).cpu().numpy()
+        assert np.array_equal(wh.view(np.uint32), oracle.dequantize(ref).view(np.uint32))
+        whb = nf4.dequantize(q, bf16=True).cpu().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(whb, oracle.dequantize_bf16_bits(ref))
+
+
+@pytest.mark.parametrize("codebook", ["int4", "fp4"])
+def test_codebook_layer_error(codebook):
+    for W, dq in ((synth.layer_weight(synth.C2)[:512], 0), (edge_weights(codebook), 256)):
+        got = float(nf4.layer_error(dev(W), dq, codebook=codebook).cpu())
+        want = oracle.layer_error(W, 64, dq, codebook)
+        say(f"  {codebook} dq={dq}: {got:.9f} vs {want:.9f}")
+        assert abs(got - want) <= 1e-6 * want
+
+
+@pytest.mark.parametrize("codebook", ["int4", "fp4"])
+def test_codebook_layer(codebook):
+    for d, s, dq in ((synth.layer_inputs(synth.C1), 2.0, 0),
+                     (synth.random_case(seed=9, rows=320, cols=192, M=37, r=17), 0.5, 256)):
+        q = nf4.quantize(dev(d["W"]), dq, codebook=codebook)
+        X, L1, L2, dY = (dev(d[k]) for k in ("X", "L1", "L2", "dY"))
+        Y, T = nf4.fwd(q, X, L1, L2, s)
+        dX, dL1, dL2 = nf4.bwd(q, X, dY, L1, L2, s, T=T)
+        torch.cuda.synchronize()
+        wh = oracle.dequantize(oracle.quantize(d["W"], 64, dq, codebook))
+        Yr, Tr = oracle.fwd(d["X"], wh, d["L1"], d["L2"], s)
+        dXr, dL1r, dL2r, _ = oracle.bwd(d["X"], d["dY"], wh, d["L1"], d["L2"], s)
+        check_close("Y", Y, Yr)
+        check_close("dX", dX, dXr)
+        check_close("dL1", dL1, dL1r)
+        check_close("dL2", dL2, dL2r)
+
