@@ -230,7 +230,8 @@ nf4_status bf16lora_bwd(const uint16_t *W, int64_t rows, int64_t cols, const uin
  * computed in fp32 (fp32 sum of the r products, then s * sum + base).
  *   base : W (fp32 [rows][cols]) when W != NULL, else q dequantized exactly
  *          as nf4_dequantize does (q->rows, q->cols must equal rows, cols).
- *   L1   : bf16 [cols][r];  L2 : bf16 [r][rows];  1 <= r <= 256.
+ *   L1   : bf16 [cols][r];  L2 : bf16 [r][rows];  1 <= r <= 256; both
+ *          16-byte aligned.
  *   W_out: fp32 [rows][cols] (out_is_bf16 == 0) or its bf16 rounding to
  *          nearest even; for an NF4 re-quantization pass the fp32 form to
  *          nf4_quantize.

@@ -33,11 +33,11 @@ print none), the 8-bit format of the double-quantized scales and the exact
 error formula (the AQLoRA page lost its equation); each is fixed by a stated
 reading and pinned only by the closed forms and invariants in the tests.
 """
-from .nf4 import (nf4_table, codebook_table, CODEBOOKS, quantize, dequantize, dequantize_bf16_bits, pack_codes,
+from .nf4 import (nf4_table, codebook_table, CODEBOOKS, quantize, quantize_residual, dequantize_residual, dequantize, dequantize_bf16_bits, pack_codes,
                   unpack_codes, layer_error, storage_bytes, protect_count, topk,
                   NF4Quant)
 from .lora import fwd, bwd, adapter_grads, merge
 
-__all__ = ["nf4_table", "codebook_table", "CODEBOOKS", "quantize", "dequantize", "dequantize_bf16_bits", "pack_codes",
+__all__ = ["nf4_table", "codebook_table", "CODEBOOKS", "quantize", "quantize_residual", "dequantize_residual", "dequantize", "dequantize_bf16_bits", "pack_codes",
            "unpack_codes", "layer_error", "storage_bytes", "protect_count", "topk",
            "NF4Quant", "fwd", "bwd", "adapter_grads", "merge"]

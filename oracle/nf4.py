@@ -190,6 +190,27 @@ def dequantize_bf16_bits(q: NF4Quant) -> np.ndarray:
     return w.view(torch.int16).numpy().view(np.uint16)
 
 
+def quantize_residual(W, block: int = BLOCK, dq_group: int = 0, codebook: str = "nf4"):
+    """Two-stage quantization: the weight, then what the first stage missed.
+
+    AQLoRA summary, section 7 (additional controls): a second NF4 stage over
+    the residuals of the first also works.  The pages give no further detail;
+    the reading taken is the plain one: q1 = quantize(W); the residual
+    R = fl32(W - w_hat1) (fp32 subtraction of the first stage's dequantized
+    weight); q2 = quantize(R) with the same block, double-quant group and
+    codebook.  Returns (q1, q2).
+    """
+    W = np.ascontiguousarray(np.asarray(W, dtype=np.float32))
+    q1 = quantize(W, block, dq_group, codebook)
+    R = (W - dequantize(q1)).astype(np.float32)
+    return q1, quantize(R, block, dq_group, codebook)
+
+
+def dequantize_residual(q1: NF4Quant, q2: NF4Quant) -> np.ndarray:
+    """The two-stage weight: w_hat = fl32(w_hat1 + w_hat2), fp32 [rows][cols]."""
+    return (dequantize(q1) + dequantize(q2)).astype(np.float32)
+
+
 def layer_error(W, block: int = BLOCK, dq_group: int = 0, codebook: str = "nf4") -> float:
     """Relative Frobenius NF4 reconstruction error ||W - W_hat||_F / ||W||_F, fp64.
 

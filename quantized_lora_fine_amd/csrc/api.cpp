@@ -662,7 +662,7 @@ nf4_status nf4lora_merge(const float* W, const nf4_tensor* q, int64_t rows, int6
   }
   if (n == 0) return NF4_OK;
   if (!L1 || !L2 || !W_out) return NF4_ERR_NULL;
-  if (!aligned16(W_out)) return NF4_ERR_ALIGN;
+  if (!aligned16(W_out) || !aligned16(L1) || !aligned16(L2)) return NF4_ERR_ALIGN;
   const Range out = rng(W_out, (size_t)n * (out_is_bf16 ? 2 : 4));
   if (overlap(out, wb[0]) || overlap(out, wb[1]) || overlap(out, wb[2]) ||
       overlap(out, rng(L1, (size_t)cols * r * 2)) || overlap(out, rng(L2, (size_t)r * rows * 2)))

@@ -52,15 +52,28 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ W, cons
   for (int j0 = 0; j0 < r; j0 += MG_RC) {
     const int jn = min(MG_RC, r - j0);
     __syncthreads();  // previous chunk fully read
-    for (int e = t; e < MG_RC * MG_COLS; e += 256) {
-      const int jj = e % MG_RC, kk = e / MG_RC;  // consecutive threads walk j: contiguous L1 reads
-      const int64_t k = k0 + kk;
-      l1t[jj * MG_LDT + kk] = (jj < jn && k < cols) ? L1[k * r + j0 + jj] : (uint16_t)0;
+    if ((r & 7) == 0) {
+      // 8 adapter columns per 16-byte load (L1 rows are 16-byte aligned when r % 8 == 0)
+      const int j8n = jn >> 3;
+      for (int e = t; e < j8n * MG_COLS; e += 256) {
+        const int j8 = e % j8n, kk = e / j8n;
+        const int64_t k = k0 + kk;
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (k < cols) v = *(const u32x4*)(L1 + k * r + j0 + j8 * 8);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) l1t[(j8 * 8 + q) * MG_LDT + kk] = (uint16_t)(v[q >> 1] >> (16 * (q & 1)));
+      }
+    } else {
+      for (int e = t; e < jn * MG_COLS; e += 256) {
+        const int jj = e % jn, kk = e / jn;  // consecutive threads walk j: contiguous L1 reads
+        const int64_t k = k0 + kk;
+        l1t[jj * MG_LDT + kk] = k < cols ? L1[k * r + j0 + jj] : (uint16_t)0;
+      }
     }
-    for (int e = t; e < MG_RC * MG_ROWS; e += 256) {
+    for (int e = t; e < jn * MG_ROWS; e += 256) {
       const int jj = e / MG_ROWS, nl = e % MG_ROWS;
       const int64_t n = n0 + nl;
-      l2s[e] = (jj < jn && n < rows) ? bf16_to_f32(L2[(int64_t)(j0 + jj) * rows + n]) : 0.f;
+      l2s[e] = n < rows ? bf16_to_f32(L2[(int64_t)(j0 + jj) * rows + n]) : 0.f;
     }
     __syncthreads();
     for (int jj = 0; jj < jn; ++jj) {

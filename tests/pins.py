@@ -560,11 +560,45 @@ def pin_codebook_roundtrip(quantize_fn=onf4.quantize, dequantize_fn=onf4.dequant
         assert np.array_equal(wh.reshape(-1).view(np.uint32), W.reshape(-1).view(np.uint32)), cb
 
 
+# ---------------------------------------------------------------------------
+# residual second stage
+# ---------------------------------------------------------------------------
+
+def pin_residual(quantize_res_fn=onf4.quantize_residual, dequantize_res_fn=onf4.dequantize_residual,
+                 table_fn=onf4.nf4_table, seed=21):
+    """The second stage quantizes fl32(W - w_hat1) exactly as brute force does; on an exactly
+    representable W the residual is zero (codes of 0, zero scales) and w_hat == W; and since 0 is a
+    code, every residual element is reconstructed at least as well as by 0, so the two-stage error
+    never exceeds the one-stage error."""
+    rng = np.random.default_rng(seed)
+    table = table_fn()
+    W = (rng.standard_t(4, size=(6, 128)) * 0.02).astype(np.float32)
+    q1, q2 = quantize_res_fn(W, 64, 0)
+    R = (W.astype(np.float64) - onf4.dequantize(q1).astype(np.float64))  # exact difference
+    Rf = np.array([f32_nearest(fr(v)) for v in R.reshape(-1)], np.float32).reshape(R.shape)
+    for b, blk in enumerate(Rf.reshape(-1, 64)):
+        ref, a = brute_codes(blk, table)
+        assert list(q2.codes.reshape(-1, 64)[b]) == ref and q2.absmax[b] == a, b
+    r2 = np.abs(R - onf4.dequantize(q2).astype(np.float64))
+    assert np.all(r2 <= np.abs(Rf.astype(np.float64)) + 1e-12), "0 is a code: never worse than 0"
+    e1 = np.linalg.norm(W.astype(np.float64) - onf4.dequantize(q1))
+    e2 = np.linalg.norm(W.astype(np.float64) - dequantize_res_fn(q1, q2))
+    assert e2 <= e1 * (1 + 1e-6) and e2 < 0.5 * e1
+    # exact grid: the residual vanishes
+    c = rng.integers(0, 16, size=(8, 64)).astype(np.uint8)
+    c[:, 0] = 15
+    Wg = (table[c] * np.float32(0.125)).astype(np.float32)
+    for dq in (0, 256):
+        g1, g2 = quantize_res_fn(Wg.reshape(2, -1), 64, dq)
+        assert np.all(g2.codes == 7) and np.all(g2.absmax == 0)
+        assert np.array_equal(dequantize_res_fn(g1, g2).reshape(-1), Wg.reshape(-1))
+
+
 ALL_PINS = [
     pin_table_structure, pin_table_independent, pin_encoder_bruteforce, pin_exact_ties,
     pin_midpoint_sweeps, pin_roundtrip, pin_absmax_exact, pin_scale_invariance,
     pin_dq_codes_unchanged, pin_dq_exact, pin_dq_bound, pin_pack, pin_storage,
     pin_fwd_bruteforce, pin_fwd_merge, pin_fwd_special, pin_bwd_finite_diff, pin_bwd_special,
     pin_error_bruteforce, pin_error_zero_on_grid, pin_error_tails, pin_counts, pin_topk,
-    pin_codebook_tables, pin_codebook_encoders, pin_codebook_roundtrip,
+    pin_codebook_tables, pin_codebook_encoders, pin_codebook_roundtrip, pin_residual,
 ]

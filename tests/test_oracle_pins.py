@@ -189,3 +189,13 @@ def test_mistake_codebooks():
         q.codes = (15 - np.argmin(d[:, ::-1], axis=1)).astype(np.uint8)
         return q
     assert _fails(pins.pin_codebook_encoders, upper_tie_quantize)
+
+
+def test_mistake_residual():
+    # the second stage dropped from the dequantized weight, or quantizing W twice instead of the residual
+    ignore_q2 = lambda q1, q2: oracle.dequantize(q1)
+    assert _fails(pins.pin_residual, dequantize_res_fn=ignore_q2)
+    def twice(W, block=64, dq=0, codebook="nf4"):
+        q1 = oracle.quantize(W, block, dq, codebook)
+        return q1, oracle.quantize(W, block, dq, codebook)
+    assert _fails(pins.pin_residual, quantize_res_fn=twice)
