@@ -226,6 +226,27 @@ def main():
         codebooks[cbn] = {"rel_frobenius_error": round(float(err_c.cpu()), 6),
                           "quantize_us": round(1e3 * e0.elapsed_time(e1) / args.steps, 3)}
 
+    # the second NF4 stage over the residual: fwd+bwd with the two-stage weight against one stage
+    q_res = nf4.quantize(W, 256, residual=True)
+    res_ms = {}
+    for name, qq in (("one_stage", q), ("two_stage", q_res)):
+        def fb():
+            nf4.fwd(qq, X, L1, L2, s, ws=ws_f, out=Y, T_out=T)
+            nf4.bwd(qq, X, dY, L1, L2, s, T=T, ws=ws_b, outs=(dX, dL1, dL2))
+        for _ in range(args.warmup):
+            fb()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fb()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res_ms[name] = e0.elapsed_time(e1) / args.steps
+    residual = {"fwd_bwd_ms_one_stage": round(res_ms["one_stage"], 5),
+                "fwd_bwd_ms_two_stage": round(res_ms["two_stage"], 5),
+                "overhead_pct": round(100.0 * (res_ms["two_stage"] / res_ms["one_stage"] - 1.0), 2)}
+    del q_res
+
     dom = max(("nf4_gemm_fwd", "nf4_gemm_dx"), key=lambda k: kernels[k]["us"])
     ach = kernels[dom]["tflops"]
     traffic = None
@@ -265,6 +286,7 @@ def main():
         "op_ms": {k: round(v, 5) for k, v in op_ms.items()},
         "kernels": kernels,
         "codebooks": codebooks,
+        "residual_stage": residual,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define NF4LORA_ABI_VERSION 2
+#define NF4LORA_ABI_VERSION 3
 
 typedef enum nf4_status {
   NF4_OK = 0,
@@ -76,6 +76,13 @@ typedef enum nf4_status {
  *                NF4) or the E2M1 4-bit float / 6 (the ordinary-float curve of
  *                the QLoRA blog's figure 3).  Zero-initialised descriptors
  *                are NF4.
+ *   residual   : NULL, or a second tensor of the same rows, cols, block,
+ *                dq_group and codebook (with no residual of its own) that
+ *                holds the quantized residual of this one: the second NF4
+ *                stage of AQLoRA's additional controls (section 7).
+ *                nf4_quantize then fills both (second stage: quantize
+ *                fl32(w - w_hat1)), and every consumer uses
+ *                w_hat = fl32(w_hat1 + w_hat2).
  * Dequantized weight: w_hat = fl32(table[code] * scale), scale = absmax
  * (fp32) or fl32(c8 * dq_scale[group]).  nblocks = rows*cols/64.
  */
@@ -88,6 +95,7 @@ typedef struct nf4_tensor {
   void *absmax;
   float *dq_scale;
   int32_t codebook;
+  const struct nf4_tensor *residual;
 } nf4_tensor;
 
 /* Codebooks for nf4_tensor.codebook and nf4_layer_error. */

@@ -31,9 +31,13 @@ DQ_GROUP = 256
 
 
 class _NF4Tensor(ctypes.Structure):
-    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("block", ctypes.c_int32),
-                ("dq_group", ctypes.c_int32), ("codes", ctypes.c_void_p), ("absmax", ctypes.c_void_p),
-                ("dq_scale", ctypes.c_void_p), ("codebook", ctypes.c_int32)]
+    pass
+
+
+_NF4Tensor._fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("block", ctypes.c_int32),
+                       ("dq_group", ctypes.c_int32), ("codes", ctypes.c_void_p), ("absmax", ctypes.c_void_p),
+                       ("dq_scale", ctypes.c_void_p), ("codebook", ctypes.c_int32),
+                       ("residual", ctypes.POINTER(_NF4Tensor))]
 
 
 class _NF4Linear(ctypes.Structure):
@@ -145,7 +149,8 @@ def _u16(t: torch.Tensor) -> torch.Tensor:
 class NF4Weight:
     """A quantized weight: the three device buffers plus the C descriptor."""
 
-    def __init__(self, rows: int, cols: int, dq_group: int = 0, device="cuda", codebook: str = "nf4"):
+    def __init__(self, rows: int, cols: int, dq_group: int = 0, device="cuda", codebook: str = "nf4",
+                 residual: bool = False):
         cb, ab, db = tensor_bytes(rows, cols, dq_group)
         self.rows, self.cols, self.dq_group, self.codebook = rows, cols, dq_group, codebook
         self.codes = torch.empty(max(cb, 1), dtype=torch.uint8, device=device)
@@ -154,6 +159,10 @@ class NF4Weight:
         self.desc = _NF4Tensor(rows, cols, BLOCK, dq_group, self.codes.data_ptr(), self.absmax.data_ptr(),
                                self.dq_scale.data_ptr() if dq_group else None, CODEBOOKS[codebook])
         self._cb, self._ab, self._db = cb, ab, db
+        # the second quantization stage (quantized residual of this one), when requested
+        self.residual = NF4Weight(rows, cols, dq_group, device, codebook) if residual else None
+        if self.residual is not None:
+            self.desc.residual = ctypes.pointer(self.residual.desc)
 
     @property
     def absmax_f32(self) -> torch.Tensor:
@@ -172,10 +181,12 @@ class NF4Weight:
         return self.codes[:self._cb]
 
 
-def quantize(W: torch.Tensor, dq_group: int = 0, out: NF4Weight | None = None, codebook: str = "nf4") -> NF4Weight:
-    """nf4_quantize of a cuda fp32 [rows][cols] tensor (into `out` when given; its codebook then applies)."""
+def quantize(W: torch.Tensor, dq_group: int = 0, out: NF4Weight | None = None, codebook: str = "nf4",
+             residual: bool = False) -> NF4Weight:
+    """nf4_quantize of a cuda fp32 [rows][cols] tensor (into `out` when given; its codebook and residual stage
+    then apply).  residual=True also quantizes what the first stage misses into q.residual."""
     assert W.dtype == torch.float32 and W.is_cuda and W.is_contiguous() and W.dim() == 2
-    q = out if out is not None else NF4Weight(W.shape[0], W.shape[1], dq_group, W.device, codebook)
+    q = out if out is not None else NF4Weight(W.shape[0], W.shape[1], dq_group, W.device, codebook, residual)
     _check(_lib.nf4_quantize(_ptr(W), ctypes.byref(q.desc), _stream()), "nf4_quantize")
     return q
 

@@ -34,7 +34,10 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
 # per-source extra flags: the quantization kernels must round exactly as the
 # format defines (one rounding per multiply, no fused multiply-add across
 # statements)
-EXTRA = {"quant.hip": ["-ffp-contract=off"]}
+EXTRA = {"quant.hip": ["-ffp-contract=off"],
+         # dequantized weights (and the two-stage sum) must round like nf4_dequantize: no fused multiply-add
+         "gemm.hip": ["-ffp-contract=off"],
+         "merge.hip": ["-ffp-contract=off"]}
 
 HIP_SOURCES = ["quant.hip", "gemm.hip", "skinny.hip", "merge.hip"]
 CPP_SOURCES = ["api.cpp", "nf4_table.cpp"]

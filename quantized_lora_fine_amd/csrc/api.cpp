@@ -66,6 +66,25 @@ nf4_status check_tensor(const nf4_tensor* q) {
   nf4_status st = check_shape(q->rows, q->cols, q->block, q->dq_group);
   if (st != NF4_OK) return st;
   if (q->codebook < 0 || q->codebook >= kCodebooks) return NF4_ERR_ARG;
+  if (q->residual) {
+    const nf4_tensor* r = q->residual;
+    if (r->residual || r == q) return NF4_ERR_ARG;
+    if (r->rows != q->rows || r->cols != q->cols || r->block != q->block || r->dq_group != q->dq_group ||
+        r->codebook != q->codebook)
+      return NF4_ERR_SHAPE;
+    if (q->rows * q->cols > 0) {
+      if (!r->codes || !r->absmax || (r->dq_group && !r->dq_scale)) return NF4_ERR_NULL;
+      if (!aligned16(r->codes) || !aligned16(r->absmax) || (r->dq_group && !aligned16(r->dq_scale)))
+        return NF4_ERR_ALIGN;
+      size_t cb, ab, db;
+      tensor_sizes(q->rows, q->cols, q->dq_group, &cb, &ab, &db);
+      const Range a[3] = {rng(q->codes, cb), rng(q->absmax, ab), rng(q->dq_scale, db)};
+      const Range b[3] = {rng(r->codes, cb), rng(r->absmax, ab), rng(r->dq_scale, db)};
+      for (const Range& x : a)
+        for (const Range& y : b)
+          if (overlap(x, y)) return NF4_ERR_ALIAS;
+    }
+  }
   if (q->rows * q->cols > 0) {
     if (!q->codes || !q->absmax) return NF4_ERR_NULL;
     if (q->dq_group && !q->dq_scale) return NF4_ERR_NULL;
@@ -181,8 +200,24 @@ struct WSrc {
   const uint8_t* codes;
   const void* absmax;
   const float* dqs;
-  Range buf[3];  // the weight's buffers, for the aliasing checks
+  const uint8_t* codes2;  // residual stage, or NULL
+  const void* absmax2;
+  const float* dqs2;
+  Range buf[6];  // the weight's buffers, for the aliasing checks
 };
+
+// the buffers of a quantized tensor and of its residual stage (empty ranges when absent)
+void tensor_ranges(const nf4_tensor* q, Range out[6]) {
+  size_t cb, ab, db;
+  tensor_sizes(q->rows, q->cols, q->dq_group, &cb, &ab, &db);
+  out[0] = rng(q->codes, cb);
+  out[1] = rng(q->absmax, ab);
+  out[2] = rng(q->dq_scale, db);
+  const nf4_tensor* r = q->residual;
+  out[3] = rng(r ? r->codes : nullptr, r ? cb : 0);
+  out[4] = rng(r ? r->absmax : nullptr, r ? ab : 0);
+  out[5] = rng(r ? r->dq_scale : nullptr, r ? db : 0);
+}
 
 nf4_status layer_shape(int64_t rows, int64_t cols) {
   if (rows <= 0 || cols <= 0 || rows % kBlock != 0 || cols % kBlock != 0) return NF4_ERR_SHAPE;
@@ -195,8 +230,6 @@ nf4_status wsrc_nf4(const nf4_tensor* W, WSrc* w) {
   if (st != NF4_OK) return st;
   st = layer_shape(W->rows, W->cols);
   if (st != NF4_OK) return st;
-  size_t cb, ab, db;
-  tensor_sizes(W->rows, W->cols, W->dq_group, &cb, &ab, &db);
   w->src = W->dq_group ? kSrcNF4DQ : kSrcNF4;
   w->codebook = W->codebook;
   w->rows = W->rows;
@@ -205,9 +238,10 @@ nf4_status wsrc_nf4(const nf4_tensor* W, WSrc* w) {
   w->codes = W->codes;
   w->absmax = W->absmax;
   w->dqs = W->dq_scale;
-  w->buf[0] = rng(W->codes, cb);
-  w->buf[1] = rng(W->absmax, ab);
-  w->buf[2] = rng(W->dq_scale, db);
+  w->codes2 = W->residual ? W->residual->codes : nullptr;
+  w->absmax2 = W->residual ? W->residual->absmax : nullptr;
+  w->dqs2 = W->residual ? W->residual->dq_scale : nullptr;
+  tensor_ranges(W, w->buf);
   return NF4_OK;
 }
 
@@ -225,9 +259,11 @@ nf4_status wsrc_bf16(const uint16_t* W, int64_t rows, int64_t cols, WSrc* w) {
   w->codes = nullptr;
   w->absmax = nullptr;
   w->dqs = nullptr;
+  w->codes2 = nullptr;
+  w->absmax2 = nullptr;
+  w->dqs2 = nullptr;
   w->buf[0] = rng(W, (size_t)(rows * cols * 2));
-  w->buf[1] = rng(nullptr, 0);
-  w->buf[2] = rng(nullptr, 0);
+  for (int i = 1; i < 6; ++i) w->buf[i] = rng(nullptr, 0);
   return NF4_OK;
 }
 
@@ -241,8 +277,8 @@ hipError_t gemm(int mode, const WSrc& w, const uint16_t* A, const uint16_t* A2, 
                 uint16_t* C, int64_t M, hipStream_t st) {
   const int64_t N = mode == MODE_FWD ? w.rows : w.cols;
   const int64_t K = mode == MODE_FWD ? w.cols : w.rows;
-  return launch_nf4_gemm(mode, w.src, A, w.wb, w.codes, w.absmax, w.dqs, A2, B2, R, C, M, (int)N, (int)K,
-                         codebook_consts(w.codebook), st);
+  return launch_nf4_gemm(mode, w.src, A, w.wb, w.codes, w.absmax, w.dqs, w.codes2, w.absmax2, w.dqs2, A2, B2, R,
+                         C, M, (int)N, (int)K, codebook_consts(w.codebook), st);
 }
 
 nf4_status layer_fwd(const WSrc& W, const uint16_t* X, int64_t M, const uint16_t* L1, const uint16_t* L2,
@@ -260,7 +296,7 @@ nf4_status layer_fwd(const WSrc& W, const uint16_t* X, int64_t M, const uint16_t
   if (ws_bytes < p.total) return NF4_ERR_WORKSPACE;
   if (!aligned16(ws)) return NF4_ERR_ALIGN;
   const Range ins[] = {rng(X, (size_t)M * h * 2), rng(L1, (size_t)h * r * 2), rng(L2, (size_t)r * o * 2),
-                       W.buf[0], W.buf[1], W.buf[2]};
+                       W.buf[0], W.buf[1], W.buf[2], W.buf[3], W.buf[4], W.buf[5]};
   const Range outs[] = {rng(Y, (size_t)M * o * 2), rng(T_out, T_out ? (size_t)M * r * 2 : 0),
                         rng(ws, p.total)};
   for (const Range& a : outs) {
@@ -308,7 +344,8 @@ nf4_status layer_bwd(const WSrc& W, const uint16_t* X, const uint16_t* dY, int64
   const Range ins[] = {rng(X, (size_t)M * h * 2),     rng(dY, (size_t)M * o * 2),
                        rng(L1, (size_t)h * r * 2),    rng(L2, (size_t)r * o * 2),
                        rng(T, T ? (size_t)M * r * 2 : 0), W.buf[0],
-                       W.buf[1],                      W.buf[2]};
+                       W.buf[1],                      W.buf[2],
+                       W.buf[3],                      W.buf[4], W.buf[5]};
   const Range outs[] = {rng(dX, dX ? (size_t)M * h * 2 : 0), rng(dL1, (size_t)h * r * 4),
                         rng(dL2, (size_t)r * o * 4), rng(ws, p.total)};
   for (const Range& a : outs) {
@@ -387,9 +424,9 @@ nf4_status plain_product(int mode, const WSrc& w, const uint16_t* A, uint16_t* C
   if (!aligned16(A) || !aligned16(C)) return NF4_ERR_ALIGN;
   const int64_t K = mode == MODE_FWD ? w.cols : w.rows, N = mode == MODE_FWD ? w.rows : w.cols;
   const Range out = rng(C, (size_t)M * N * 2);
-  if (overlap(out, rng(A, (size_t)M * K * 2)) || overlap(out, w.buf[0]) || overlap(out, w.buf[1]) ||
-      overlap(out, w.buf[2]))
-    return NF4_ERR_ALIAS;
+  if (overlap(out, rng(A, (size_t)M * K * 2))) return NF4_ERR_ALIAS;
+  for (const Range& b : w.buf)
+    if (overlap(out, b)) return NF4_ERR_ALIAS;
   return hip_status(gemm(mode, w, A, nullptr, nullptr, 0, C, M, (hipStream_t)stream));
 }
 
@@ -445,14 +482,18 @@ nf4_status nf4_quantize(const float* W, const nf4_tensor* q, void* stream) {
   if (n == 0) return NF4_OK;
   if (!W) return NF4_ERR_NULL;
   if (!aligned16(W)) return NF4_ERR_ALIGN;
-  size_t cb, ab, db;
-  tensor_sizes(q->rows, q->cols, q->dq_group, &cb, &ab, &db);
+  Range bufs[6];
+  tensor_ranges(q, bufs);
   const Range in = rng(W, (size_t)n * 4);
-  if (overlap(in, rng(q->codes, cb)) || overlap(in, rng(q->absmax, ab)) ||
-      (db && overlap(in, rng(q->dq_scale, db))) || overlap(rng(q->codes, cb), rng(q->absmax, ab)))
-    return NF4_ERR_ALIAS;
+  for (int i = 0; i < 6; ++i) {
+    if (overlap(in, bufs[i])) return NF4_ERR_ALIAS;
+    for (int j = i + 1; j < 6; ++j)
+      if (overlap(bufs[i], bufs[j])) return NF4_ERR_ALIAS;
+  }
+  const nf4_tensor* r = q->residual;
   return hip_status(launch_quantize(W, n / kBlock, q->dq_group != 0, q->codes, q->absmax, q->dq_scale,
-                                    codebook_enc(q->codebook), (hipStream_t)stream));
+                                    r ? r->codes : nullptr, r ? r->absmax : nullptr, r ? r->dq_scale : nullptr,
+                                    codebook_enc(q->codebook), codebook_consts(q->codebook), (hipStream_t)stream));
 }
 
 nf4_status nf4_dequantize(const nf4_tensor* q, void* W_out, int32_t out_is_bf16, void* stream) {
@@ -462,14 +503,15 @@ nf4_status nf4_dequantize(const nf4_tensor* q, void* W_out, int32_t out_is_bf16,
   if (n == 0) return NF4_OK;
   if (!W_out) return NF4_ERR_NULL;
   if (!aligned16(W_out)) return NF4_ERR_ALIGN;
-  size_t cb, ab, db;
-  tensor_sizes(q->rows, q->cols, q->dq_group, &cb, &ab, &db);
+  Range bufs[6];
+  tensor_ranges(q, bufs);
   const Range out = rng(W_out, (size_t)n * (out_is_bf16 ? 2 : 4));
-  if (overlap(out, rng(q->codes, cb)) || overlap(out, rng(q->absmax, ab)) ||
-      (db && overlap(out, rng(q->dq_scale, db))))
-    return NF4_ERR_ALIAS;
-  return hip_status(launch_dequantize(q->codes, q->absmax, q->dq_scale, n, q->dq_group != 0, out_is_bf16 != 0,
-                                      W_out, codebook_consts(q->codebook), (hipStream_t)stream));
+  for (const Range& b : bufs)
+    if (overlap(out, b)) return NF4_ERR_ALIAS;
+  const nf4_tensor* r = q->residual;
+  return hip_status(launch_dequantize(q->codes, q->absmax, q->dq_scale, r ? r->codes : nullptr,
+                                      r ? r->absmax : nullptr, r ? r->dq_scale : nullptr, n, q->dq_group != 0,
+                                      out_is_bf16 != 0, W_out, codebook_consts(q->codebook), (hipStream_t)stream));
 }
 
 nf4_status nf4_workspace_bytes(int32_t op, int64_t M, int64_t rows, int64_t cols, int32_t r, size_t* bytes) {
@@ -534,16 +576,15 @@ nf4_status nf4_matmul(const nf4_tensor* W, int32_t transpose, const uint16_t* A,
   if (!aligned16(A) || !aligned16(C) || (R > 0 && (!aligned16(A2) || !aligned16(B2)))) return NF4_ERR_ALIGN;
   const int64_t o = W->rows, h = W->cols;
   const int64_t K = transpose ? o : h, N = transpose ? h : o;
-  size_t cb, ab, db;
-  tensor_sizes(o, h, W->dq_group, &cb, &ab, &db);
-  const Range out = rng(C, (size_t)M * N * 2);
-  const Range ins[] = {rng(A, (size_t)M * K * 2), rng(A2, R ? (size_t)M * R * 2 : 0), rng(B2, R ? (size_t)N * R * 2 : 0),
-                       rng(W->codes, cb), rng(W->absmax, ab), rng(W->dq_scale, db)};
-  for (const Range& b : ins)
-    if (overlap(out, b)) return NF4_ERR_ALIAS;
   WSrc w;
   st = wsrc_nf4(W, &w);
   if (st != NF4_OK) return st;
+  const Range out = rng(C, (size_t)M * N * 2);
+  const Range ins[] = {rng(A, (size_t)M * K * 2), rng(A2, R ? (size_t)M * R * 2 : 0), rng(B2, R ? (size_t)N * R * 2 : 0)};
+  for (const Range& b : ins)
+    if (overlap(out, b)) return NF4_ERR_ALIAS;
+  for (const Range& b : w.buf)
+    if (overlap(out, b)) return NF4_ERR_ALIAS;
   return hip_status(gemm(transpose ? MODE_DX : MODE_FWD, w, A, A2, B2, R, C, M, (hipStream_t)stream));
 }
 
@@ -643,18 +684,15 @@ nf4_status nf4lora_merge(const float* W, const nf4_tensor* q, int64_t rows, int6
   if (r < 1 || r > 256) return NF4_ERR_SHAPE;
   if (rows > INT32_MAX / 2 || cols > INT32_MAX / 2) return NF4_ERR_SHAPE;
   const int64_t n = rows * cols;
-  Range wb[3] = {rng(nullptr, 0), rng(nullptr, 0), rng(nullptr, 0)};
+  Range wb[6];
+  for (Range& x : wb) x = rng(nullptr, 0);
   int base = 0;
   if (!W) {
     if (!q) return NF4_ERR_NULL;
     st = check_tensor(q);
     if (st != NF4_OK) return st;
     if (q->rows != rows || q->cols != cols) return NF4_ERR_SHAPE;
-    size_t cb, ab, db;
-    tensor_sizes(rows, cols, q->dq_group, &cb, &ab, &db);
-    wb[0] = rng(q->codes, cb);
-    wb[1] = rng(q->absmax, ab);
-    wb[2] = rng(q->dq_scale, db);
+    tensor_ranges(q, wb);
     base = q->dq_group ? 2 : 1;
   } else {
     if (!aligned16(W)) return NF4_ERR_ALIGN;
@@ -664,12 +702,16 @@ nf4_status nf4lora_merge(const float* W, const nf4_tensor* q, int64_t rows, int6
   if (!L1 || !L2 || !W_out) return NF4_ERR_NULL;
   if (!aligned16(W_out) || !aligned16(L1) || !aligned16(L2)) return NF4_ERR_ALIGN;
   const Range out = rng(W_out, (size_t)n * (out_is_bf16 ? 2 : 4));
-  if (overlap(out, wb[0]) || overlap(out, wb[1]) || overlap(out, wb[2]) ||
-      overlap(out, rng(L1, (size_t)cols * r * 2)) || overlap(out, rng(L2, (size_t)r * rows * 2)))
+  if (overlap(out, rng(L1, (size_t)cols * r * 2)) || overlap(out, rng(L2, (size_t)r * rows * 2)))
     return NF4_ERR_ALIAS;
-  return hip_status(launch_merge(base, W, q && !W ? q->codes : nullptr, q && !W ? q->absmax : nullptr,
-                                 q && !W ? q->dq_scale : nullptr, L1, L2, r, s, rows, cols, out_is_bf16 != 0,
-                                 W_out, codebook_consts(q && !W ? q->codebook : 0), (hipStream_t)stream));
+  for (const Range& b : wb)
+    if (overlap(out, b)) return NF4_ERR_ALIAS;
+  const nf4_tensor* qq = W ? nullptr : q;  // the NF4 base, when the fp32 base is absent
+  const nf4_tensor* rr = qq ? qq->residual : nullptr;
+  return hip_status(launch_merge(base, W, qq ? qq->codes : nullptr, qq ? qq->absmax : nullptr,
+                                 qq ? qq->dq_scale : nullptr, rr ? rr->codes : nullptr, rr ? rr->absmax : nullptr,
+                                 rr ? rr->dq_scale : nullptr, L1, L2, r, s, rows, cols, out_is_bf16 != 0, W_out,
+                                 codebook_consts(qq ? qq->codebook : 0), (hipStream_t)stream));
 }
 
 }  // extern "C"

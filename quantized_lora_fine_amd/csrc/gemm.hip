@@ -57,6 +57,9 @@ struct GemmArgs {
   const uint8_t* codes;
   const void* absmax;
   const float* dqs;
+  const uint8_t* codes2;  // residual (second-stage) NF4 tensor, same layout (RES)
+  const void* absmax2;
+  const float* dqs2;
   const uint16_t* A2;
   const uint16_t* B2;
   uint16_t* C;
@@ -77,7 +80,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcFlags);
 }
 
-template <int MODE, int SRC>
+template <int MODE, int SRC, bool RES>
 __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
   constexpr bool DQ = SRC == kSrcNF4DQ;
   constexpr bool BF = SRC == kSrcBF16;
@@ -176,10 +179,40 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
     }
     const __amdgpu_buffer_rsrc_t s_rsrc = make_rsrc(p.absmax, (uint32_t)(p.nblocks * (DQ ? 1 : 4)));
     const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(p.dqs, (uint32_t)(DQ ? ((p.nblocks + 255) / 256) * 4 : 0));
+    // the residual stage: same offsets into its own buffers
+    __amdgpu_buffer_rsrc_t c2_rsrc = c_rsrc, s2_rsrc = s_rsrc, q2_rsrc = q_rsrc;
+    if constexpr (RES) {
+      if constexpr (MODE == MODE_FWD) {
+        const int nrows = (N - n0) < GBN ? (N - n0) : GBN;
+        c2_rsrc = make_rsrc(p.codes2 + (int64_t)n0 * (K >> 1), (uint32_t)((int64_t)nrows * (K >> 1)));
+      } else {
+        c2_rsrc = make_rsrc(p.codes2, (uint32_t)(p.nblocks * 32));
+      }
+      s2_rsrc = make_rsrc(p.absmax2, (uint32_t)(p.nblocks * (DQ ? 1 : 4)));
+      q2_rsrc = make_rsrc(p.dqs2, (uint32_t)(DQ ? ((p.nblocks + 255) / 256) * 4 : 0));
+    }
 
-    u32x4 creg[2];
-    uint32_t sraw[2][4];
-    float sstep[2][4];
+    u32x4 creg[2], creg2[2];
+    uint32_t sraw[2][4], sraw2[2][4];
+    float sstep[2][4], sstep2[2][4];
+    auto load_scale2 = [&](uint32_t blk, int set, int i) {
+      if constexpr (DQ) {
+        sraw2[set][i] = __builtin_amdgcn_raw_buffer_load_b8(s2_rsrc, blk, 0, 0);
+        sstep2[set][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(q2_rsrc, (blk >> 8) * 4, 0, 0));
+      } else {
+        sraw2[set][i] = __builtin_amdgcn_raw_buffer_load_b32(s2_rsrc, blk * 4, 0, 0);
+      }
+    };
+    auto scale2 = [&](int set, int i) -> float {
+      if constexpr (DQ) return (float)sraw2[set][i] * sstep2[set][i];
+      else return __builtin_bit_cast(float, sraw2[set][i]);
+    };
+    // dequantized weight of one code: fl32(t * sc), or with the residual stage
+    // fl32(fl32(t * sc) + fl32(t2 * sc2)) (no fused multiply-add)
+    auto wval = [&](float t, float sc, float t2, float sc2) -> float {
+      if constexpr (RES) return __fadd_rn(__fmul_rn(t, sc), __fmul_rn(t2, sc2));
+      else return t * sc;
+    };
     auto load_scale = [&](uint32_t blk, int set, int i) {
       if constexpr (DQ) {
         sraw[set][i] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, blk, 0, 0);
@@ -208,6 +241,10 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
       } else if constexpr (MODE == MODE_FWD) {
         creg[set] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, c_voff[0] + kt * 32, 0, 0);
         load_scale(s_voff[0] + kt, set, 0);
+        if constexpr (RES) {
+          creg2[set] = __builtin_amdgcn_raw_buffer_load_b128(c2_rsrc, c_voff[0] + kt * 32, 0, 0);
+          load_scale2(s_voff[0] + kt, set, 0);
+        }
       } else {
         const uint32_t drow = (uint32_t)kt * 64u * (uint32_t)(N >> 1);
         const uint32_t dblk = (uint32_t)kt * 64u * (uint32_t)(N >> 6);
@@ -215,10 +252,14 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
         for (int i = 0; i < 4; ++i) {
           creg[set][i] = __builtin_amdgcn_raw_buffer_load_b32(c_rsrc, c_voff[i] + drow, 0, 0);
           load_scale(s_voff[i] + dblk, set, i);
+          if constexpr (RES) {
+            creg2[set][i] = __builtin_amdgcn_raw_buffer_load_b32(c2_rsrc, c_voff[i] + drow, 0, 0);
+            load_scale2(s_voff[i] + dblk, set, i);
+          }
         }
       }
     };
-    constexpr int kWLoads = BF ? 4 : (MODE == MODE_FWD) ? (DQ ? 3 : 2) : (DQ ? 12 : 8);
+    constexpr int kWLoads = BF ? 4 : ((MODE == MODE_FWD) ? (DQ ? 3 : 2) : (DQ ? 12 : 8)) * (RES ? 2 : 1);
     constexpr int kWaitW = (kWLoads & 15) | ((kWLoads >> 4) << 14) | (0x7 << 4) | (0xF << 8);
     auto dequant = [&](int set, int b) {
       uint8_t* dst = bbuf(b);
@@ -245,31 +286,42 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
         }
       } else if constexpr (MODE == MODE_FWD) {
         const float sc = scale(set, 0);
+        const float sc2 = RES ? scale2(set, 0) : 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t w = creg[set][q];
-          const float2 t0 = ptab[w & 0xFFu], t1 = ptab[(w >> 8) & 0xFFu], t2 = ptab[(w >> 16) & 0xFFu],
-                       t3 = ptab[w >> 24];
+          const uint32_t w2 = RES ? creg2[set][q] : 0u;
+          uint32_t ov[4];
+#pragma unroll
+          for (int bq = 0; bq < 4; ++bq) {
+            const float2 t = ptab[(w >> (8 * bq)) & 0xFFu];
+            const float2 t2 = RES ? ptab[(w2 >> (8 * bq)) & 0xFFu] : make_float2(0.f, 0.f);
+            ov[bq] = pack_bf16x2(wval(t.x, sc, t2.x, sc2), wval(t.y, sc, t2.y, sc2));
+          }
           uint4 o;
-          o.x = pack_bf16x2(t0.x * sc, t0.y * sc);
-          o.y = pack_bf16x2(t1.x * sc, t1.y * sc);
-          o.z = pack_bf16x2(t2.x * sc, t2.y * sc);
-          o.w = pack_bf16x2(t3.x * sc, t3.y * sc);
+          o.x = ov[0];
+          o.y = ov[1];
+          o.z = ov[2];
+          o.w = ov[3];
           *(uint4*)(dst + lds_off(ptid >> 1, (ptid & 1) * 4 + q)) = o;
         }
       } else {
         const int og = ptid >> 4;
         const int hc = ptid & 15;
-        float sc[4];
+        float sc[4], sc2[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[i] = scale(set, i);
+        for (int i = 0; i < 4; ++i) {
+          sc[i] = scale(set, i);
+          sc2[i] = RES ? scale2(set, i) : 0.f;
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float2 v[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float2 t = ptab[(creg[set][i] >> (8 * q)) & 0xFFu];
-            v[i] = make_float2(t.x * sc[i], t.y * sc[i]);
+            const float2 t2 = RES ? ptab[(creg2[set][i] >> (8 * q)) & 0xFFu] : make_float2(0.f, 0.f);
+            v[i] = make_float2(wval(t.x, sc[i], t2.x, sc2[i]), wval(t.y, sc[i], t2.y, sc2[i]));
           }
           const int row0 = hc * 8 + 2 * q;
           uint2 e0, e1;
@@ -455,8 +507,9 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
 }
 
 hipError_t launch_nf4_gemm(int mode, int src, const uint16_t* A, const uint16_t* Wb, const uint8_t* codes,
-                           const void* absmax, const float* dqs, const uint16_t* A2, const uint16_t* B2, int R,
-                           uint16_t* C, int64_t M, int N, int K, const NF4Consts& c, hipStream_t st) {
+                           const void* absmax, const float* dqs, const uint8_t* codes2, const void* absmax2,
+                           const float* dqs2, const uint16_t* A2, const uint16_t* B2, int R, uint16_t* C, int64_t M,
+                           int N, int K, const NF4Consts& c, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   GemmArgs p;
   p.A = A;
@@ -464,6 +517,9 @@ hipError_t launch_nf4_gemm(int mode, int src, const uint16_t* A, const uint16_t*
   p.codes = codes;
   p.absmax = absmax;
   p.dqs = dqs;
+  p.codes2 = codes2;
+  p.absmax2 = absmax2;
+  p.dqs2 = dqs2;
   p.A2 = A2;
   p.B2 = B2;
   p.C = C;
@@ -476,16 +532,18 @@ hipError_t launch_nf4_gemm(int mode, int src, const uint16_t* A, const uint16_t*
   p.tiles_n = (N + GBN - 1) / GBN;
   const int64_t nwg = tiles_m * p.tiles_n;
   const dim3 gr((unsigned)nwg), bl(GNT);
-#define NF4K_GEMM(MD, SR) hipLaunchKernelGGL((k_nf4_gemm<MD, SR>), gr, bl, 0, st, p, c)
+  const bool res = codes2 != nullptr && src != kSrcBF16;
+#define NF4K_GEMM(MD, SR, RS) hipLaunchKernelGGL((k_nf4_gemm<MD, SR, RS>), gr, bl, 0, st, p, c)
+#define NF4K_GEMM_SRC(MD)                                                                      \
+  if (src == kSrcBF16) NF4K_GEMM(MD, kSrcBF16, false);                                         \
+  else if (src == kSrcNF4DQ) { if (res) NF4K_GEMM(MD, kSrcNF4DQ, true); else NF4K_GEMM(MD, kSrcNF4DQ, false); } \
+  else { if (res) NF4K_GEMM(MD, kSrcNF4, true); else NF4K_GEMM(MD, kSrcNF4, false); }
   if (mode == MODE_FWD) {
-    if (src == kSrcNF4DQ) NF4K_GEMM(MODE_FWD, kSrcNF4DQ);
-    else if (src == kSrcNF4) NF4K_GEMM(MODE_FWD, kSrcNF4);
-    else NF4K_GEMM(MODE_FWD, kSrcBF16);
+    NF4K_GEMM_SRC(MODE_FWD)
   } else {
-    if (src == kSrcNF4DQ) NF4K_GEMM(MODE_DX, kSrcNF4DQ);
-    else if (src == kSrcNF4) NF4K_GEMM(MODE_DX, kSrcNF4);
-    else NF4K_GEMM(MODE_DX, kSrcBF16);
+    NF4K_GEMM_SRC(MODE_DX)
   }
+#undef NF4K_GEMM_SRC
 #undef NF4K_GEMM
   return hipGetLastError();
 }

@@ -10,10 +10,13 @@ namespace nf4k {
 
 enum { MODE_FWD = 0, MODE_DX = 1 };
 
+// codes2/absmax2/dqs2: the residual (second-stage) tensor, or NULL for one stage.
 hipError_t launch_quantize(const float* W, int64_t nblocks, bool dq, uint8_t* codes, void* absmax, float* dqs,
-                           const NF4Enc& c, hipStream_t st);
-hipError_t launch_dequantize(const uint8_t* codes, const void* absmax, const float* dqs, int64_t nweights, bool dq,
-                             bool bf16, void* out, const NF4Consts& c, hipStream_t st);
+                           uint8_t* codes2, void* absmax2, float* dqs2, const NF4Enc& e, const NF4Consts& c,
+                           hipStream_t st);
+hipError_t launch_dequantize(const uint8_t* codes, const void* absmax, const float* dqs, const uint8_t* codes2,
+                             const void* absmax2, const float* dqs2, int64_t nweights, bool dq, bool bf16, void* out,
+                             const NF4Consts& c, hipStream_t st);
 hipError_t launch_error(const float* W, int64_t nblocks, bool dq, double* part, double* err, const NF4Enc& c,
                         hipStream_t st);
 hipError_t launch_topk(const double* e, int n, int k, int* idx, hipStream_t st);
@@ -22,13 +25,15 @@ hipError_t launch_topk(const double* e, int n, int k, int* idx, hipStream_t st);
 // double-quantized scales, or a bf16 weight (no quantization).
 enum { kSrcNF4 = 0, kSrcNF4DQ = 1, kSrcBF16 = 2 };
 hipError_t launch_nf4_gemm(int mode, int src, const uint16_t* A, const uint16_t* Wb, const uint8_t* codes,
-                           const void* absmax, const float* dqs, const uint16_t* A2, const uint16_t* B2, int R,
-                           uint16_t* C, int64_t M, int N, int K, const NF4Consts& c, hipStream_t st);
+                           const void* absmax, const float* dqs, const uint8_t* codes2, const void* absmax2,
+                           const float* dqs2, const uint16_t* A2, const uint16_t* B2, int R, uint16_t* C, int64_t M,
+                           int N, int K, const NF4Consts& c, hipStream_t st);
 
 // W' = base + s (L1 L2)^T into fp32 or bf16; base 0: fp32 W, 1: NF4, 2: NF4 with 8-bit scales.
 hipError_t launch_merge(int base, const float* W, const uint8_t* codes, const void* absmax, const float* dqs,
-                        const uint16_t* L1, const uint16_t* L2, int r, float s, int64_t rows, int64_t cols,
-                        bool out_bf16, void* out, const NF4Consts& c, hipStream_t st);
+                        const uint8_t* codes2, const void* absmax2, const float* dqs2, const uint16_t* L1,
+                        const uint16_t* L2, int r, float s, int64_t rows, int64_t cols, bool out_bf16, void* out,
+                        const NF4Consts& c, hipStream_t st);
 
 // One launch of k_prep: up to kPrepPads layout copies and kPrepZeros clears.
 // Unused jobs have orows * ocols == 0 / n == 0.

@@ -29,9 +29,12 @@ constexpr int MG_ROWS = 16;   // rows per workgroup
 constexpr int MG_RC = 64;     // adapter columns per LDS chunk
 constexpr int MG_LDT = MG_COLS + 8;
 
-template <int BASE, bool OUT_BF16>  // BASE: 0 fp32 W, 1 NF4 (fp32 absmax), 2 NF4 (8-bit scales)
+// BASE: 0 fp32 W, 1 NF4 (fp32 absmax), 2 NF4 (8-bit scales); RES: NF4 base with a residual stage
+template <int BASE, bool OUT_BF16, bool RES>
 __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ W, const uint8_t* __restrict__ codes,
                                                const void* __restrict__ absmax, const float* __restrict__ dqs,
+                                               const uint8_t* __restrict__ codes2, const void* __restrict__ absmax2,
+                                               const float* __restrict__ dqs2,
                                                const uint16_t* __restrict__ L1, const uint16_t* __restrict__ L2,
                                                int r, float s, int64_t rows, int64_t cols, void* __restrict__ out,
                                                NF4Consts cst) {
@@ -103,13 +106,22 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ W, cons
       base[0] = u.x; base[1] = u.y; base[2] = u.z; base[3] = u.w;
       base[4] = v.x; base[5] = v.y; base[6] = v.z; base[7] = v.w;
     } else {
-      const uint32_t c = *(const uint32_t*)(codes + idx / 2);
       const int64_t blk = idx / 64;
-      float sc;
-      if constexpr (BASE == 2) sc = (float)((const uint8_t*)absmax)[blk] * dqs[blk / 256];
-      else sc = ((const float*)absmax)[blk];
+      auto scale = [&](const void* am, const float* dq) -> float {
+        if constexpr (BASE == 2) return (float)((const uint8_t*)am)[blk] * dq[blk / 256];
+        else return ((const float*)am)[blk];
+      };
+      const uint32_t c = *(const uint32_t*)(codes + idx / 2);
+      const float sc = scale(absmax, dqs);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) base[e] = tab[(c >> (4 * e)) & 15u] * sc;
+      for (int e = 0; e < 8; ++e) base[e] = __fmul_rn(tab[(c >> (4 * e)) & 15u], sc);
+      if constexpr (RES) {
+        // two-stage weight: fl32(w_hat1 + w_hat2), exactly as nf4_dequantize forms it
+        const uint32_t c2 = *(const uint32_t*)(codes2 + idx / 2);
+        const float sc2 = scale(absmax2, dqs2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) base[e] = __fadd_rn(base[e], __fmul_rn(tab[(c2 >> (4 * e)) & 15u], sc2));
+      }
     }
     float o[8];
 #pragma unroll
@@ -126,19 +138,25 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ W, cons
 }
 
 hipError_t launch_merge(int base, const float* W, const uint8_t* codes, const void* absmax, const float* dqs,
-                        const uint16_t* L1, const uint16_t* L2, int r, float s, int64_t rows, int64_t cols,
-                        bool out_bf16, void* out, const NF4Consts& c, hipStream_t st) {
+                        const uint8_t* codes2, const void* absmax2, const float* dqs2, const uint16_t* L1,
+                        const uint16_t* L2, int r, float s, int64_t rows, int64_t cols, bool out_bf16, void* out,
+                        const NF4Consts& c, hipStream_t st) {
   if (rows == 0 || cols == 0) return hipSuccess;
   const dim3 gr((unsigned)((cols + MG_COLS - 1) / MG_COLS), (unsigned)((rows + MG_ROWS - 1) / MG_ROWS)), bl(256);
-#define NF4K_MERGE(B, O) \
-  hipLaunchKernelGGL((k_merge<B, O>), gr, bl, 0, st, W, codes, absmax, dqs, L1, L2, r, s, rows, cols, out, c)
+  const bool res = base != 0 && codes2 != nullptr;
+#define NF4K_MERGE(B, O, R)                                                                                        \
+  hipLaunchKernelGGL((k_merge<B, O, R>), gr, bl, 0, st, W, codes, absmax, dqs, codes2, absmax2, dqs2, L1, L2, r, s, \
+                     rows, cols, out, c)
+#define NF4K_MERGE_O(B, R) \
+  if (out_bf16) NF4K_MERGE(B, true, R); else NF4K_MERGE(B, false, R);
   if (base == 0) {
-    if (out_bf16) NF4K_MERGE(0, true); else NF4K_MERGE(0, false);
+    NF4K_MERGE_O(0, false)
   } else if (base == 1) {
-    if (out_bf16) NF4K_MERGE(1, true); else NF4K_MERGE(1, false);
+    if (res) { NF4K_MERGE_O(1, true) } else { NF4K_MERGE_O(1, false) }
   } else {
-    if (out_bf16) NF4K_MERGE(2, true); else NF4K_MERGE(2, false);
+    if (res) { NF4K_MERGE_O(2, true) } else { NF4K_MERGE_O(2, false) }
   }
+#undef NF4K_MERGE_O
 #undef NF4K_MERGE
   return hipGetLastError();
 }

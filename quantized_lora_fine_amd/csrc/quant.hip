@@ -112,13 +112,19 @@ __device__ __forceinline__ float group_max(float gm, int lane, int wave) {
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-template <bool DQ>
-__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, int64_t nblocks,
-                                                  uint8_t* __restrict__ codes,
-                                                  float* __restrict__ absmax,
-                                                  uint8_t* __restrict__ c8,
-                                                  float* __restrict__ dqs, NF4Enc enc) {
+// Outputs of one quantization stage (absmax: fp32 scales; c8/dqs: 8-bit scales and steps).
+struct QStage {
+  uint8_t* codes;
+  float* absmax;
+  uint8_t* c8;
+  float* dqs;
+};
+
+template <bool DQ, bool RES>
+__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, int64_t nblocks, QStage o1, QStage o2,
+                                                  NF4Enc enc, NF4Consts cst) {
   __shared__ EncEntry etab[kMaxBuckets];
+  __shared__ float tab[16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -128,71 +134,103 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
   const int64_t gb0 = g * 256;
   const uint32_t nb = (uint32_t)min((int64_t)256, nblocks - gb0);  // blocks in this group
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(W + gb0 * 64, nb * 256);
-  const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes + gb0 * 32, nb * 32);
   enc_to_lds<false>(enc, etab, tid);
+  if (RES && tid < 16) tab[tid] = cst.table[tid];
 
   floatx4 v[16];
   load_group(wr, wave, sub, l16, v);
-  __syncthreads();  // encoder table
+  __syncthreads();  // encoder tables
 
   float amax[16];
+  uint32_t packed[16];
+  // one stage over v: codes, block scales and (DQ) the group's 8-bit scales;
+  // returns the group step S (0 without double quantization)
+  auto stage = [&](const QStage& o) -> float {
+    const __amdgpu_buffer_rsrc_t cr = make_rsrc(o.codes + gb0 * 32, nb * 32);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float m = block_absmax(v[i]);
-    amax[i] = m;
-    const int lb = wave * 64 + 4 * i + sub;
-    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)encode4(v[i], block_enc(m), enc.bscale, enc.boffset, etab), cr, lb * 32 + l16 * 2, 0, kNT);
-  }
-  // lane l16 of row `sub` owns the block of round l16: lb = wave*64 + 4*l16 + sub
-  float mine = amax[0];
+    for (int i = 0; i < 16; ++i) {
+      const float m = block_absmax(v[i]);
+      amax[i] = m;
+      packed[i] = encode4(v[i], block_enc(m), enc.bscale, enc.boffset, etab);
+      const int lb = wave * 64 + 4 * i + sub;
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)packed[i], cr, lb * 32 + l16 * 2, 0, kNT);
+    }
+    // lane l16 of row `sub` owns the block of round l16: lb = wave*64 + 4*l16 + sub
+    float mine = amax[0];
 #pragma unroll
-  for (int i = 1; i < 16; ++i) mine = (l16 == i) ? amax[i] : mine;
-  const int mylb = wave * 64 + 4 * l16 + sub;
-
-  if constexpr (!DQ) {
-    const __amdgpu_buffer_rsrc_t ar = make_rsrc(absmax + gb0, nb * 4);
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, mine), ar, mylb * 4, 0, 0);
-  } else {
-    // group max of 256 absmax values: the 16 rows of this lane's round, then lanes, then waves
-    float gm = mine;
-    gm = fmaxf(gm, __shfl_xor(gm, 1));
-    gm = fmaxf(gm, __shfl_xor(gm, 2));
-    gm = fmaxf(gm, __shfl_xor(gm, 4));
-    gm = fmaxf(gm, __shfl_xor(gm, 8));
-    gm = group_max(gm, lane, wave);
-    const float S = gm / 255.0f;
-    if (tid == 0) dqs[g] = S;
-    const uint32_t q = (S > 0.f) ? (uint32_t)fminf(255.f, rintf(mine / S)) : 0u;
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(c8 + gb0, nb);
-    __builtin_amdgcn_raw_buffer_store_b8((unsigned char)q, qr, mylb, 0, 0);
+    for (int i = 1; i < 16; ++i) mine = (l16 == i) ? amax[i] : mine;
+    const int mylb = wave * 64 + 4 * l16 + sub;
+    if constexpr (!DQ) {
+      const __amdgpu_buffer_rsrc_t ar = make_rsrc(o.absmax + gb0, nb * 4);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, mine), ar, mylb * 4, 0, 0);
+      return 0.f;
+    } else {
+      // group max of 256 absmax values: the 16 rows of this lane's round, then lanes, then waves
+      float gm = mine;
+      gm = fmaxf(gm, __shfl_xor(gm, 1));
+      gm = fmaxf(gm, __shfl_xor(gm, 2));
+      gm = fmaxf(gm, __shfl_xor(gm, 4));
+      gm = fmaxf(gm, __shfl_xor(gm, 8));
+      gm = group_max(gm, lane, wave);
+      const float S = gm / 255.0f;
+      if (tid == 0) o.dqs[g] = S;
+      const uint32_t q = (S > 0.f) ? (uint32_t)fminf(255.f, rintf(mine / S)) : 0u;
+      const __amdgpu_buffer_rsrc_t qr = make_rsrc(o.c8 + gb0, nb);
+      __builtin_amdgcn_raw_buffer_store_b8((unsigned char)q, qr, mylb, 0, 0);
+      return S;
+    }
+  };
+  const float S1 = stage(o1);
+  if constexpr (RES) {
+    // residual of the first stage, in place: r = fl32(w - fl32(table[c] * a_hat))
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float sc = amax[i];
+      if constexpr (DQ) sc = (S1 > 0.f) ? fminf(255.f, rintf(amax[i] / S1)) * S1 : 0.f;
+      v[i].x = v[i].x - tab[packed[i] & 15u] * sc;
+      v[i].y = v[i].y - tab[(packed[i] >> 4) & 15u] * sc;
+      v[i].z = v[i].z - tab[(packed[i] >> 8) & 15u] * sc;
+      v[i].w = v[i].w - tab[(packed[i] >> 12) & 15u] * sc;
+    }
+    __syncthreads();  // the first stage's group-max slots are read before the second stage reuses them
+    stage(o2);
   }
 }
 
 // ---------------------------------------------------------------------------
 // dequantize: each thread expands one code dword (8 weights of one block)
 // ---------------------------------------------------------------------------
-template <bool DQ, bool BF16>
+template <bool DQ, bool BF16, bool RES>
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes,
                                                     const void* __restrict__ absmax,
                                                     const float* __restrict__ dqs,
+                                                    const uint8_t* __restrict__ codes2,
+                                                    const void* __restrict__ absmax2,
+                                                    const float* __restrict__ dqs2,
                                                     int64_t nwords, void* __restrict__ out,
                                                     NF4Consts cst) {
   __shared__ float tab[16];
   if (threadIdx.x < 16) tab[threadIdx.x] = cst.table[threadIdx.x];
   __syncthreads();
+  auto scale = [&](const void* am, const float* dq, int64_t blk) -> float {
+    if constexpr (DQ) return (float)((const uint8_t*)am)[blk] * dq[blk >> 8];
+    else return ((const float*)am)[blk];
+  };
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nwords; t += stride) {
     const uint32_t w = __builtin_nontemporal_load((const uint32_t*)codes + t);
     const int64_t blk = t >> 3;
-    float sc;
-    if constexpr (DQ) {
-      sc = (float)((const uint8_t*)absmax)[blk] * dqs[blk >> 8];
-    } else {
-      sc = ((const float*)absmax)[blk];
-    }
+    const float sc = scale(absmax, dqs, blk);
     float f[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) f[e] = tab[(w >> (4 * e)) & 15u] * sc;
+    if constexpr (RES) {
+      // second stage: w_hat = fl32(w_hat1 + w_hat2)
+      const uint32_t w2 = __builtin_nontemporal_load((const uint32_t*)codes2 + t);
+      const float sc2 = scale(absmax2, dqs2, blk);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = f[e] + tab[(w2 >> (4 * e)) & 15u] * sc2;
+    }
     if constexpr (BF16) {
       const u32x4 o = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
                        pack_bf16x2(f[6], f[7])};
@@ -340,31 +378,48 @@ __global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ e, int
 // ---------------------------------------------------------------------------
 // host-side launchers (called from the C ABI layer)
 // ---------------------------------------------------------------------------
-hipError_t launch_quantize(const float* W, int64_t nblocks, bool dq, uint8_t* codes, void* absmax,
-                           float* dqs, const NF4Enc& c, hipStream_t st) {
+hipError_t launch_quantize(const float* W, int64_t nblocks, bool dq, uint8_t* codes, void* absmax, float* dqs,
+                           uint8_t* codes2, void* absmax2, float* dqs2, const NF4Enc& e, const NF4Consts& c,
+                           hipStream_t st) {
   const int64_t ng = (nblocks + 255) / 256;
   if (ng == 0) return hipSuccess;
-  if (dq) {
-    hipLaunchKernelGGL(k_quantize<true>, dim3((unsigned)ng), dim3(256), 0, st, W, nblocks, codes,
-                       nullptr, (uint8_t*)absmax, dqs, c);
+  QStage o1{codes, dq ? nullptr : (float*)absmax, dq ? (uint8_t*)absmax : nullptr, dqs};
+  QStage o2{codes2, dq ? nullptr : (float*)absmax2, dq ? (uint8_t*)absmax2 : nullptr, dqs2};
+  const dim3 gr((unsigned)ng), bl(256);
+  if (codes2) {
+    if (dq) hipLaunchKernelGGL((k_quantize<true, true>), gr, bl, 0, st, W, nblocks, o1, o2, e, c);
+    else hipLaunchKernelGGL((k_quantize<false, true>), gr, bl, 0, st, W, nblocks, o1, o2, e, c);
   } else {
-    hipLaunchKernelGGL(k_quantize<false>, dim3((unsigned)ng), dim3(256), 0, st, W, nblocks, codes,
-                       (float*)absmax, nullptr, nullptr, c);
+    if (dq) hipLaunchKernelGGL((k_quantize<true, false>), gr, bl, 0, st, W, nblocks, o1, o2, e, c);
+    else hipLaunchKernelGGL((k_quantize<false, false>), gr, bl, 0, st, W, nblocks, o1, o2, e, c);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_dequantize(const uint8_t* codes, const void* absmax, const float* dqs, int64_t nweights,
-                             bool dq, bool bf16, void* out, const NF4Consts& c, hipStream_t st) {
+hipError_t launch_dequantize(const uint8_t* codes, const void* absmax, const float* dqs, const uint8_t* codes2,
+                             const void* absmax2, const float* dqs2, int64_t nweights, bool dq, bool bf16, void* out,
+                             const NF4Consts& c, hipStream_t st) {
   const int64_t nwords = nweights / 8;
   if (nwords == 0) return hipSuccess;
   int64_t blocks = (nwords + 255) / 256;
   if (blocks > 256 * 64) blocks = 256 * 64;
   const dim3 gr((unsigned)blocks), bl(256);
-  if (dq && bf16) hipLaunchKernelGGL((k_dequantize<true, true>), gr, bl, 0, st, codes, absmax, dqs, nwords, out, c);
-  if (dq && !bf16) hipLaunchKernelGGL((k_dequantize<true, false>), gr, bl, 0, st, codes, absmax, dqs, nwords, out, c);
-  if (!dq && bf16) hipLaunchKernelGGL((k_dequantize<false, true>), gr, bl, 0, st, codes, absmax, dqs, nwords, out, c);
-  if (!dq && !bf16) hipLaunchKernelGGL((k_dequantize<false, false>), gr, bl, 0, st, codes, absmax, dqs, nwords, out, c);
+#define NF4K_DEQ(D, B, R)                                                                                         \
+  hipLaunchKernelGGL((k_dequantize<D, B, R>), gr, bl, 0, st, codes, absmax, dqs, codes2, absmax2, dqs2, nwords, \
+                     out, c)
+  const bool res = codes2 != nullptr;
+  if (res) {
+    if (dq && bf16) NF4K_DEQ(true, true, true);
+    else if (dq) NF4K_DEQ(true, false, true);
+    else if (bf16) NF4K_DEQ(false, true, true);
+    else NF4K_DEQ(false, false, true);
+  } else {
+    if (dq && bf16) NF4K_DEQ(true, true, false);
+    else if (dq) NF4K_DEQ(true, false, false);
+    else if (bf16) NF4K_DEQ(false, true, false);
+    else NF4K_DEQ(false, false, false);
+  }
+#undef NF4K_DEQ
   return hipGetLastError();
 }
 

@@ -35,7 +35,7 @@ def test_exports_match_header():
 
 
 def test_abi_version_and_status_strings():
-    assert nf4.abi_version() == 2
+    assert nf4.abi_version() == 3
     for s in range(8):
         assert nf4.status_str(s)
     assert "unknown" in nf4.status_str(99)
@@ -258,3 +258,25 @@ def test_codebook_values_match_oracle():
     d.codebook = 5
     assert st_quant(d) == nf4.NF4_ERR_ARG
 
+
+
+def test_residual_validation():
+    d = desc(rows=128, cols=128)
+    r = desc(rows=128, cols=128, codes=E, absmax=F)
+    d.residual = ctypes.pointer(r)
+    bad = desc(rows=64, cols=128, codes=E, absmax=F)
+    d.residual = ctypes.pointer(bad)
+    assert st_quant(d) == nf4.NF4_ERR_SHAPE                      # residual shape differs
+    other = desc(rows=128, cols=128, dq=256, codes=E, absmax=F, dqs=G)
+    d.residual = ctypes.pointer(other)
+    assert st_quant(d) == nf4.NF4_ERR_SHAPE                      # residual double quant differs
+    nested = desc(rows=128, cols=128, codes=E, absmax=F)
+    nested.residual = ctypes.pointer(desc(rows=128, cols=128, codes=G, absmax=H))
+    d.residual = ctypes.pointer(nested)
+    assert st_quant(d) == nf4.NF4_ERR_ARG                        # no residual of a residual
+    alias = desc(rows=128, cols=128, codes=A + 64, absmax=F)
+    d.residual = ctypes.pointer(alias)
+    assert st_quant(d) == nf4.NF4_ERR_ALIAS                      # residual codes inside the first codes
+    noptr = desc(rows=128, cols=128, codes=None, absmax=F)
+    d.residual = ctypes.pointer(noptr)
+    assert st_quant(d) == nf4.NF4_ERR_NULL

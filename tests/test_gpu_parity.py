@@ -452,3 +452,50 @@ def test_codebook_layer(codebook):
         check_close("dL1", dL1, dL1r)
         check_close("dL2", dL2, dL2r)
 
+
+
+# ---------------------------------------------------------------------------
+# residual second stage through the same kernels
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dq", [0, 256])
+def test_residual_quantize(dq):
+    for W in (synth.layer_inputs(synth.C1)["W"], edge_weights()):
+        q = nf4.quantize(dev(W), dq, residual=True)
+        r1, r2 = oracle.quantize_residual(W, 64, dq)
+        check_quant(q, r1)
+        check_quant(q.residual, r2)
+        wh = nf4.dequantize(q).cpu().numpy()
+        assert np.array_equal(wh.view(np.uint32), oracle.dequantize_residual(r1, r2).view(np.uint32))
+        whb = nf4.dequantize(q, bf16=True).cpu().view(torch.int16).numpy().view(np.uint16)
+        ref_b = torch.from_numpy(oracle.dequantize_residual(r1, r2)).to(torch.bfloat16)
+        assert np.array_equal(whb, ref_b.view(torch.int16).numpy().view(np.uint16))
+
+
+def test_residual_layer_and_merge():
+    for d, s, dq in ((synth.layer_inputs(synth.C1), 2.0, 0),
+                     (synth.random_case(seed=19, rows=384, cols=256, M=257, r=64), 2.0, 256)):
+        q = nf4.quantize(dev(d["W"]), dq, residual=True)
+        X, L1, L2, dY = (dev(d[k]) for k in ("X", "L1", "L2", "dY"))
+        Y, T = nf4.fwd(q, X, L1, L2, s)
+        dX, dL1, dL2 = nf4.bwd(q, X, dY, L1, L2, s, T=T)
+        torch.cuda.synchronize()
+        wh = oracle.dequantize_residual(*oracle.quantize_residual(d["W"], 64, dq))
+        Yr, _ = oracle.fwd(d["X"], wh, d["L1"], d["L2"], s)
+        dXr, dL1r, dL2r, _ = oracle.bwd(d["X"], d["dY"], wh, d["L1"], d["L2"], s)
+        check_close("Y", Y, Yr)
+        check_close("dX", dX, dXr)
+        check_close("dL1", dL1, dL1r)
+        check_close("dL2", dL2, dL2r)
+        # the residual stage tightens the base: closer to the fp32 W than one stage
+        one = oracle.dequantize(oracle.quantize(d["W"], 64, dq))
+        assert np.linalg.norm(wh - d["W"]) < 0.5 * np.linalg.norm(one - d["W"])
+        # merge on the two-stage base
+        got = nf4.merge(q, L1, L2, s).cpu().numpy().astype(np.float64)
+        ref = oracle.merge(wh, d["L1"], d["L2"], s)
+        u = 2.0 ** -24
+        terms = s * (np.abs(oracle.lora._f64(d["L1"])) @ np.abs(oracle.lora._f64(d["L2"]))).T
+        tol = (d["L1"].shape[1] + 2) * u * terms + 2 * u * np.abs(ref)
+        viol = np.abs(got - ref) - tol
+        i = np.unravel_index(np.argmax(viol), viol.shape)
+        assert viol[i] <= 0, (i, got[i], ref[i], wh[i], tol[i], terms[i])
