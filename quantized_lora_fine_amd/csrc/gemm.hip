@@ -75,6 +75,16 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 3); }
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ swz(row)) << 4); }
+// Input-grad B tile kept as W is stored, [k][n]: 64 rows of 128 bf16 (256 B, 16
+// slots of 16 B).  Slot L of row k sits at 4*((L/4) ^ (k%4)) + ((L%4) ^ (k%4)):
+// the 16 lanes of a transposing read (4 rows x 32 B) and of the producer's
+// 16-byte writes (4 rows x 4 slots) then fall on distinct banks.
+__device__ __forceinline__ int lds_off_kn(int k, int slot) {
+  const int x = k & 3;
+  return k * 256 + ((((slot >> 2) ^ x) << 2 | ((slot & 3) ^ x)) << 4);
+}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcFlags);
@@ -144,38 +154,49 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)dst, 16, a_voff[i] + kt * 128, 0, 0, 0);
       }
     };
-    // FWD: (n = ptid>>1, half = ptid&1): 32 consecutive codes (or bf16) of W row n0+n.
-    // DX : (og = ptid>>4, hc = ptid&15): W rows 4*og .. 4*og+3 of the step, columns n0+hc*8 .. +8.
+    // Each producer thread owns 32 consecutive weights of one W row per K step:
+    //   FWD: B row n = ptid/2 (W row n0+n), K columns 32*(ptid%2) .. +32 of the step;
+    //   DX : step row kr = 16*pw + lane/4 (W row 64*kt + kr), columns n0 + 32*(lane%4) .. +32.
+    // Either way that is one 16-byte load of codes (64 bytes of bf16) and one block
+    // scale, dequantized into four 16-byte chunks of the B tile.
+    const int kr = pw * 16 + (lane >> 2);
+    const int cq = lane & 3;
     __amdgpu_buffer_rsrc_t c_rsrc;
-    uint32_t c_voff[4], s_voff[4];
-    if constexpr (BF && MODE == MODE_FWD) {
+    uint32_t c_voff, s_voff = 0, c_step, s_step = 0;
+    if constexpr (MODE == MODE_FWD) {
       const int n = ptid >> 1;
       const int nrows = (N - n0) < GBN ? (N - n0) : GBN;
-      c_rsrc = make_rsrc(p.Wb + (int64_t)n0 * K, (uint32_t)((int64_t)nrows * K * 2));
-      c_voff[0] = (uint32_t)(n * K * 2 + (ptid & 1) * 64);
-    } else if constexpr (BF) {
-      const int og = ptid >> 4;
-      const int hc = ptid & 15;
-      const bool ok = n0 + hc * 8 < N;
-      c_rsrc = make_rsrc(p.Wb, (uint32_t)((int64_t)K * N * 2));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) c_voff[i] = ok ? (uint32_t)(((og * 4 + i) * N + n0 + hc * 8) * 2) : kOOB;
-    } else if constexpr (MODE == MODE_FWD) {
-      const int n = ptid >> 1;
-      const int nrows = (N - n0) < GBN ? (N - n0) : GBN;
-      c_rsrc = make_rsrc(p.codes + (int64_t)n0 * (K >> 1), (uint32_t)((int64_t)nrows * (K >> 1)));
-      c_voff[0] = (uint32_t)(n * (K >> 1) + (ptid & 1) * 16);
-      s_voff[0] = (uint32_t)(n0 + n) * (uint32_t)(K >> 6);
-    } else {
-      const int og = ptid >> 4;
-      const int hc = ptid & 15;
-      const bool ok = n0 + hc * 8 < N;
-      c_rsrc = make_rsrc(p.codes, (uint32_t)(p.nblocks * 32));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c_voff[i] = ok ? (uint32_t)((og * 4 + i) * (N >> 1) + ((n0 + hc * 8) >> 1)) : kOOB;
-        s_voff[i] = ok ? (uint32_t)((og * 4 + i) * (N >> 6) + ((n0 + hc * 8) >> 6)) : kOOB;
+      if constexpr (BF) {
+        c_rsrc = make_rsrc(p.Wb + (int64_t)n0 * K, (uint32_t)((int64_t)nrows * K * 2));
+        c_voff = (uint32_t)(n * K * 2 + (ptid & 1) * 64);
+        c_step = 128;
+      } else {
+        c_rsrc = make_rsrc(p.codes + (int64_t)n0 * (K >> 1), (uint32_t)((int64_t)nrows * (K >> 1)));
+        c_voff = (uint32_t)(n * (K >> 1) + (ptid & 1) * 16);
+        c_step = 32;
+        s_voff = (uint32_t)(n0 + n) * (uint32_t)(K >> 6);
+        s_step = 1;
       }
+    } else {
+      const bool ok = n0 + cq * 32 < N;  // N is a multiple of 64: a chunk is all in or all out
+      if constexpr (BF) {
+        c_rsrc = make_rsrc(p.Wb, (uint32_t)((int64_t)K * N * 2));
+        c_voff = ok ? (uint32_t)((kr * N + n0 + cq * 32) * 2) : kOOB;
+        c_step = 128u * (uint32_t)N;
+      } else {
+        c_rsrc = make_rsrc(p.codes, (uint32_t)(p.nblocks * 32));
+        c_voff = ok ? (uint32_t)(kr * (N >> 1) + ((n0 + cq * 32) >> 1)) : kOOB;
+        c_step = 32u * (uint32_t)N;
+        s_voff = ok ? (uint32_t)(kr * (N >> 6) + ((n0 + cq * 32) >> 6)) : kOOB;
+        s_step = (uint32_t)N;
+      }
+    }
+    // LDS byte offsets of the thread's four 16-byte chunks in a B buffer
+    uint32_t w_off[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (MODE == MODE_FWD) w_off[q] = (uint32_t)lds_off(ptid >> 1, (ptid & 1) * 4 + q);
+      else w_off[q] = (uint32_t)lds_off_kn(kr, cq * 4 + q);
     }
     const __amdgpu_buffer_rsrc_t s_rsrc = make_rsrc(p.absmax, (uint32_t)(p.nblocks * (DQ ? 1 : 4)));
     const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(p.dqs, (uint32_t)(DQ ? ((p.nblocks + 255) / 256) * 4 : 0));
@@ -193,19 +214,31 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
     }
 
     u32x4 creg[2], creg2[2];
-    uint32_t sraw[2][4], sraw2[2][4];
-    float sstep[2][4], sstep2[2][4];
-    auto load_scale2 = [&](uint32_t blk, int set, int i) {
+    uint32_t sraw[2], sraw2[2];
+    float sstep[2], sstep2[2];
+    auto load_scale = [&](uint32_t blk, int set) {
       if constexpr (DQ) {
-        sraw2[set][i] = __builtin_amdgcn_raw_buffer_load_b8(s2_rsrc, blk, 0, 0);
-        sstep2[set][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(q2_rsrc, (blk >> 8) * 4, 0, 0));
+        sraw[set] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, blk, 0, 0);
+        sstep[set] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(q_rsrc, (blk >> 8) * 4, 0, 0));
       } else {
-        sraw2[set][i] = __builtin_amdgcn_raw_buffer_load_b32(s2_rsrc, blk * 4, 0, 0);
+        sraw[set] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, blk * 4, 0, 0);
       }
     };
-    auto scale2 = [&](int set, int i) -> float {
-      if constexpr (DQ) return (float)sraw2[set][i] * sstep2[set][i];
-      else return __builtin_bit_cast(float, sraw2[set][i]);
+    auto load_scale2 = [&](uint32_t blk, int set) {
+      if constexpr (DQ) {
+        sraw2[set] = __builtin_amdgcn_raw_buffer_load_b8(s2_rsrc, blk, 0, 0);
+        sstep2[set] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(q2_rsrc, (blk >> 8) * 4, 0, 0));
+      } else {
+        sraw2[set] = __builtin_amdgcn_raw_buffer_load_b32(s2_rsrc, blk * 4, 0, 0);
+      }
+    };
+    auto scale = [&](int set) -> float {
+      if constexpr (DQ) return (float)sraw[set] * sstep[set];
+      else return __builtin_bit_cast(float, sraw[set]);
+    };
+    auto scale2 = [&](int set) -> float {
+      if constexpr (DQ) return (float)sraw2[set] * sstep2[set];
+      else return __builtin_bit_cast(float, sraw2[set]);
     };
     // dequantized weight of one code: fl32(t * sc), or with the residual stage
     // fl32(fl32(t * sc) + fl32(t2 * sc2)) (no fused multiply-add)
@@ -213,124 +246,50 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
       if constexpr (RES) return __fadd_rn(__fmul_rn(t, sc), __fmul_rn(t2, sc2));
       else return t * sc;
     };
-    auto load_scale = [&](uint32_t blk, int set, int i) {
-      if constexpr (DQ) {
-        sraw[set][i] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, blk, 0, 0);
-        sstep[set][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(q_rsrc, (blk >> 8) * 4, 0, 0));
-      } else {
-        sraw[set][i] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, blk * 4, 0, 0);
-      }
-    };
-    auto scale = [&](int set, int i) -> float {
-      if constexpr (DQ) {
-        return (float)sraw[set][i] * sstep[set][i];
-      } else {
-        return __builtin_bit_cast(float, sraw[set][i]);
-      }
-    };
     u32x4 wreg[2][4];  // bf16 weight chunks (SRC == kSrcBF16)
     auto issue_W = [&](int kt, int set) {
-      if constexpr (BF && MODE == MODE_FWD) {
+      const uint32_t co = c_voff + (uint32_t)kt * c_step;
+      if constexpr (BF) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          wreg[set][q] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, c_voff[0] + kt * 128 + q * 16, 0, 0);
-      } else if constexpr (BF) {
-        const uint32_t drow = (uint32_t)kt * 128u * (uint32_t)N;  // 64 rows of N bf16
-#pragma unroll
-        for (int i = 0; i < 4; ++i) wreg[set][i] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, c_voff[i] + drow, 0, 0);
-      } else if constexpr (MODE == MODE_FWD) {
-        creg[set] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, c_voff[0] + kt * 32, 0, 0);
-        load_scale(s_voff[0] + kt, set, 0);
-        if constexpr (RES) {
-          creg2[set] = __builtin_amdgcn_raw_buffer_load_b128(c2_rsrc, c_voff[0] + kt * 32, 0, 0);
-          load_scale2(s_voff[0] + kt, set, 0);
-        }
+        for (int q = 0; q < 4; ++q) wreg[set][q] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, co + q * 16, 0, 0);
       } else {
-        const uint32_t drow = (uint32_t)kt * 64u * (uint32_t)(N >> 1);
-        const uint32_t dblk = (uint32_t)kt * 64u * (uint32_t)(N >> 6);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          creg[set][i] = __builtin_amdgcn_raw_buffer_load_b32(c_rsrc, c_voff[i] + drow, 0, 0);
-          load_scale(s_voff[i] + dblk, set, i);
-          if constexpr (RES) {
-            creg2[set][i] = __builtin_amdgcn_raw_buffer_load_b32(c2_rsrc, c_voff[i] + drow, 0, 0);
-            load_scale2(s_voff[i] + dblk, set, i);
-          }
+        const uint32_t so = s_voff + (uint32_t)kt * s_step;
+        creg[set] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, co, 0, 0);
+        load_scale(so, set);
+        if constexpr (RES) {
+          creg2[set] = __builtin_amdgcn_raw_buffer_load_b128(c2_rsrc, co, 0, 0);
+          load_scale2(so, set);
         }
       }
     };
-    constexpr int kWLoads = BF ? 4 : ((MODE == MODE_FWD) ? (DQ ? 3 : 2) : (DQ ? 12 : 8)) * (RES ? 2 : 1);
+    constexpr int kWLoads = BF ? 4 : (DQ ? 3 : 2) * (RES ? 2 : 1);
     constexpr int kWaitW = (kWLoads & 15) | ((kWLoads >> 4) << 14) | (0x7 << 4) | (0xF << 8);
     auto dequant = [&](int set, int b) {
       uint8_t* dst = bbuf(b);
-      if constexpr (BF && MODE == MODE_FWD) {
+      if constexpr (BF) {
         // bf16 source: the 4 chunks go to the tile as they are
 #pragma unroll
-        for (int q = 0; q < 4; ++q) *(u32x4*)(dst + lds_off(ptid >> 1, (ptid & 1) * 4 + q)) = wreg[set][q];
-      } else if constexpr (BF) {
-        // bf16 source, transposed: dword q of row i holds columns 2q (low half) and 2q+1 (high half);
-        // B row n gets the 4 rows' values of column n as one 8-byte chunk
-        const int og = ptid >> 4;
-        const int hc = ptid & 15;
+        for (int q = 0; q < 4; ++q) *(u32x4*)(dst + w_off[q]) = wreg[set][q];
+      } else {
+        // all table reads first: one LDS round trip per step, not one per 16-byte chunk
+        float2 t[4][4], t2[4][4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t a0 = wreg[set][0][q], a1 = wreg[set][1][q], a2 = wreg[set][2][q], a3 = wreg[set][3][q];
-          const int row0 = hc * 8 + 2 * q;
-          uint2 e0, e1;
-          e0.x = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-          e0.y = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-          e1.x = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-          e1.y = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-          *(uint2*)(dst + row0 * 128 + (((og >> 1) ^ swz(row0)) << 4) + (og & 1) * 8) = e0;
-          *(uint2*)(dst + (row0 + 1) * 128 + (((og >> 1) ^ swz(row0 + 1)) << 4) + (og & 1) * 8) = e1;
-        }
-      } else if constexpr (MODE == MODE_FWD) {
-        const float sc = scale(set, 0);
-        const float sc2 = RES ? scale2(set, 0) : 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t w = creg[set][q];
-          const uint32_t w2 = RES ? creg2[set][q] : 0u;
-          uint32_t ov[4];
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int bq = 0; bq < 4; ++bq) {
-            const float2 t = ptab[(w >> (8 * bq)) & 0xFFu];
-            const float2 t2 = RES ? ptab[(w2 >> (8 * bq)) & 0xFFu] : make_float2(0.f, 0.f);
-            ov[bq] = pack_bf16x2(wval(t.x, sc, t2.x, sc2), wval(t.y, sc, t2.y, sc2));
+            t[q][bq] = ptab[(creg[set][q] >> (8 * bq)) & 0xFFu];
+            if constexpr (RES) t2[q][bq] = ptab[(creg2[set][q] >> (8 * bq)) & 0xFFu];
+            else t2[q][bq] = make_float2(0.f, 0.f);
           }
-          uint4 o;
-          o.x = ov[0];
-          o.y = ov[1];
-          o.z = ov[2];
-          o.w = ov[3];
-          *(uint4*)(dst + lds_off(ptid >> 1, (ptid & 1) * 4 + q)) = o;
-        }
-      } else {
-        const int og = ptid >> 4;
-        const int hc = ptid & 15;
-        float sc[4], sc2[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sc[i] = scale(set, i);
-          sc2[i] = RES ? scale2(set, i) : 0.f;
-        }
+        const float sc = scale(set);
+        const float sc2 = RES ? scale2(set) : 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float2 v[4];
+          u32x4 o;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float2 t = ptab[(creg[set][i] >> (8 * q)) & 0xFFu];
-            const float2 t2 = RES ? ptab[(creg2[set][i] >> (8 * q)) & 0xFFu] : make_float2(0.f, 0.f);
-            v[i] = make_float2(wval(t.x, sc[i], t2.x, sc2[i]), wval(t.y, sc[i], t2.y, sc2[i]));
-          }
-          const int row0 = hc * 8 + 2 * q;
-          uint2 e0, e1;
-          e0.x = pack_bf16x2(v[0].x, v[1].x);
-          e0.y = pack_bf16x2(v[2].x, v[3].x);
-          e1.x = pack_bf16x2(v[0].y, v[1].y);
-          e1.y = pack_bf16x2(v[2].y, v[3].y);
-          *(uint2*)(dst + row0 * 128 + (((og >> 1) ^ swz(row0)) << 4) + (og & 1) * 8) = e0;
-          *(uint2*)(dst + (row0 + 1) * 128 + (((og >> 1) ^ swz(row0 + 1)) << 4) + (og & 1) * 8) = e1;
+          for (int bq = 0; bq < 4; ++bq)
+            o[bq] = pack_bf16x2(wval(t[q][bq].x, sc, t2[q][bq].x, sc2), wval(t[q][bq].y, sc, t2[q][bq].y, sc2));
+          *(u32x4*)(dst + w_off[q]) = o;
         }
       }
     };
@@ -373,6 +332,17 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
     struct Frags {
       bf16x8 a[4], b[2];
     };
+    // Input grad: B fragments come from the [k][n] tile through ds_read_b64_tr_b16.
+    // In each group of 16 lanes, lane 4e+q points at row k0+e, columns nb+4q..+3,
+    // and lane j receives column nb+j of rows k0..k0+3; two reads (k0 and k0+4)
+    // give the 8 consecutive k of the MFMA operand.
+    uint32_t b_off[2];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+      const int nb = wn * 64 + ni * 32 + 16 * (g & 1);
+      b_off[ni] = (uint32_t)(lds_off_kn(8 * (g >> 1) + e, (nb >> 3) + (q >> 1)) + 8 * (q & 1));
+    }
     auto load_frags = [&](int b, int kk, Frags& f) {
       const uint8_t* Ab = abuf(b);
       const uint8_t* Bb = bbuf(b);
@@ -381,8 +351,16 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
       for (int mi = 0; mi < 4; ++mi)
         f.a[mi] = *(const bf16x8*)(Ab + lds_off(wm * 128 + mi * 32 + (lane & 31), chunk));
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        f.b[ni] = *(const bf16x8*)(Bb + lds_off(wn * 64 + ni * 32 + (lane & 31), chunk));
+      for (int ni = 0; ni < 2; ++ni) {
+        if constexpr (MODE == MODE_FWD) {
+          f.b[ni] = *(const bf16x8*)(Bb + lds_off(wn * 64 + ni * 32 + (lane & 31), chunk));
+        } else {
+          uint8_t* src = const_cast<uint8_t*>(Bb) + kk * 4096 + b_off[ni];
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)src);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(src + 1024));
+          f.b[ni] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      }
     };
     auto mma = [&](const Frags& f) {
 #pragma unroll
@@ -391,13 +369,14 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
         for (int ni = 0; ni < 2; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0);
     };
+    constexpr int kReads = MODE == MODE_FWD ? 6 : 8;  // LDS reads per K16 group
     auto interleave = [&]() {
 #pragma unroll
-      for (int i = 0; i < 6; ++i) {
+      for (int i = 0; i < kReads; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one fragment read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if constexpr (kReads < 8) __builtin_amdgcn_sched_group_barrier(0x008, 8 - kReads, 0);
     };
     Frags f0, f1;
     __syncthreads();  // (1)
