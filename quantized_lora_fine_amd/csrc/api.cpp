@@ -316,7 +316,7 @@ nf4_status layer_fwd(const WSrc& W, const uint16_t* X, int64_t M, const uint16_t
   PrepArgs pa{};
   pa.pad[0] = pad_job(L1, 1, r, r, h, l1t, p.RP, h);
   pa.pad[1] = pad_job(L2, 1, o, o, r, l2t, o, p.RP);
-  pa.zero[0] = ZeroJob{cnt, p.ncnt};
+  if (!skinny_nt_whole(M, p.RP)) pa.zero[0] = ZeroJob{cnt, p.ncnt};
   NF4_TRY(launch_prep(pa, hs));
   // T = X L1 (split K, fixed-order reduction) -> T_out (bf16) and s*T (bf16, padded)
   NtArgs nt{X, l1t, M, (int)h, p.ks, p.kr, part, cnt, r, 1.0f, T_out, r, s, ts};
@@ -376,14 +376,22 @@ nf4_status layer_bwd(const WSrc& W, const uint16_t* X, const uint16_t* dY, int64
   float* p2 = (float*)(w + p.off_p2);
   float* p1 = (float*)(w + p.off_p1);
 
-  // one prep launch: L1 [h][RP], L2 [RP][o], counters, and L1^T [RP][h] when T is recomputed
-  // or T [M][RP] when the given T has rows that are not whole 16-byte chunks
+  // one prep launch: L1 [h][RP] and L2 [RP][o] with zero padding (L1 and L2 are used
+  // as they are when r is a multiple of 16), counters when a split product runs, and
+  // L1^T [RP][h] when T is recomputed or T [M][RP] when the given T has rows that are
+  // not whole 16-byte chunks
   PrepArgs pa{};
-  pa.pad[0] = pad_job(L1, r, 1, h, r, l1p, h, p.RP);
-  pa.pad[1] = pad_job(L2, o, 1, r, o, l2p, p.RP, o);
+  const uint16_t* l1b = L1;
+  const uint16_t* l2b = L2;
+  if (r != p.RP) {
+    pa.pad[0] = pad_job(L1, r, 1, h, r, l1p, h, p.RP);
+    pa.pad[1] = pad_job(L2, o, 1, r, o, l2p, p.RP, o);
+    l1b = l1p;
+    l2b = l2p;
+  }
   if (!T) pa.pad[2] = pad_job(L1, 1, r, r, h, l1t, p.RP, h);
   else if (r % 8 != 0) pa.pad[2] = pad_job(T, r, 1, M, r, tb, M, p.RP);
-  pa.zero[0] = ZeroJob{cnt, p.ncnt};
+  if (!skinny_nt_whole(M, p.RP) || !skinny_tn_whole(M, p.RP)) pa.zero[0] = ZeroJob{cnt, p.ncnt};
   NF4_TRY(launch_prep(pa, hs));
   const uint16_t* tsrc = T;
   int ldt = r;
@@ -397,7 +405,7 @@ nf4_status layer_bwd(const WSrc& W, const uint16_t* X, const uint16_t* dY, int64
     ldt = p.RP;
   }
   // G = s dY L2^T  (bf16 [M][RP], columns >= r zero)
-  NtArgs ng{dY, l2p, M, (int)o, p.ks_g, p.kr_g, pnt, cnt + p.cnt_g, r, 1.0f, nullptr, 0, s, g};
+  NtArgs ng{dY, l2b, M, (int)o, p.ks_g, p.kr_g, pnt, cnt + p.cnt_g, r, 1.0f, nullptr, 0, s, g};
   NF4_TRY(launch_skinny_nt(ng, p.RP, hs));
   // dL2 = s T^T dY  ([r][o]),  dL1 = X^T G  (stored [h][r])
   TnArgs t2{tsrc, ldt, r, dY, M, (int)o, p.ms2, p.mr2, p2, cnt + p.cnt_2, s, 0, dL2};
@@ -406,7 +414,7 @@ nf4_status layer_bwd(const WSrc& W, const uint16_t* X, const uint16_t* dY, int64
   NF4_TRY(launch_skinny_tn(t1, p.RP, hs));
   // dX = dY w_hat + G L1^T
   if (dX) {
-    NF4_TRY(gemm(MODE_DX, W, dY, g, l1p, p.RP, dX, M, hs));
+    NF4_TRY(gemm(MODE_DX, W, dY, g, l1b, p.RP, dX, M, hs));
   }
   return NF4_OK;
 }

@@ -89,5 +89,9 @@ void plan_nt(int64_t M, int K, int* ksplit, int* krange);
 void plan_tn(int64_t M, int N, int* msplit, int64_t* mrange);
 hipError_t launch_skinny_nt(const NtArgs& a, int RP, hipStream_t st);
 hipError_t launch_skinny_tn(const TnArgs& a, int RP, hipStream_t st);
+// true when the launchers above use the unsplit kernels (whole K / all tokens
+// per workgroup), which need neither the partial buffers nor the counters
+bool skinny_nt_whole(int64_t M, int RP);
+bool skinny_tn_whole(int64_t M, int RP);
 
 }  // namespace nf4k

@@ -203,6 +203,105 @@ __global__ __launch_bounds__(256) void k_skinny_nt(NtArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// NT skinny, whole K per workgroup (RP <= 64): the same product as k_skinny_nt
+// without a split: a 1024-thread workgroup owns RW rows of A (RW = 8, 16 or 32,
+// so that the B bytes it reads from L2 are at most twice its A bytes) and all
+// of K.  Its 16 waves take interleaved K steps of 32 (at each unrolled step the
+// workgroup streams 512 contiguous columns of its rows), U steps per round
+// with every load of the round in flight, so a few hundred workgroups keep
+// enough bytes in flight to stream A at HBM speed.  The 16 wave tiles are
+// added in LDS in wave order; no partials, counters or second pass.
+// With RW = 8 the MFMA A operand's rows 8..15 are zero.
+// ---------------------------------------------------------------------------
+template <int RPT>
+struct NtRows {
+  static constexpr int RW = RPT <= 16 ? 8 : (RPT <= 32 ? 16 : 32);
+  static constexpr int FRA = RW >= 16 ? RW / 16 : 1;    // A fragments of 16 rows
+  static constexpr int NJ = RPT / 16;
+  static constexpr int U = 16 / (FRA + NJ);             // K steps per wave per round
+};
+
+template <int RPT>
+__global__ __launch_bounds__(1024) void k_skinny_nt_rows(NtArgs p) {
+  using S = NtRows<RPT>;
+  constexpr int RW = S::RW, FRA = S::FRA, NJ = S::NJ, U = S::U;
+  __shared__ float red[16 * RW * RPT];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t m0 = (int64_t)blockIdx.x * RW;
+  const int64_t M = p.M;
+  const int K = p.K;
+  const int li = lane & 15;
+  const int kq = (lane >> 4) * 8;
+
+  floatx4 acc[FRA][NJ];
+#pragma unroll
+  for (int a = 0; a < FRA; ++a)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[a][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const uint16_t* arow[FRA];
+  bool aval[FRA];
+#pragma unroll
+  for (int a = 0; a < FRA; ++a) {
+    const int row = a * 16 + li;
+    const int64_t m = m0 + row;
+    aval[a] = row < RW && m < M;
+    arow[a] = p.A + (aval[a] ? m : 0) * (int64_t)K;
+  }
+  const uint16_t* brow = p.B + (int64_t)li * K + kq;
+  for (int k0 = 32 * wave; k0 < K; k0 += 512 * U) {
+    bf16x8 af[U][FRA], bf[U][NJ];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = k0 + 512 * u;
+      const bool kv = k < K;
+#pragma unroll
+      for (int a = 0; a < FRA; ++a) {
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (kv && aval[a]) v = __builtin_nontemporal_load((const u32x4*)(arow[a] + k + kq));
+        af[u][a] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (kv) v = *(const u32x4*)(brow + (int64_t)j * 16 * K + k);
+        bf[u][j] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int a = 0; a < FRA; ++a)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u][a], bf[u][j], acc[a][j], 0, 0, 0);
+  }
+  // D[i][jj]: lane holds column jj = lane%16, rows i = 4*(lane/16) + v
+#pragma unroll
+  for (int a = 0; a < FRA; ++a)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = a * 16 + 4 * (lane >> 4) + v;
+      if (row < RW) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) red[(wave * RW + row) * RPT + j * 16 + li] = acc[a][j][v];
+      }
+    }
+  __syncthreads();
+  for (int e = tid; e < RW * RPT; e += 1024) {
+    const int64_t m = m0 + e / RPT;
+    if (m >= M) continue;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) sum += red[w * RW * RPT + e];
+    const int j = e % RPT;
+    if (p.out1 && j < p.r) p.out1[m * p.ld1 + j] = f32_to_bf16(p.alpha1 * sum);
+    if (p.out2) p.out2[m * RPT + j] = f32_to_bf16(p.alpha2 * sum);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // TN skinny: out[j][n] = alpha * sum_m P[m][j] * Q[m][n]   (j < r)
 // P [M][ldp] bf16 with ldp % 8 == 0 and columns r .. ceil8(r)-1 zero (P is
 // read in 16-byte chunks of 8 columns; chunks at or past r are not read),
@@ -339,6 +438,159 @@ __global__ __launch_bounds__(256) void k_skinny_tn(TnArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// TN skinny, all tokens per workgroup (RP <= 64): the same product as
+// k_skinny_tn without a token split.  A workgroup of WAVES waves (16 for rank
+// 16, else 8 so the larger tiles fit in registers) owns NC = 64 (or 32)
+// columns of Q.  Wave w takes the 32-token chunks w, w+WAVES, ...: it copies
+// each chunk of Q ([32][NC]) and P ([32][RP]) row-major into its own LDS
+// area with 16-byte stores (DEPTH chunks ahead in registers) and builds both
+// MFMA operands with ds_read_b64_tr_b16, which hands each lane 4 consecutive
+// tokens of one column (in each group of 16 lanes, lane 4e+q addresses token
+// row e, columns c+4q..c+4q+3, and lane i receives column c+i of the 4 rows).
+// LDS rows are padded so the 4 rows of a transposing read fall on distinct
+// banks.  The wave tiles are added in LDS in wave order (rounds of four
+// slots), so the result does not depend on scheduling.
+// ---------------------------------------------------------------------------
+template <int RPT, int NC, int WAVES>
+struct TnCols {
+  static constexpr int NJ = RPT / 16, NG = NC / 16;
+  static constexpr int QROW = NC * 2 + (NC == 64 ? 16 : 32);  // LDS bytes per token row
+  static constexpr int PROW = RPT * 2 + (RPT * 2 % 64 == 32 ? 16 : (RPT * 2 % 128 == 0 ? 16 : 32));
+  static constexpr int QPR = NC / 8, QTL = 64 / QPR, QL = 32 / QTL;     // Q pieces per row, tokens per load, loads
+  static constexpr int PPR = RPT / 8, PTL = 64 / PPR, PL = (32 + PTL - 1) / PTL;
+  static constexpr int STAGE = 32 * (QROW + PROW);                       // bytes per wave
+  // chunks in flight per wave, as many as the register budget allows
+  static constexpr int DEPTH = WAVES == 16 ? (NC == 32 ? 4 : 2) : (QL + PL <= 6 ? 3 : 2);
+  static constexpr int SMEM = WAVES * STAGE > 4 * RPT * NC * 4 ? WAVES * STAGE : 4 * RPT * NC * 4;
+};
+
+typedef short s16x4_tn __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_tn* lds_s16x4_tn;
+
+__device__ __forceinline__ bf16x8 tr_frag(uint8_t* lo, int row_bytes) {
+  const s16x4_tn a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_tn)lo);
+  const s16x4_tn b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_tn)(lo + 4 * row_bytes));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int RPT, int NC, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_skinny_tn_cols(TnArgs p) {
+  using S = TnCols<RPT, NC, WAVES>;
+  constexpr int NJ = S::NJ, NG = S::NG, QROW = S::QROW, PROW = S::PROW;
+  constexpr int QPR = S::QPR, QTL = S::QTL, QL = S::QL, PPR = S::PPR, PTL = S::PTL, PL = S::PL;
+  constexpr int DEPTH = S::DEPTH;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[S::SMEM];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  // neighbouring column bands share 128-byte lines of Q: keep them on one XCD
+  // (workgroups are dealt to the 8 XCDs round-robin) so they meet in its L2
+  int bid = blockIdx.x;
+  if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+  const int n0 = bid * NC;
+  const int64_t M = p.M;
+  const int N = p.N;
+  uint8_t* qs = smem + wave * S::STAGE;
+  uint8_t* ps = qs + 32 * QROW;
+
+  // this lane's pieces of a chunk: Q token QTL*i + lane/QPR, columns 8*(lane%QPR);
+  // P token PTL*i + lane/PPR, columns 8*(lane%PPR) (read only below r)
+  const int qcol = n0 + 8 * (lane % QPR);
+  const bool qok = qcol < N;
+  const int pj = 8 * (lane % PPR);
+  const bool pok = pj < p.r;
+  u32x4 qr[DEPTH][QL], pr[DEPTH][PL];
+  const int64_t nchunk = (M + 31) / 32;
+  auto load = [&](int slot, int64_t c) {
+    const int64_t m0 = c * 32;
+#pragma unroll
+    for (int i = 0; i < QL; ++i) {
+      const int64_t m = m0 + QTL * i + lane / QPR;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (c < nchunk && m < M && qok) v = __builtin_nontemporal_load((const u32x4*)(p.Q + m * N + qcol));
+      qr[slot][i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int t = PTL * i + lane / PPR;
+      const int64_t m = m0 + t;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (c < nchunk && t < 32 && m < M && pok) v = *(const u32x4*)(p.P + m * p.ldp + pj);
+      pr[slot][i] = v;
+    }
+  };
+  auto stage = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < QL; ++i) *(u32x4*)(qs + (QTL * i + lane / QPR) * QROW + 16 * (lane % QPR)) = qr[slot][i];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int t = PTL * i + lane / PPR;
+      if (t < 32) *(u32x4*)(ps + t * PROW + 16 * (lane % PPR)) = pr[slot][i];
+    }
+  };
+  floatx4 acc[NJ][NG];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int g = 0; g < NG; ++g) acc[j][g] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // transposing-read addresses: 16-lane group g16 covers tokens 8*g16 .. +7
+  const int g16 = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+  const int trow = 8 * g16 + e;
+  auto compute = [&]() {
+    bf16x8 bq[NG], ap[NJ];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) bq[g] = tr_frag(qs + trow * QROW + 2 * (16 * g + 4 * q), QROW);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) ap[j] = tr_frag(ps + trow * PROW + 2 * (16 * j + 4 * q), PROW);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) acc[j][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[j], bq[g], acc[j][g], 0, 0, 0);
+  };
+  // chunks wave, wave+WAVES, ...: DEPTH in flight in registers while one is multiplied
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) load(d, wave + (int64_t)d * WAVES);
+  for (int64_t c = wave; c < nchunk; c += (int64_t)DEPTH * WAVES) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int64_t cc = c + (int64_t)d * WAVES;
+      if (cc < nchunk) {
+        stage(d);
+        load(d, cc + (int64_t)DEPTH * WAVES);
+        compute();
+      }
+    }
+  }
+  // D[i][jj]: lane holds column jj = lane%16 (of column group g), rows i = 4*(lane/16) + v (of j fragment)
+  __syncthreads();
+  float* slot = (float*)smem;
+#pragma unroll
+  for (int f = 0; f < WAVES / 4; ++f) {
+    if ((wave >> 2) == f) {
+      float* mine = slot + (wave & 3) * RPT * NC;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int idx = (j * 16 + 4 * (lane >> 4) + v) * NC + g * 16 + (lane & 15);
+            mine[idx] = f == 0 ? acc[j][g][v] : mine[idx] + acc[j][g][v];
+          }
+    }
+    __syncthreads();
+  }
+  for (int idx = tid; idx < RPT * NC; idx += WAVES * 64) {
+    const int j = idx / NC;
+    const int n = n0 + idx % NC;
+    if (j >= p.r || n >= N) continue;
+    const float sum = ((slot[idx] + slot[RPT * NC + idx]) + slot[2 * RPT * NC + idx]) + slot[3 * RPT * NC + idx];
+    if (p.trans) p.out[(int64_t)n * p.r + j] = p.alpha * sum;
+    else p.out[(int64_t)j * N + n] = p.alpha * sum;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_prep(const PrepArgs& a, hipStream_t st) {
@@ -404,8 +656,32 @@ void plan_tn(int64_t M, int N, int* msplit, int64_t* mrange) {
     default: return hipErrorInvalidValue; \
   }
 
+// whole-K workgroups when the rank is small and there are rows enough for them
+bool skinny_nt_whole(int64_t M, int RP) {
+  if (RP > 64) return false;
+  const int rw = RP <= 16 ? 8 : (RP <= 32 ? 16 : 32);
+  return (M + rw - 1) / rw >= 64;
+}
+
+// all tokens per workgroup when the rank is small and the token count is not tiny
+bool skinny_tn_whole(int64_t M, int RP) { return RP <= 64 && M >= 512; }
+
 hipError_t launch_skinny_nt(const NtArgs& a, int RP, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
+  {
+    if (skinny_nt_whole(a.M, RP)) {
+      const int rw = RP <= 16 ? 8 : (RP <= 32 ? 16 : 32);
+      const int64_t nwg = (a.M + rw - 1) / rw;
+      const dim3 gr((unsigned)nwg), bl(1024);
+      switch (RP) {
+        case 16: hipLaunchKernelGGL(k_skinny_nt_rows<16>, gr, bl, 0, st, a); break;
+        case 32: hipLaunchKernelGGL(k_skinny_nt_rows<32>, gr, bl, 0, st, a); break;
+        case 48: hipLaunchKernelGGL(k_skinny_nt_rows<48>, gr, bl, 0, st, a); break;
+        default: hipLaunchKernelGGL(k_skinny_nt_rows<64>, gr, bl, 0, st, a); break;
+      }
+      return hipGetLastError();
+    }
+  }
   const int64_t mblocks = (a.M + 63) / 64;
   const dim3 gr((unsigned)(mblocks * a.ksplit)), bl(256);
 #define L_NT(R) hipLaunchKernelGGL(k_skinny_nt<R>, gr, bl, 0, st, a)
@@ -416,6 +692,24 @@ hipError_t launch_skinny_nt(const NtArgs& a, int RP, hipStream_t st) {
 
 hipError_t launch_skinny_tn(const TnArgs& a, int RP, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
+  // all tokens per workgroup when the rank is small: 64 columns each, or 32
+  // when that leaves too few workgroups to stream Q
+  if (skinny_tn_whole(a.M, RP)) {
+    const bool wide = (a.N + 63) / 64 >= 128;
+    const int nc = wide ? 64 : 32;
+    const dim3 gr((unsigned)((a.N + nc - 1) / nc)), bl(RP == 16 ? 1024 : 512);
+#define L_TNC(R)                                                                                 \
+  if (wide) hipLaunchKernelGGL((k_skinny_tn_cols<R, 64, R == 16 ? 16 : 8>), gr, bl, 0, st, a); \
+  else hipLaunchKernelGGL((k_skinny_tn_cols<R, 32, R == 16 ? 16 : 8>), gr, bl, 0, st, a);
+    switch (RP) {
+      case 16: L_TNC(16) break;
+      case 32: L_TNC(32) break;
+      case 48: L_TNC(48) break;
+      default: L_TNC(64) break;
+    }
+#undef L_TNC
+    return hipGetLastError();
+  }
   const int nblocks = (a.N + 63) / 64;
   const dim3 gr((unsigned)(nblocks * a.msplit)), bl(256);
 #define L_TN(R) hipLaunchKernelGGL(k_skinny_tn<R>, gr, bl, 0, st, a)
