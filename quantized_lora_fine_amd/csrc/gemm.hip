@@ -95,17 +95,20 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
   constexpr bool DQ = SRC == kSrcNF4DQ;
   constexpr bool BF = SRC == kSrcBF16;
   // three buffers each for A and the dequantized B: tile t lives in buffer t%3
+  // the codebook pair table is placed first in LDS (its alignment sorts it
+  // ahead of the tiles), so its reads carry the address in the 16-bit offset
+  // field instead of adding a base register per lookup
+  __shared__ __attribute__((aligned(1024))) float2 ptab[256];
   __shared__ __attribute__((aligned(16))) uint8_t As0[GBM * 128];
   __shared__ __attribute__((aligned(16))) uint8_t As1[GBM * 128];
   __shared__ __attribute__((aligned(16))) uint8_t As2[GBM * 128];
   __shared__ __attribute__((aligned(16))) uint8_t Bs0[GBN * 128];
   __shared__ __attribute__((aligned(16))) uint8_t Bs1[GBN * 128];
   __shared__ __attribute__((aligned(16))) uint8_t Bs2[GBN * 128];
-  __shared__ __attribute__((aligned(16))) float2 ptab[256];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;            // 0..7
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7, wave-uniform (scalar)
   const bool producer = wave >= 4;      // waves 4..7 load and dequantize, waves 0..3 multiply
   const int ptid = tid - 256;           // producer thread id 0..255
   const int wm = wave & 1;              // consumer wave tile (128 x 64)
