@@ -39,6 +39,8 @@
 //     that the 16-byte MFMA fragment reads are bank-conflict free.
 //   * Workgroup ids are remapped so the tiles that run together on one XCD
 //     share the same rows of A (its L2 keeps that panel).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -150,11 +152,14 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
       const int r = (pw * 8 + i) * 8 + (lane >> 3);
       a_voff[i] = (uint32_t)(r * K * 2 + (((lane & 7) ^ swz(r)) << 4));
     }
+    // The step's column offset goes in the scalar soffset field (no VALU add per
+    // copy). Rows past M still read zero through the range check on voffset;
+    // steps past K are not issued at all (callers check kt < KT).
     auto issue_A = [&](int kt, int b) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         uint8_t* dst = abuf(b) + (pw * 8 + i) * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)dst, 16, a_voff[i] + kt * 128, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)dst, 16, a_voff[i], kt * 128, 0, 0);
       }
     };
     // Each producer thread owns 32 consecutive weights of one W row per K step:
@@ -250,17 +255,19 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
       else return t * sc;
     };
     u32x4 wreg[2][4];  // bf16 weight chunks (SRC == kSrcBF16)
+    // codes (or bf16 W) with the step offset in soffset, as for X; only for kt < KT
     auto issue_W = [&](int kt, int set) {
-      const uint32_t co = c_voff + (uint32_t)kt * c_step;
+      const int cs = (int)((uint32_t)kt * c_step);
       if constexpr (BF) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) wreg[set][q] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, co + q * 16, 0, 0);
+        for (int q = 0; q < 4; ++q)
+          wreg[set][q] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, c_voff + q * 16, cs, 0);
       } else {
         const uint32_t so = s_voff + (uint32_t)kt * s_step;
-        creg[set] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, co, 0, 0);
+        creg[set] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, c_voff, cs, 0);
         load_scale(so, set);
         if constexpr (RES) {
-          creg2[set] = __builtin_amdgcn_raw_buffer_load_b128(c2_rsrc, co, 0, 0);
+          creg2[set] = __builtin_amdgcn_raw_buffer_load_b128(c2_rsrc, c_voff, cs, 0);
           load_scale2(so, set);
         }
       }
@@ -298,37 +305,52 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
     };
     // prologue: tiles 0 and 1 into buffers 0 and 1; W(2) into set 0
     issue_A(0, 0);
-    issue_A(1, 1);
+    if (KT > 1) issue_A(1, 1);
     issue_W(0, 0);
-    issue_W(1, 1);
+    if (KT > 1) issue_W(1, 1);
     __syncthreads();  // (1) ptab
     dequant(0, 0);
-    dequant(1, 1);
-    issue_W(2, 0);
-    __builtin_amdgcn_s_waitcnt(kWaitW);
+    if (KT > 1) dequant(1, 1);
+    if (KT > 2) {
+      issue_W(2, 0);
+      __builtin_amdgcn_s_waitcnt(kWaitW);  // all but W(2): the X copies have landed
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+    }
     __syncthreads();  // (2) tiles 0, 1 published
     // step s: produce tile s+2 (A DMA into buffer (s+2)%3, dequant from set s%2),
     // fetch the codes of tile s+3 into set (s+1)%2, then the step's barrier.
     // Buffer (s+2)%3 held tile s-1, fully consumed before the previous barrier.
-    auto pstep = [&](int s, int j) {
+    // Near the end, tiles past K are neither loaded nor dequantized; a step that
+    // issues no codes waits for every load (the fixed count assumes W was last).
+    // FULL steps (s + 3 < KT) skip the checks.
+    auto pstep = [&](int s, int j, auto full) {
       __builtin_amdgcn_sched_barrier(0);
-      issue_A(s + 2, (j + 2) % 3);
+      if (full || s + 2 < KT) issue_A(s + 2, (j + 2) % 3);
       __builtin_amdgcn_sched_barrier(0);
-      issue_W(s + 3, (j + 1) & 1);
+      if (full || s + 3 < KT) issue_W(s + 3, (j + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
-      dequant(j & 1, (j + 2) % 3);
-      __builtin_amdgcn_s_waitcnt(kWaitW);
+      if (full || s + 2 < KT) dequant(j & 1, (j + 2) % 3);
+      if (full || s + 3 < KT) __builtin_amdgcn_s_waitcnt(kWaitW);  // all but W(s+3): X of tile s+2 landed
+      else __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     };
+    constexpr std::true_type kFull{};
+    constexpr std::false_type kTail{};
     int s = 0;
-    for (; s + 6 <= KT; s += 6) {
-      pstep(s, 0); pstep(s + 1, 1); pstep(s + 2, 2); pstep(s + 3, 3); pstep(s + 4, 4); pstep(s + 5, 5);
+    for (; s + 9 <= KT; s += 6) {
+      pstep(s, 0, kFull); pstep(s + 1, 1, kFull); pstep(s + 2, 2, kFull);
+      pstep(s + 3, 3, kFull); pstep(s + 4, 4, kFull); pstep(s + 5, 5, kFull);
     }
-    if (s < KT) pstep(s, 0);
-    if (s + 1 < KT) pstep(s + 1, 1);
-    if (s + 2 < KT) pstep(s + 2, 2);
-    if (s + 3 < KT) pstep(s + 3, 3);
-    if (s + 4 < KT) pstep(s + 4, 4);
+    // at most 8 steps remain; j keeps counting modulo 6
+    if (s < KT) pstep(s, 0, kTail);
+    if (s + 1 < KT) pstep(s + 1, 1, kTail);
+    if (s + 2 < KT) pstep(s + 2, 2, kTail);
+    if (s + 3 < KT) pstep(s + 3, 3, kTail);
+    if (s + 4 < KT) pstep(s + 4, 4, kTail);
+    if (s + 5 < KT) pstep(s + 5, 5, kTail);
+    if (s + 6 < KT) pstep(s + 6, 0, kTail);
+    if (s + 7 < KT) pstep(s + 7, 1, kTail);
     __builtin_amdgcn_s_waitcnt(0);
   } else {
     // ================= consumer waves: fragment reads and MFMAs only =================

@@ -216,6 +216,26 @@ def test_layer_ragged(M, o, h, r, dq, s):
     check_layer(d, s, dq)
 
 
+@pytest.mark.parametrize("kt", list(range(1, 17)))
+def test_gemm_k_steps(kt):
+    """The fused GEMM alone at every K-step count from 1 to 16 (K = 64*kt), both
+    directions, with a 16-column adapter tail and a ragged M: covers each length of
+    the pipeline's prologue and tail, which load and dequantize nothing past K."""
+    n = 64 * kt
+    d = synth.random_case(seed=300 + kt, rows=n, cols=n, M=70, r=16)
+    q = nf4.quantize(dev(d["W"]), 256)
+    wh = oracle.dequantize(oracle.quantize(d["W"], 64, 256)).astype(np.float64)
+    A2 = (d["X"][:, :16].float() * 0.5).bfloat16()
+    B2 = (d["dY"][:16, :].t().float() * 0.02).bfloat16().contiguous()  # [n][16]
+    say(f"gemm K-steps {kt}: M=70, o=h={n}")
+    Y = nf4.matmul(q, dev(d["X"]), False, dev(A2), dev(B2))
+    dX = nf4.matmul(q, dev(d["dY"]), True, dev(A2), dev(B2))
+    torch.cuda.synchronize()
+    tail = f64(A2) @ f64(B2).T
+    check_close("Y", Y, f64(d["X"]) @ wh.T + tail)
+    check_close("dX", dX, f64(d["dY"]) @ wh + tail)
+
+
 def test_layer_options_and_determinism():
     d = synth.random_case(seed=21, rows=256, cols=320, M=200, r=16)
     a = run_layer(d, 2.0, 256, use_T=True)
