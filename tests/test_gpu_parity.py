@@ -236,6 +236,20 @@ def test_gemm_k_steps(kt):
     check_close("dX", dX, f64(d["dY"]) @ wh + tail)
 
 
+@pytest.mark.parametrize("M,o,h,r", [
+    (1000, 320, 192, 16),    # padded rank 16: 8-row whole-K workgroups, 16-wave token chunks
+    (2048, 320, 192, 20),    # padded rank 32, r not a multiple of 8 (padded T)
+    (2048, 384, 256, 40),    # padded rank 48
+    (2048, 320, 576, 64),    # padded rank 64
+])
+def test_layer_unsplit_adapter_kernels(M, o, h, r):
+    """Token counts large enough for the whole-K and all-token adapter kernels at
+    every padded rank they serve, with ragged K steps, column bands and chunks."""
+    say(f"unsplit adapter products M={M} o={o} h={h} r={r}")
+    d = synth.random_case(seed=400 + r, rows=o, cols=h, M=M, r=r)
+    check_layer(d, 2.0, 256)
+
+
 def test_layer_options_and_determinism():
     d = synth.random_case(seed=21, rows=256, cols=320, M=200, r=16)
     a = run_layer(d, 2.0, 256, use_T=True)
