@@ -273,12 +273,13 @@ nf4_status check_batch(int64_t M, int32_t r) {
   return NF4_OK;
 }
 
+// B2 is [N][R], or k-major [R][N] with its first b2kn rows present (b2kn > 0)
 hipError_t gemm(int mode, const WSrc& w, const uint16_t* A, const uint16_t* A2, const uint16_t* B2, int R,
-                uint16_t* C, int64_t M, hipStream_t st) {
+                int b2kn, uint16_t* C, int64_t M, hipStream_t st) {
   const int64_t N = mode == MODE_FWD ? w.rows : w.cols;
   const int64_t K = mode == MODE_FWD ? w.cols : w.rows;
   return launch_nf4_gemm(mode, w.src, A, w.wb, w.codes, w.absmax, w.dqs, w.codes2, w.absmax2, w.dqs2, A2, B2, R,
-                         C, M, (int)N, (int)K, codebook_consts(w.codebook), st);
+                         b2kn, C, M, (int)N, (int)K, codebook_consts(w.codebook), st);
 }
 
 nf4_status layer_fwd(const WSrc& W, const uint16_t* X, int64_t M, const uint16_t* L1, const uint16_t* L2,
@@ -312,6 +313,14 @@ nf4_status layer_fwd(const WSrc& W, const uint16_t* X, int64_t M, const uint16_t
   uint16_t* ts = (uint16_t*)(w + p.off_ts);
   float* part = (float*)(w + p.off_part);
   unsigned* cnt = (unsigned*)(w + p.off_cnt);
+  if (skinny_nt_whole(M, p.RP) && r % 8 == 0) {
+    // no prep launch: the whole-K product reads L1 as stored (k-major, staged and
+    // read transposed in LDS) and the GEMM tail reads L2 as stored ([r][o])
+    NtArgs nt{X, L1, M, (int)h, 1, (int)h, part, cnt, r, 1.0f, T_out, r, s, ts, r};
+    NF4_TRY(launch_skinny_nt(nt, p.RP, hs));
+    NF4_TRY(gemm(MODE_FWD, W, X, ts, L2, p.RP, r, Y, M, hs));
+    return NF4_OK;
+  }
   // one prep launch: L1^T [RP][h] (rows >= r zero), L2^T [o][RP] (columns >= r zero), counters
   PrepArgs pa{};
   pa.pad[0] = pad_job(L1, 1, r, r, h, l1t, p.RP, h);
@@ -322,7 +331,7 @@ nf4_status layer_fwd(const WSrc& W, const uint16_t* X, int64_t M, const uint16_t
   NtArgs nt{X, l1t, M, (int)h, p.ks, p.kr, part, cnt, r, 1.0f, T_out, r, s, ts};
   NF4_TRY(launch_skinny_nt(nt, p.RP, hs));
   // Y = X w_hat^T + (s T) L2
-  NF4_TRY(gemm(MODE_FWD, W, X, ts, l2t, p.RP, Y, M, hs));
+  NF4_TRY(gemm(MODE_FWD, W, X, ts, l2t, p.RP, 0, Y, M, hs));
   return NF4_OK;
 }
 
@@ -414,7 +423,7 @@ nf4_status layer_bwd(const WSrc& W, const uint16_t* X, const uint16_t* dY, int64
   NF4_TRY(launch_skinny_tn(t1, p.RP, hs));
   // dX = dY w_hat + G L1^T
   if (dX) {
-    NF4_TRY(gemm(MODE_DX, W, dY, g, l1b, p.RP, dX, M, hs));
+    NF4_TRY(gemm(MODE_DX, W, dY, g, l1b, p.RP, 0, dX, M, hs));
   }
   return NF4_OK;
 }
@@ -435,7 +444,7 @@ nf4_status plain_product(int mode, const WSrc& w, const uint16_t* A, uint16_t* C
   if (overlap(out, rng(A, (size_t)M * K * 2))) return NF4_ERR_ALIAS;
   for (const Range& b : w.buf)
     if (overlap(out, b)) return NF4_ERR_ALIAS;
-  return hip_status(gemm(mode, w, A, nullptr, nullptr, 0, C, M, (hipStream_t)stream));
+  return hip_status(gemm(mode, w, A, nullptr, nullptr, 0, 0, C, M, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -593,7 +602,7 @@ nf4_status nf4_matmul(const nf4_tensor* W, int32_t transpose, const uint16_t* A,
     if (overlap(out, b)) return NF4_ERR_ALIAS;
   for (const Range& b : w.buf)
     if (overlap(out, b)) return NF4_ERR_ALIAS;
-  return hip_status(gemm(transpose ? MODE_DX : MODE_FWD, w, A, A2, B2, R, C, M, (hipStream_t)stream));
+  return hip_status(gemm(transpose ? MODE_DX : MODE_FWD, w, A, A2, B2, R, 0, C, M, (hipStream_t)stream));
 }
 
 nf4_status nf4_layer_error(const float* W, int64_t rows, int64_t cols, int32_t block, int32_t dq_group,

@@ -68,7 +68,8 @@ struct GemmArgs {
   int64_t M;
   int N;
   int K;
-  int R;  // tail width, a multiple of 16 (0 = no tail)
+  int R;     // tail width, a multiple of 16 (0 = no tail)
+  int b2kn;  // 0: B2 is [N][R]; > 0: B2 is [R][N] with its first b2kn rows present
   int tiles_n;
   int64_t nblocks;
 };
@@ -142,6 +143,18 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  // Input grad (and a k-major tail): B fragments come from the [k][n] tile through
+  // ds_read_b64_tr_b16.
+  // In each group of 16 lanes, lane 4e+q points at row k0+e, columns nb+4q..+3,
+  // and lane j receives column nb+j of rows k0..k0+3; two reads (k0 and k0+4)
+  // give the 8 consecutive k of the MFMA operand.
+  uint32_t b_off[2];
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) {
+    const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+    const int nb = wn * 64 + ni * 32 + 16 * (g & 1);
+    b_off[ni] = (uint32_t)(lds_off_kn(8 * (g >> 1) + e, (nb >> 3) + (q >> 1)) + 8 * (q & 1));
+  }
   if (producer) {
     // ================= producer waves =================
     const int pw = wave - 4;
@@ -357,17 +370,6 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
     struct Frags {
       bf16x8 a[4], b[2];
     };
-    // Input grad: B fragments come from the [k][n] tile through ds_read_b64_tr_b16.
-    // In each group of 16 lanes, lane 4e+q points at row k0+e, columns nb+4q..+3,
-    // and lane j receives column nb+j of rows k0..k0+3; two reads (k0 and k0+4)
-    // give the 8 consecutive k of the MFMA operand.
-    uint32_t b_off[2];
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
-      const int nb = wn * 64 + ni * 32 + 16 * (g & 1);
-      b_off[ni] = (uint32_t)(lds_off_kn(8 * (g >> 1) + e, (nb >> 3) + (q >> 1)) + 8 * (q & 1));
-    }
     auto load_frags = [&](int b, int kk, Frags& f) {
       const uint8_t* Ab = abuf(b);
       const uint8_t* Bb = bbuf(b);
@@ -447,7 +449,9 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
   if (p.R > 0) {
     const __amdgpu_buffer_rsrc_t a2 = make_rsrc(p.A2 + m0 * p.R, (uint32_t)(arows * p.R * 2));
     const int nrows = (N - n0) < GBN ? (N - n0) : GBN;
-    const __amdgpu_buffer_rsrc_t b2 = make_rsrc(p.B2 + (int64_t)n0 * p.R, (uint32_t)(nrows * p.R * 2));
+    const __amdgpu_buffer_rsrc_t b2 =
+        p.b2kn ? make_rsrc(p.B2, (uint32_t)((int64_t)p.b2kn * N * 2))
+               : make_rsrc(p.B2 + (int64_t)n0 * p.R, (uint32_t)(nrows * p.R * 2));
     for (int c0 = 0; c0 < p.R; c0 += GBK) {
       const int width = min(GBK, p.R - c0);
 #pragma unroll
@@ -457,12 +461,24 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
         const uint32_t off = kc * 8 < width ? (uint32_t)((r * p.R + c0 + kc * 8) * 2) : kOOB;
         *(u32x4*)(As0 + lds_off(r, kc)) = __builtin_amdgcn_raw_buffer_load_b128(a2, off, 0, 0);
       }
+      if (p.b2kn) {
+        // k-major B2: 64 tail rows x 128 columns into the [k][n] layout
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int r = tid >> 2;
-        const int kc = (tid & 3) * 2 + jj;
-        const uint32_t off = kc * 8 < width ? (uint32_t)((r * p.R + c0 + kc * 8) * 2) : kOOB;
-        *(u32x4*)(Bs0 + lds_off(r, kc)) = __builtin_amdgcn_raw_buffer_load_b128(b2, off, 0, 0);
+        for (int jj = 0; jj < 2; ++jj) {
+          const int e = tid + 512 * jj;
+          const int kr = e >> 4, slot = e & 15;
+          const bool ok = kr < width && n0 + slot * 8 < N;
+          const uint32_t off = ok ? (uint32_t)(((int64_t)(c0 + kr) * N + n0 + slot * 8) * 2) : kOOB;
+          *(u32x4*)(Bs0 + lds_off_kn(kr, slot)) = __builtin_amdgcn_raw_buffer_load_b128(b2, off, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int r = tid >> 2;
+          const int kc = (tid & 3) * 2 + jj;
+          const uint32_t off = kc * 8 < width ? (uint32_t)((r * p.R + c0 + kc * 8) * 2) : kOOB;
+          *(u32x4*)(Bs0 + lds_off(r, kc)) = __builtin_amdgcn_raw_buffer_load_b128(b2, off, 0, 0);
+        }
       }
       __syncthreads();
       if (!producer) {
@@ -473,8 +489,16 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
           for (int mi = 0; mi < 4; ++mi)
             fa[mi] = *(const bf16x8*)(As0 + lds_off(wm * 128 + mi * 32 + (lane & 31), chunk));
 #pragma unroll
-          for (int ni = 0; ni < 2; ++ni)
-            fb[ni] = *(const bf16x8*)(Bs0 + lds_off(wn * 64 + ni * 32 + (lane & 31), chunk));
+          for (int ni = 0; ni < 2; ++ni) {
+            if (p.b2kn) {
+              uint8_t* src = Bs0 + kk * 4096 + b_off[ni];
+              const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)src);
+              const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(src + 1024));
+              fb[ni] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            } else {
+              fb[ni] = *(const bf16x8*)(Bs0 + lds_off(wn * 64 + ni * 32 + (lane & 31), chunk));
+            }
+          }
 #pragma unroll
           for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -512,8 +536,8 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
 
 hipError_t launch_nf4_gemm(int mode, int src, const uint16_t* A, const uint16_t* Wb, const uint8_t* codes,
                            const void* absmax, const float* dqs, const uint8_t* codes2, const void* absmax2,
-                           const float* dqs2, const uint16_t* A2, const uint16_t* B2, int R, uint16_t* C, int64_t M,
-                           int N, int K, const NF4Consts& c, hipStream_t st) {
+                           const float* dqs2, const uint16_t* A2, const uint16_t* B2, int R, int b2kn, uint16_t* C,
+                           int64_t M, int N, int K, const NF4Consts& c, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   GemmArgs p;
   p.A = A;
@@ -531,6 +555,7 @@ hipError_t launch_nf4_gemm(int mode, int src, const uint16_t* A, const uint16_t*
   p.N = N;
   p.K = K;
   p.R = R;
+  p.b2kn = R > 0 ? b2kn : 0;
   p.nblocks = (int64_t)N * K / 64;
   const int64_t tiles_m = (M + GBM - 1) / GBM;
   p.tiles_n = (N + GBN - 1) / GBN;

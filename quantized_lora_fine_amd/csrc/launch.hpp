@@ -24,10 +24,11 @@ hipError_t launch_topk(const double* e, int n, int k, int* idx, hipStream_t st);
 // Weight source of the fused GEMM: NF4 with fp32 absmax, NF4 with 8-bit
 // double-quantized scales, or a bf16 weight (no quantization).
 enum { kSrcNF4 = 0, kSrcNF4DQ = 1, kSrcBF16 = 2 };
+// Tail B2: [N][R] (b2kn == 0), or k-major [R][N] with rows b2kn .. R-1 absent (read as zero).
 hipError_t launch_nf4_gemm(int mode, int src, const uint16_t* A, const uint16_t* Wb, const uint8_t* codes,
                            const void* absmax, const float* dqs, const uint8_t* codes2, const void* absmax2,
-                           const float* dqs2, const uint16_t* A2, const uint16_t* B2, int R, uint16_t* C, int64_t M,
-                           int N, int K, const NF4Consts& c, hipStream_t st);
+                           const float* dqs2, const uint16_t* A2, const uint16_t* B2, int R, int b2kn, uint16_t* C,
+                           int64_t M, int N, int K, const NF4Consts& c, hipStream_t st);
 
 // W' = base + s (L1 L2)^T into fp32 or bf16; base 0: fp32 W, 1: NF4, 2: NF4 with 8-bit scales.
 hipError_t launch_merge(int base, const float* W, const uint8_t* codes, const void* absmax, const float* dqs,
@@ -69,6 +70,8 @@ struct NtArgs {
   int ld1;
   float alpha2;
   uint16_t* out2;   // [M][RP], or NULL
+  int bkn;          // 0: B is [RP][K]; > 0: B is k-major [K][bkn] (its first r columns used;
+                    // whole-K kernel only, bkn % 8 == 0)
 };
 // TN skinny product with its split reduction: out = alpha * P[M][:r]^T Q[M][N].
 struct TnArgs {

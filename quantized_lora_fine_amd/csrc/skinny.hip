@@ -213,19 +213,40 @@ __global__ __launch_bounds__(256) void k_skinny_nt(NtArgs p) {
 // added in LDS in wave order; no partials, counters or second pass.
 // With RW = 8 the MFMA A operand's rows 8..15 are zero.
 // ---------------------------------------------------------------------------
+// 8 consecutive rows (k) of one column as an MFMA operand: two transposing
+// reads of 4 rows each; `lo` is this lane's address in the first 4 rows.
+typedef short s16x4_tn __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_tn* lds_s16x4_tn;
+
+__device__ __forceinline__ bf16x8 tr_frag(uint8_t* lo, int row_bytes) {
+  const s16x4_tn a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_tn)lo);
+  const s16x4_tn b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_tn)(lo + 4 * row_bytes));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 template <int RPT>
 struct NtRows {
   static constexpr int RW = RPT <= 16 ? 8 : (RPT <= 32 ? 16 : 32);
   static constexpr int FRA = RW >= 16 ? RW / 16 : 1;    // A fragments of 16 rows
   static constexpr int NJ = RPT / 16;
   static constexpr int U = 16 / (FRA + NJ);             // K steps per wave per round
+  // k-major B: each wave stages one K step of B (32 rows x RPT) in LDS, rows
+  // padded so a transposing read's 4 rows fall on distinct banks
+  static constexpr int ROWB = RPT * 2 + (RPT * 2 % 128 == 0 ? 16 : 0);
+  static constexpr int PPR = RPT / 8;                   // 16-byte pieces per B row
+  static constexpr int BL = (32 * PPR + 63) / 64;       // B loads per lane per K step
+  static constexpr int RED = 16 * RW * RPT * 4, STG = 16 * 32 * ROWB;
+  static constexpr int SMEM = RED > STG ? RED : STG;
 };
 
-template <int RPT>
+template <int RPT, bool BKN>
 __global__ __launch_bounds__(1024) void k_skinny_nt_rows(NtArgs p) {
   using S = NtRows<RPT>;
   constexpr int RW = S::RW, FRA = S::FRA, NJ = S::NJ, U = S::U;
-  __shared__ float red[16 * RW * RPT];
+  constexpr int ROWB = S::ROWB, PPR = S::PPR, BL = S::BL;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[BKN ? S::SMEM : S::RED];
+  float* red = (float*)smem;
+  uint8_t* stage = smem + (BKN ? (threadIdx.x >> 6) * 32 * ROWB : 0);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -250,8 +271,12 @@ __global__ __launch_bounds__(1024) void k_skinny_nt_rows(NtArgs p) {
     arow[a] = p.A + (aval[a] ? m : 0) * (int64_t)K;
   }
   const uint16_t* brow = p.B + (int64_t)li * K + kq;
+  // transposing-read address of this lane in a staged K step (k-major B)
+  const int trow = 8 * (lane >> 4) + ((lane >> 2) & 3);
   for (int k0 = 32 * wave; k0 < K; k0 += 512 * U) {
-    bf16x8 af[U][FRA], bf[U][NJ];
+    bf16x8 af[U][FRA];
+    bf16x8 bf[BKN ? 1 : U][NJ];
+    u32x4 breg[BKN ? U : 1][BL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = k0 + 512 * u;
@@ -262,21 +287,49 @@ __global__ __launch_bounds__(1024) void k_skinny_nt_rows(NtArgs p) {
         if (kv && aval[a]) v = __builtin_nontemporal_load((const u32x4*)(arow[a] + k + kq));
         af[u][a] = __builtin_bit_cast(bf16x8, v);
       }
+      if constexpr (BKN) {
+        // rows k .. k+31 of B as 16-byte pieces (piece e: row e/PPR, columns 8*(e%PPR) ..)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (kv) v = *(const u32x4*)(brow + (int64_t)j * 16 * K + k);
-        bf[u][j] = __builtin_bit_cast(bf16x8, v);
+        for (int i = 0; i < BL; ++i) {
+          const int e = lane + 64 * i;
+          const int row = e / PPR, c8 = 8 * (e % PPR);
+          u32x4 v = u32x4{0u, 0u, 0u, 0u};
+          if (kv && e < 32 * PPR && c8 < p.r) v = *(const u32x4*)(p.B + (int64_t)(k + row) * p.bkn + c8);
+          breg[u][i] = v;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          u32x4 v = u32x4{0u, 0u, 0u, 0u};
+          if (kv) v = *(const u32x4*)(brow + (int64_t)j * 16 * K + k);
+          bf[u][j] = __builtin_bit_cast(bf16x8, v);
+        }
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      bf16x8 bk[NJ];
+      if constexpr (BKN) {
+        // stage the step row-major, then read each 16-column group transposed
+#pragma unroll
+        for (int i = 0; i < BL; ++i) {
+          const int e = lane + 64 * i;
+          if (e < 32 * PPR) *(u32x4*)(stage + (e / PPR) * ROWB + 16 * (e % PPR)) = breg[u][i];
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) bk[j] = tr_frag(stage + trow * ROWB + 2 * (16 * j + 4 * (lane & 3)), ROWB);
+      } else {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) bk[j] = bf[u][j];
+      }
 #pragma unroll
       for (int a = 0; a < FRA; ++a)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          acc[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u][a], bf[u][j], acc[a][j], 0, 0, 0);
+          acc[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u][a], bk[j], acc[a][j], 0, 0, 0);
+    }
   }
+  if constexpr (BKN) __syncthreads();  // every wave is done with its stage before the tiles reuse it
   // D[i][jj]: lane holds column jj = lane%16, rows i = 4*(lane/16) + v
 #pragma unroll
   for (int a = 0; a < FRA; ++a)
@@ -463,15 +516,6 @@ struct TnCols {
   static constexpr int DEPTH = WAVES == 16 ? (NC == 32 ? 4 : 2) : (QL + PL <= 6 ? 3 : 2);
   static constexpr int SMEM = WAVES * STAGE > 4 * RPT * NC * 4 ? WAVES * STAGE : 4 * RPT * NC * 4;
 };
-
-typedef short s16x4_tn __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4_tn* lds_s16x4_tn;
-
-__device__ __forceinline__ bf16x8 tr_frag(uint8_t* lo, int row_bytes) {
-  const s16x4_tn a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_tn)lo);
-  const s16x4_tn b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_tn)(lo + 4 * row_bytes));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-}
 
 template <int RPT, int NC, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_skinny_tn_cols(TnArgs p) {
@@ -668,17 +712,22 @@ bool skinny_tn_whole(int64_t M, int RP) { return RP <= 64 && M >= 512; }
 
 hipError_t launch_skinny_nt(const NtArgs& a, int RP, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
+  if (a.bkn && !skinny_nt_whole(a.M, RP)) return hipErrorInvalidValue;  // k-major B: whole-K kernel only
   {
     if (skinny_nt_whole(a.M, RP)) {
       const int rw = RP <= 16 ? 8 : (RP <= 32 ? 16 : 32);
       const int64_t nwg = (a.M + rw - 1) / rw;
       const dim3 gr((unsigned)nwg), bl(1024);
+#define L_NTR(R)                                                                     \
+  if (a.bkn) hipLaunchKernelGGL((k_skinny_nt_rows<R, true>), gr, bl, 0, st, a);      \
+  else hipLaunchKernelGGL((k_skinny_nt_rows<R, false>), gr, bl, 0, st, a);
       switch (RP) {
-        case 16: hipLaunchKernelGGL(k_skinny_nt_rows<16>, gr, bl, 0, st, a); break;
-        case 32: hipLaunchKernelGGL(k_skinny_nt_rows<32>, gr, bl, 0, st, a); break;
-        case 48: hipLaunchKernelGGL(k_skinny_nt_rows<48>, gr, bl, 0, st, a); break;
-        default: hipLaunchKernelGGL(k_skinny_nt_rows<64>, gr, bl, 0, st, a); break;
+        case 16: L_NTR(16) break;
+        case 32: L_NTR(32) break;
+        case 48: L_NTR(48) break;
+        default: L_NTR(64) break;
       }
+#undef L_NTR
       return hipGetLastError();
     }
   }
