@@ -77,9 +77,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--workload", default="c2", choices=["c2", "c4-stack"],
-                    help="c2: the 4096x4096 layer (default); c4-stack: the 280-linear 14B-shaped stack with "
-                         "AQLoRA's allocation against QLoRA")
+    ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c5", "c4-stack"],
+                    help="c2: the 4096x4096 layer (default); c3: the three 7B-shaped MLP linears; c5: the "
+                         "70B-shaped up projection; c4-stack: the 280-linear 14B-shaped stack with AQLoRA's "
+                         "allocation against QLoRA")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -96,6 +97,8 @@ def main():
 
     if args.workload == "c4-stack":
         return bench_stack(args)
+    if args.workload in ("c3", "c5"):
+        return bench_layers(args)
 
     cfg = synth.C2
     M, o, h, r, s = cfg.M, cfg.rows, cfg.cols, cfg.r, cfg.s
@@ -290,6 +293,87 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    print(json.dumps(out), flush=True)
+
+
+def bench_layers(args):
+    """Larger single layers at their full sizes: c3 (gate, up, down of a 7B-shaped
+    MLP, M=8192, r=64) or c5 (a 70B-shaped up projection, M=16384, r=64).  Per
+    linear: quantize (8-bit DQ scales) and bf16 dequantize as standalone passes,
+    and the fused fwd and bwd, each timed with HIP events over `steps` calls after
+    `warmup`.  The value is the fwd+bwd FLOP of all the linears over their summed
+    fwd+bwd time.  The CPU oracle is not timed at these sizes (cpu_baseline is
+    null); the full-size parity tests check these workloads against it."""
+    import torch
+
+    import quantized_lora_fine_amd as nf4
+    import synth
+
+    layers = {"c3": [synth.C3_GATE, synth.C3_UP, synth.C3_DOWN], "c5": [synth.C5]}[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    print(f"# device {torch.cuda.get_device_name(0)}; workload {args.workload}", file=sys.stderr, flush=True)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps  # ms
+
+    per, F_all, ms_all = [], 0.0, 0.0
+    for cfg in layers:
+        M, o, h, r, s = cfg.M, cfg.rows, cfg.cols, cfg.r, cfg.s
+        d = synth.layer_inputs(cfg)
+        W = torch.from_numpy(d["W"]).to(dev)
+        X, L1, L2, dY = (d[k].to(dev).contiguous() for k in ("X", "L1", "L2", "dY"))
+        del d
+        q = nf4.NF4Weight(o, h, 256, dev)
+        n = o * h
+        q_ms = timed(lambda: nf4.quantize(W, 256, out=q))
+        Wd = torch.empty(o, h, dtype=torch.bfloat16, device=dev)
+        dq_ms = timed(lambda: nf4.dequantize(q, bf16=True, out=Wd))
+        del Wd, W
+        ws_f = nf4.workspace(nf4.NF4_OP_FWD, M, q, r)
+        ws_b = nf4.workspace(nf4.NF4_OP_BWD, M, q, r)
+        Y = torch.empty(M, o, dtype=torch.bfloat16, device=dev)
+        T = torch.empty(M, r, dtype=torch.bfloat16, device=dev)
+        dX = torch.empty(M, h, dtype=torch.bfloat16, device=dev)
+        dL1 = torch.empty(h, r, dtype=torch.float32, device=dev)
+        dL2 = torch.empty(r, o, dtype=torch.float32, device=dev)
+        f_ms = timed(lambda: nf4.fwd(q, X, L1, L2, s, ws=ws_f, out=Y, T_out=T))
+        b_ms = timed(lambda: nf4.bwd(q, X, dY, L1, L2, s, T=T, ws=ws_b, outs=(dX, dL1, dL2)))
+        F = flops_fwd_bwd(M, h, o, r)
+        F_all += F
+        ms_all += f_ms + b_ms
+        q_bytes = 4 * n + n // 2 + n // 64 + 4 * (n // 64 // 256)
+        dq_bytes = n // 2 + n // 64 + 4 * (n // 64 // 256) + 2 * n
+        tf = F / ((f_ms + b_ms) * 1e-3) / 1e12
+        per.append({"linear": cfg.name, "o": o, "h": h, "tokens": M, "rank": r, "flops_fwd_bwd": F,
+                    "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4), "fwd_bwd_tflops": round(tf, 1),
+                    "fwd_bwd_pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                    "quantize_us": round(1e3 * q_ms, 2), "quantize_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+                    "dequantize_bf16_us": round(1e3 * dq_ms, 2),
+                    "dequantize_GBps": round(dq_bytes / (dq_ms * 1e-3) / 1e9, 1)})
+        print(f"# {cfg.name}: fwd {f_ms:.3f} ms, bwd {b_ms:.3f} ms ({tf:.1f} TFLOP/s); quantize {1e3 * q_ms:.1f} us, "
+              f"dequantize {1e3 * dq_ms:.1f} us", file=sys.stderr, flush=True)
+        del q, X, L1, L2, dY, Y, T, dX, dL1, dL2, ws_f, ws_b
+        torch.cuda.empty_cache()
+    value = F_all / (ms_all * 1e-3) / 1e12
+    wl = {"c3": "llama7b MLP gate, up (W 11008x4096) and down (W 4096x11008), NF4 + DQ/256, M=8192, r=64, s=2",
+          "c5": "70b up projection W 28672x8192, NF4 + DQ/256, M=16384, r=64, s=2"}[args.workload]
+    out = {"metric": f"fused NF4-LoRA linear fwd+bwd TFLOP/s and % bf16 MFMA peak, {args.workload}",
+           "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_all, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": wl, "step": "fwd+bwd of each linear", "flops_fwd_bwd": F_all},
+           "fwd_bwd_pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+           "linears": per, "roofline": None, "cpu_baseline": None}
     print(json.dumps(out), flush=True)
 
 

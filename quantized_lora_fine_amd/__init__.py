@@ -191,8 +191,12 @@ def quantize(W: torch.Tensor, dq_group: int = 0, out: NF4Weight | None = None, c
     return q
 
 
-def dequantize(q: NF4Weight, bf16: bool = False) -> torch.Tensor:
-    out = torch.empty(q.rows, q.cols, dtype=torch.bfloat16 if bf16 else torch.float32, device=q.codes.device)
+def dequantize(q: NF4Weight, bf16: bool = False, out: torch.Tensor | None = None) -> torch.Tensor:
+    """nf4_dequantize into fp32 (or bf16) [rows][cols], into `out` when given."""
+    if out is None:
+        out = torch.empty(q.rows, q.cols, dtype=torch.bfloat16 if bf16 else torch.float32, device=q.codes.device)
+    assert out.dtype == (torch.bfloat16 if bf16 else torch.float32) and out.is_contiguous()
+    assert out.shape == (q.rows, q.cols)
     _check(_lib.nf4_dequantize(ctypes.byref(q.desc), _ptr(out), 1 if bf16 else 0, _stream()), "nf4_dequantize")
     return out
 
