@@ -29,6 +29,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
+// MFMA operand of 8 consecutive rows (k) of one column from a row-major LDS
+// tile, through two ds_read_b64_tr_b16 of 4 rows each.  In each group of 16
+// lanes, lane 4e+q passes the address of row e, columns c+4q .. c+4q+3 (`lo`,
+// 8-byte aligned; the second read is row_bytes*4 further), and lane i receives
+// column c+i of the 4 rows.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+__device__ __forceinline__ bf16x8 lds_tr8(uint8_t* lo, int row_bytes) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)lo);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(lo + 4 * row_bytes));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Max over the 16 lanes of a DPP row (lanes 16k .. 16k+15) of non-negative
 // fp32 values given as bit patterns (for which unsigned order is float order);
 // every lane of the row receives the result.  bound_ctrl reads 0 (the
@@ -39,22 +52,6 @@ __device__ __forceinline__ uint32_t row16_max_bits(uint32_t x) {
   x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, true));  // row_half_mirror
   x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, true));  // row_mirror
   return x;
-}
-
-// Max over the 16 lanes of a DPP row of |v| (every lane of the row receives it).
-__device__ __forceinline__ float row16_absmax(float v) {
-  return __builtin_bit_cast(float, row16_max_bits(__builtin_bit_cast(uint32_t, v) & 0x7FFFFFFFu));
-}
-
-// Sum over the 16 lanes of a DPP row, same pattern as row16_max (fixed order,
-// identical result in every lane of the row).
-__device__ __forceinline__ double row16_sum(double v) {
-  double s = v;
-  s += __shfl_xor(s, 1, 16);
-  s += __shfl_xor(s, 2, 16);
-  s += __shfl_xor(s, 4, 16);
-  s += __shfl_xor(s, 8, 16);
-  return s;
 }
 
 }  // namespace nf4k

@@ -86,8 +86,6 @@ __device__ __forceinline__ int lds_off_kn(int k, int slot) {
   const int x = k & 3;
   return k * 256 + ((((slot >> 2) ^ x) << 2 | ((slot & 3) ^ x)) << 4);
 }
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcFlags);
@@ -382,10 +380,7 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
         if constexpr (MODE == MODE_FWD) {
           f.b[ni] = *(const bf16x8*)(Bb + lds_off(wn * 64 + ni * 32 + (lane & 31), chunk));
         } else {
-          uint8_t* src = const_cast<uint8_t*>(Bb) + kk * 4096 + b_off[ni];
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)src);
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(src + 1024));
-          f.b[ni] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          f.b[ni] = lds_tr8(const_cast<uint8_t*>(Bb) + kk * 4096 + b_off[ni], 256);
         }
       }
     };
@@ -491,10 +486,7 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
 #pragma unroll
           for (int ni = 0; ni < 2; ++ni) {
             if (p.b2kn) {
-              uint8_t* src = Bs0 + kk * 4096 + b_off[ni];
-              const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)src);
-              const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(src + 1024));
-              fb[ni] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+              fb[ni] = lds_tr8(Bs0 + kk * 4096 + b_off[ni], 256);
             } else {
               fb[ni] = *(const bf16x8*)(Bs0 + lds_off(wn * 64 + ni * 32 + (lane & 31), chunk));
             }

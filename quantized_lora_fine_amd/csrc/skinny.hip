@@ -213,17 +213,6 @@ __global__ __launch_bounds__(256) void k_skinny_nt(NtArgs p) {
 // added in LDS in wave order; no partials, counters or second pass.
 // With RW = 8 the MFMA A operand's rows 8..15 are zero.
 // ---------------------------------------------------------------------------
-// 8 consecutive rows (k) of one column as an MFMA operand: two transposing
-// reads of 4 rows each; `lo` is this lane's address in the first 4 rows.
-typedef short s16x4_tn __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4_tn* lds_s16x4_tn;
-
-__device__ __forceinline__ bf16x8 tr_frag(uint8_t* lo, int row_bytes) {
-  const s16x4_tn a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_tn)lo);
-  const s16x4_tn b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_tn)(lo + 4 * row_bytes));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
 template <int RPT>
 struct NtRows {
   static constexpr int RW = RPT <= 16 ? 8 : (RPT <= 32 ? 16 : 32);
@@ -317,7 +306,7 @@ __global__ __launch_bounds__(1024) void k_skinny_nt_rows(NtArgs p) {
           if (e < 32 * PPR) *(u32x4*)(stage + (e / PPR) * ROWB + 16 * (e % PPR)) = breg[u][i];
         }
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) bk[j] = tr_frag(stage + trow * ROWB + 2 * (16 * j + 4 * (lane & 3)), ROWB);
+        for (int j = 0; j < NJ; ++j) bk[j] = lds_tr8(stage + trow * ROWB + 2 * (16 * j + 4 * (lane & 3)), ROWB);
       } else {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) bk[j] = bf[u][j];
@@ -583,9 +572,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_skinny_tn_cols(TnArgs p) {
   auto compute = [&]() {
     bf16x8 bq[NG], ap[NJ];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) bq[g] = tr_frag(qs + trow * QROW + 2 * (16 * g + 4 * q), QROW);
+    for (int g = 0; g < NG; ++g) bq[g] = lds_tr8(qs + trow * QROW + 2 * (16 * g + 4 * q), QROW);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) ap[j] = tr_frag(ps + trow * PROW + 2 * (16 * j + 4 * q), PROW);
+    for (int j = 0; j < NJ; ++j) ap[j] = lds_tr8(ps + trow * PROW + 2 * (16 * j + 4 * q), PROW);
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
