@@ -418,9 +418,8 @@ nf4_status layer_bwd(const WSrc& W, const uint16_t* X, const uint16_t* dY, int64
   NF4_TRY(launch_skinny_nt(ng, p.RP, hs));
   // dL2 = s T^T dY  ([r][o]),  dL1 = X^T G  (stored [h][r])
   TnArgs t2{tsrc, ldt, r, dY, M, (int)o, p.ms2, p.mr2, p2, cnt + p.cnt_2, s, 0, dL2};
-  NF4_TRY(launch_skinny_tn(t2, p.RP, hs));
   TnArgs t1{g, p.RP, r, X, M, (int)h, p.ms1, p.mr1, p1, cnt + p.cnt_1, 1.0f, 1, dL1};
-  NF4_TRY(launch_skinny_tn(t1, p.RP, hs));
+  NF4_TRY(launch_skinny_tn2(t2, &t1, p.RP, hs));
   // dX = dY w_hat + G L1^T
   if (dX) {
     NF4_TRY(gemm(MODE_DX, W, dY, g, l1b, p.RP, 0, dX, M, hs));

@@ -92,6 +92,8 @@ void plan_nt(int64_t M, int K, int* ksplit, int* krange);
 void plan_tn(int64_t M, int N, int* msplit, int64_t* mrange);
 hipError_t launch_skinny_nt(const NtArgs& a, int RP, hipStream_t st);
 hipError_t launch_skinny_tn(const TnArgs& a, int RP, hipStream_t st);
+// two TN products over the same tokens in one launch when possible (b may be NULL)
+hipError_t launch_skinny_tn2(const TnArgs& a, const TnArgs* b, int RP, hipStream_t st);
 // true when the launchers above use the unsplit kernels (whole K / all tokens
 // per workgroup), which need neither the partial buffers nor the counters
 bool skinny_nt_whole(int64_t M, int RP);

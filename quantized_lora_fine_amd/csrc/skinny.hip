@@ -506,20 +506,19 @@ struct TnCols {
   static constexpr int SMEM = WAVES * STAGE > 4 * RPT * NC * 4 ? WAVES * STAGE : 4 * RPT * NC * 4;
 };
 
+// One workgroup's share of one product: column band `bid` of `nwg`.
 template <int RPT, int NC, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void k_skinny_tn_cols(TnArgs p) {
+__device__ __forceinline__ void tn_cols_band(const TnArgs& p, int bid, int nwg, uint8_t* smem) {
   using S = TnCols<RPT, NC, WAVES>;
   constexpr int NJ = S::NJ, NG = S::NG, QROW = S::QROW, PROW = S::PROW;
   constexpr int QPR = S::QPR, QTL = S::QTL, QL = S::QL, PPR = S::PPR, PTL = S::PTL, PL = S::PL;
   constexpr int DEPTH = S::DEPTH;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[S::SMEM];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   // neighbouring column bands share 128-byte lines of Q: keep them on one XCD
   // (workgroups are dealt to the 8 XCDs round-robin) so they meet in its L2
-  int bid = blockIdx.x;
-  if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+  if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);
   const int n0 = bid * NC;
   const int64_t M = p.M;
   const int N = p.N;
@@ -621,6 +620,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_skinny_tn_cols(TnArgs p) {
     if (p.trans) p.out[(int64_t)n * p.r + j] = p.alpha * sum;
     else p.out[(int64_t)j * N + n] = p.alpha * sum;
   }
+}
+
+// Two TN products in one launch (the first nwg0 workgroups run p0, the rest
+// p1), so that two narrow products together fill the chip; nwg1 = 0 runs one.
+template <int RPT, int NC, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_skinny_tn_cols(TnArgs p0, TnArgs p1, int nwg0, int nwg1) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[TnCols<RPT, NC, WAVES>::SMEM];
+  if ((int)blockIdx.x < nwg0) tn_cols_band<RPT, NC, WAVES>(p0, blockIdx.x, nwg0, smem);
+  else tn_cols_band<RPT, NC, WAVES>(p1, blockIdx.x - nwg0, nwg1, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -728,17 +736,21 @@ hipError_t launch_skinny_nt(const NtArgs& a, int RP, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_skinny_tn(const TnArgs& a, int RP, hipStream_t st) {
+// One TN product, or two (b != NULL, same M) in one launch when both take the
+// all-token kernel; otherwise the split kernel runs each.
+hipError_t launch_skinny_tn2(const TnArgs& a, const TnArgs* b, int RP, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
   // all tokens per workgroup when the rank is small: 64 columns each, or 32
   // when that leaves too few workgroups to stream Q
   if (skinny_tn_whole(a.M, RP)) {
-    const bool wide = (a.N + 63) / 64 >= 128;
+    const bool wide = (a.N + 63) / 64 >= 128 && (!b || (b->N + 63) / 64 >= 128);
     const int nc = wide ? 64 : 32;
-    const dim3 gr((unsigned)((a.N + nc - 1) / nc)), bl(RP == 16 ? 1024 : 512);
-#define L_TNC(R)                                                                                 \
-  if (wide) hipLaunchKernelGGL((k_skinny_tn_cols<R, 64, R == 16 ? 16 : 8>), gr, bl, 0, st, a); \
-  else hipLaunchKernelGGL((k_skinny_tn_cols<R, 32, R == 16 ? 16 : 8>), gr, bl, 0, st, a);
+    const int nwg0 = (a.N + nc - 1) / nc, nwg1 = b ? (b->N + nc - 1) / nc : 0;
+    const TnArgs& a1 = b ? *b : a;
+    const dim3 gr((unsigned)(nwg0 + nwg1)), bl(RP == 16 ? 1024 : 512);
+#define L_TNC(R)                                                                                          \
+  if (wide) hipLaunchKernelGGL((k_skinny_tn_cols<R, 64, R == 16 ? 16 : 8>), gr, bl, 0, st, a, a1, nwg0, nwg1); \
+  else hipLaunchKernelGGL((k_skinny_tn_cols<R, 32, R == 16 ? 16 : 8>), gr, bl, 0, st, a, a1, nwg0, nwg1);
     switch (RP) {
       case 16: L_TNC(16) break;
       case 32: L_TNC(32) break;
@@ -748,12 +760,19 @@ hipError_t launch_skinny_tn(const TnArgs& a, int RP, hipStream_t st) {
 #undef L_TNC
     return hipGetLastError();
   }
-  const int nblocks = (a.N + 63) / 64;
-  const dim3 gr((unsigned)(nblocks * a.msplit)), bl(256);
-#define L_TN(R) hipLaunchKernelGGL(k_skinny_tn<R>, gr, bl, 0, st, a)
-  NF4K_RP_SWITCH(RP, L_TN)
+  for (const TnArgs* t : {&a, b}) {
+    if (!t) continue;
+    const int nblocks = (t->N + 63) / 64;
+    const dim3 gr((unsigned)(nblocks * t->msplit)), bl(256);
+#define L_TN(R) hipLaunchKernelGGL(k_skinny_tn<R>, gr, bl, 0, st, *t)
+    NF4K_RP_SWITCH(RP, L_TN)
 #undef L_TN
-  return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
+
+hipError_t launch_skinny_tn(const TnArgs& a, int RP, hipStream_t st) { return launch_skinny_tn2(a, nullptr, RP, st); }
 
 }  // namespace nf4k
