@@ -328,6 +328,23 @@ nf4_status nf4_layer_error(const float *W, int64_t rows, int64_t cols, int32_t b
                            size_t ws_bytes, void *stream);
 
 /*
+ * nf4_quantize and nf4_layer_error from one read of W: quantizes W into *q
+ * exactly as nf4_quantize does, and writes to err_dev the value that
+ * nf4_layer_error(W, q->rows, q->cols, 64, err_dq_group, q->codebook, ...)
+ * returns, bit for bit (AQLoRA section 3.1 ranks the layers by this error;
+ * the QLoRA blog's "1. NormalFloat" and "2. Double quantization" define the
+ * codes and scales).  One stage only: q->residual must be NULL.
+ *   err_dq_group: 0 (error with the plain block absmax as scale) or
+ *                 q->dq_group (with the double-quantized scales).
+ *   ws:           nf4_workspace_bytes(NF4_OP_ERROR, ...) bytes, 16-byte aligned.
+ * W, the buffers of *q, ws and err_dev must not overlap.
+ * Errors: NF4_ERR_NULL, _SHAPE, _ARG (residual set, err_dq_group not 0 or
+ * q->dq_group), _ALIGN, _ALIAS, _WORKSPACE, _HIP.
+ */
+nf4_status nf4_quantize_error(const float *W, const nf4_tensor *q, int32_t err_dq_group, double *err_dev,
+                              void *ws, size_t ws_bytes, void *stream);
+
+/*
  * The protected set of AQLoRA's precision allocation (section 3.2): indices
  * of the k largest of n errors (device double[n]), largest first, equal
  * errors ordered by lower index, written to device int32 idx_dev[k].

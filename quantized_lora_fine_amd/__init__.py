@@ -68,6 +68,7 @@ _SIGS = {
                      ctypes.c_int),
     "nf4_matmul": ([_T, _i32, _vp, _i64, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
     "nf4_layer_error": ([_vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "nf4_quantize_error": ([_vp, _T, _i32, _vp, _vp, _sz, _vp], ctypes.c_int),
     "nf4_codebook_values": ([_i32, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
     "nf4_topk": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
     "nf4_protect_count": ([_f64, _i32], _i32),
@@ -291,6 +292,22 @@ def layer_error(W: torch.Tensor, dq_group: int = 0, out: torch.Tensor | None = N
     _check(_lib.nf4_layer_error(_ptr(W), rows, cols, BLOCK, dq_group, CODEBOOKS[codebook], _ptr(err), _ptr(ws),
                                 ws.numel(), _stream()), "nf4_layer_error")
     return err
+
+
+def quantize_error(W: torch.Tensor, dq_group: int = 0, err_dq_group: int = 0, out: NF4Weight | None = None,
+                   err: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                   codebook: str = "nf4") -> tuple[NF4Weight, torch.Tensor]:
+    """nf4_quantize_error: (q, err) from one pass over W; q as quantize() gives it (one stage; `out`'s codebook
+    applies when given), err a cuda float64 [1] equal to layer_error(W, err_dq_group, codebook=q's)."""
+    assert W.dtype == torch.float32 and W.is_cuda and W.is_contiguous() and W.dim() == 2
+    rows, cols = W.shape
+    q = out if out is not None else NF4Weight(rows, cols, dq_group, W.device, codebook)
+    err = err if err is not None else torch.empty(1, dtype=torch.float64, device=W.device)
+    if ws is None:
+        ws = torch.empty(workspace_bytes(NF4_OP_ERROR, 0, rows, cols, 1), dtype=torch.uint8, device=W.device)
+    _check(_lib.nf4_quantize_error(_ptr(W), ctypes.byref(q.desc), err_dq_group, _ptr(err), _ptr(ws), ws.numel(),
+                                   _stream()), "nf4_quantize_error")
+    return q, err
 
 
 def matmul(q: NF4Weight, A: torch.Tensor, transpose: bool = False, A2: torch.Tensor | None = None,

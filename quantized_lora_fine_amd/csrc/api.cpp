@@ -623,6 +623,34 @@ nf4_status nf4_layer_error(const float* W, int64_t rows, int64_t cols, int32_t b
                                  (hipStream_t)stream));
 }
 
+nf4_status nf4_quantize_error(const float* W, const nf4_tensor* q, int32_t err_dq_group, double* err_dev, void* ws,
+                              size_t ws_bytes, void* stream) {
+  nf4_status st = check_tensor(q);
+  if (st != NF4_OK) return st;
+  if (q->residual) return NF4_ERR_ARG;
+  if (err_dq_group != 0 && err_dq_group != q->dq_group) return NF4_ERR_ARG;
+  if (!err_dev) return NF4_ERR_NULL;
+  const int64_t n = q->rows * q->cols;
+  if (n > 0 && !W) return NF4_ERR_NULL;
+  if (!ws) return NF4_ERR_WORKSPACE;
+  const size_t need = error_ws(q->rows, q->cols);
+  if (ws_bytes < need) return NF4_ERR_WORKSPACE;
+  if ((W && !aligned16(W)) || !aligned16(ws) || !aligned16(err_dev)) return NF4_ERR_ALIGN;
+  Range bufs[8];
+  tensor_ranges(q, bufs);
+  bufs[6] = rng(ws, need);
+  bufs[7] = rng(err_dev, 8);
+  const Range in = rng(W, (size_t)n * 4);
+  for (int i = 0; i < 8; ++i) {
+    if (overlap(in, bufs[i])) return NF4_ERR_ALIAS;
+    for (int j = i + 1; j < 8; ++j)
+      if (overlap(bufs[i], bufs[j])) return NF4_ERR_ALIAS;
+  }
+  return hip_status(launch_quantize_error(W, n / kBlock, q->dq_group != 0, q->codes, q->absmax, q->dq_scale,
+                                          err_dq_group != 0, (double*)ws, err_dev, codebook_enc(q->codebook),
+                                          codebook_consts(q->codebook), (hipStream_t)stream));
+}
+
 nf4_status nf4_topk(const double* err_dev, int32_t n, int32_t k, int32_t* idx_dev, void* stream) {
   if (n < 0 || k < 0 || k > n || n > 65536) return NF4_ERR_SHAPE;
   if (k == 0) return NF4_OK;

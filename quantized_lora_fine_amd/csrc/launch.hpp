@@ -17,6 +17,12 @@ hipError_t launch_quantize(const float* W, int64_t nblocks, bool dq, uint8_t* co
 hipError_t launch_dequantize(const uint8_t* codes, const void* absmax, const float* dqs, const uint8_t* codes2,
                              const void* absmax2, const float* dqs2, int64_t nweights, bool dq, bool bf16, void* out,
                              const NF4Consts& c, hipStream_t st);
+// nf4 quantize of one stage plus the reconstruction error of W (as launch_error
+// computes it) from the same read of W; err_dq: error with the double-quantized
+// scales (requires dq) rather than the plain block absmax.
+hipError_t launch_quantize_error(const float* W, int64_t nblocks, bool dq, uint8_t* codes, void* absmax, float* dqs,
+                                 bool err_dq, double* part, double* err, const NF4Enc& e, const NF4Consts& c,
+                                 hipStream_t st);
 hipError_t launch_error(const float* W, int64_t nblocks, bool dq, double* part, double* err, const NF4Enc& c,
                         hipStream_t st);
 hipError_t launch_topk(const double* e, int n, int k, int* idx, hipStream_t st);

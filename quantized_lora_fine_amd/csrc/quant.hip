@@ -120,9 +120,60 @@ struct QStage {
   float* dqs;
 };
 
-template <bool DQ, bool RES>
+// Squared reconstruction error and squared weight of one round (4 weights of
+// one block), added to the running sums: the decoded value fl32(table[c] * sc)
+// in fp32 as the format defines, differences and squares in fp64 (squares of
+// fp32 weights can leave the fp32 range).  The 4 squares are added pairwise
+// before joining the sums, rounds in order: the summation order of the
+// per-group partial sums is fixed.
+__device__ __forceinline__ void error_round(floatx4 v, uint32_t packed, float sc, const float* tab, double& dsum,
+                                            double& wsum) {
+  const float w4[4] = {v.x, v.y, v.z, v.w};
+  double d2[4], w2[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float wh = tab[(packed >> (4 * e)) & 15u] * sc;
+    const double wd = (double)w4[e];
+    const double d = wd - (double)wh;
+    d2[e] = d * d;
+    w2[e] = wd * wd;
+  }
+  dsum += (d2[0] + d2[1]) + (d2[2] + d2[3]);
+  wsum += (w2[0] + w2[1]) + (w2[2] + w2[3]);
+  // materialise the sums here: otherwise the compiler sinks every round's
+  // error arithmetic past the group-max barrier and keeps all 16 rounds live
+  asm volatile("" : "+v"(dsum), "+v"(wsum));
+}
+
+// One group's partial sums {sum (w - w_hat)^2, sum w^2} to part[2g], part[2g+1]:
+// xor tree inside each wave, then waves 0..3 in order.
+__device__ __forceinline__ void error_group_out(double dsum, double wsum, int lane, int wave, int tid, int64_t g,
+                                                double* __restrict__ part) {
+  __shared__ double redd[2][4];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    dsum += __shfl_xor(dsum, o);
+    wsum += __shfl_xor(wsum, o);
+  }
+  if (lane == 0) {
+    redd[0][wave] = dsum;
+    redd[1][wave] = wsum;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    part[2 * g + 0] = ((redd[0][0] + redd[0][1]) + redd[0][2]) + redd[0][3];
+    part[2 * g + 1] = ((redd[1][0] + redd[1][1]) + redd[1][2]) + redd[1][3];
+  }
+}
+
+// ERR: 0 = quantize only; 1 = also the reconstruction error with the plain
+// block absmax as scale; 2 = with the double-quantized scales (DQ only).  The
+// error's per-group partials (as k_error_partial writes them) go to `part`.
+template <bool DQ, bool RES, int ERR>
 __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, int64_t nblocks, QStage o1, QStage o2,
-                                                  NF4Enc enc, NF4Consts cst) {
+                                                  double* __restrict__ part, NF4Enc enc, NF4Consts cst) {
+  static_assert(ERR == 0 || !RES, "the error pass covers one stage");
+  static_assert(ERR != 2 || DQ, "the double-quantized error needs the group step");
   __shared__ EncEntry etab[kMaxBuckets];
   __shared__ float tab[16];
   const int tid = threadIdx.x;
@@ -135,7 +186,7 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
   const uint32_t nb = (uint32_t)min((int64_t)256, nblocks - gb0);  // blocks in this group
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(W + gb0 * 64, nb * 256);
   enc_to_lds<false>(enc, etab, tid);
-  if (RES && tid < 16) tab[tid] = cst.table[tid];
+  if ((RES || ERR) && tid < 16) tab[tid] = cst.table[tid];
 
   floatx4 v[16];
   load_group(wr, wave, sub, l16, v);
@@ -143,36 +194,58 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
 
   float amax[16];
   uint32_t packed[16];
+  double dsum = 0.0, wsum = 0.0;
+  // lane l16 of row `sub` owns the block of round l16: lb = wave*64 + 4*l16 + sub
+  const int mylb = wave * 64 + 4 * l16 + sub;
+  // (absmax bit patterns are non-negative integers: an integer max over the
+  // rounds, the others masked to 0, picks round l16's value bit for bit)
+  auto my_amax = [&]() -> float {
+    uint32_t mb = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mb = max(mb, (l16 == i) ? __builtin_bit_cast(uint32_t, amax[i]) : 0u);
+    return __builtin_bit_cast(float, mb);
+  };
+  // double-quantization step of the group, S = fl32(max absmax / 255): the 16
+  // rows of this lane's round, then lanes, then waves
+  auto group_step = [&](float mine) -> float {
+    float gm = mine;
+    gm = fmaxf(gm, __shfl_xor(gm, 1));
+    gm = fmaxf(gm, __shfl_xor(gm, 2));
+    gm = fmaxf(gm, __shfl_xor(gm, 4));
+    gm = fmaxf(gm, __shfl_xor(gm, 8));
+    return group_max(gm, lane, wave) / 255.0f;
+  };
   // one stage over v: codes, block scales and (DQ) the group's 8-bit scales;
   // returns the group step S (0 without double quantization)
   auto stage = [&](const QStage& o) -> float {
     const __amdgpu_buffer_rsrc_t cr = make_rsrc(o.codes + gb0 * 32, nb * 32);
+    float S = 0.f;
+    if constexpr (ERR == 2) {
+      // the error with 8-bit scales needs S before any round: block maxima first
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax[i] = block_absmax(v[i]);
+      S = group_step(my_amax());
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float m = block_absmax(v[i]);
+      // with the error, one round at a time keeps the fp64 temporaries short-lived
+      if constexpr (ERR != 0) __builtin_amdgcn_sched_barrier(0);
+      const float m = (ERR == 2) ? amax[i] : block_absmax(v[i]);
       amax[i] = m;
       packed[i] = encode4(v[i], block_enc(m), enc.bscale, enc.boffset, etab);
+      if constexpr (ERR == 1) error_round(v[i], packed[i], m, tab, dsum, wsum);
+      if constexpr (ERR == 2)
+        error_round(v[i], packed[i], (S > 0.f) ? fminf(255.f, rintf(m / S)) * S : 0.f, tab, dsum, wsum);
       const int lb = wave * 64 + 4 * i + sub;
       __builtin_amdgcn_raw_buffer_store_b16((unsigned short)packed[i], cr, lb * 32 + l16 * 2, 0, kNT);
     }
-    // lane l16 of row `sub` owns the block of round l16: lb = wave*64 + 4*l16 + sub
-    float mine = amax[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mine = (l16 == i) ? amax[i] : mine;
-    const int mylb = wave * 64 + 4 * l16 + sub;
+    const float mine = my_amax();
     if constexpr (!DQ) {
       const __amdgpu_buffer_rsrc_t ar = make_rsrc(o.absmax + gb0, nb * 4);
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, mine), ar, mylb * 4, 0, 0);
       return 0.f;
     } else {
-      // group max of 256 absmax values: the 16 rows of this lane's round, then lanes, then waves
-      float gm = mine;
-      gm = fmaxf(gm, __shfl_xor(gm, 1));
-      gm = fmaxf(gm, __shfl_xor(gm, 2));
-      gm = fmaxf(gm, __shfl_xor(gm, 4));
-      gm = fmaxf(gm, __shfl_xor(gm, 8));
-      gm = group_max(gm, lane, wave);
-      const float S = gm / 255.0f;
+      if constexpr (ERR != 2) S = group_step(mine);
       if (tid == 0) o.dqs[g] = S;
       const uint32_t q = (S > 0.f) ? (uint32_t)fminf(255.f, rintf(mine / S)) : 0u;
       const __amdgpu_buffer_rsrc_t qr = make_rsrc(o.c8 + gb0, nb);
@@ -181,6 +254,7 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
     }
   };
   const float S1 = stage(o1);
+  if constexpr (ERR != 0) error_group_out(dsum, wsum, lane, wave, tid, g, part);
   if constexpr (RES) {
     // residual of the first stage, in place: r = fl32(w - fl32(table[c] * a_hat))
 #pragma unroll
@@ -253,7 +327,6 @@ template <bool DQ>
 __global__ __launch_bounds__(256) void k_error_partial(const float* __restrict__ W, int64_t nblocks,
                                                        double* __restrict__ part, NF4Enc enc) {
   __shared__ EncEntry etab[kMaxBuckets];
-  __shared__ double redd[2][4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -310,21 +383,7 @@ __global__ __launch_bounds__(256) void k_error_partial(const float* __restrict__
     dsum += (d2[0] + d2[1]) + (d2[2] + d2[3]);
     wsum += (w2[0] + w2[1]) + (w2[2] + w2[3]);
   }
-  // fixed-order reduction: xor tree inside the wave, then waves 0..3 in order
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    dsum += __shfl_xor(dsum, o);
-    wsum += __shfl_xor(wsum, o);
-  }
-  if (lane == 0) {
-    redd[0][wave] = dsum;
-    redd[1][wave] = wsum;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    part[2 * g + 0] = ((redd[0][0] + redd[0][1]) + redd[0][2]) + redd[0][3];
-    part[2 * g + 1] = ((redd[1][0] + redd[1][1]) + redd[1][2]) + redd[1][3];
-  }
+  error_group_out(dsum, wsum, lane, wave, tid, g, part);
 }
 
 // stage 2: one workgroup sums the per-group partials in a fixed order.
@@ -332,10 +391,22 @@ __global__ __launch_bounds__(256) void k_error_final(const double* __restrict__ 
                                                      double* __restrict__ err) {
   __shared__ double sd[256], sw[256];
   const int tid = threadIdx.x;
+  // thread t adds groups t, t + 256, t + 512, ... in that order; the loads of
+  // four consecutive terms are issued together (a missing term adds +0.0,
+  // which leaves the non-negative sums unchanged)
   double d = 0.0, w = 0.0;
-  for (int64_t g = tid; g < ngroups; g += 256) {
-    d += part[2 * g];
-    w += part[2 * g + 1];
+  for (int64_t g0 = tid; g0 < ngroups; g0 += 1024) {
+    double2 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t g = g0 + 256 * u;
+      x[u] = (g < ngroups) ? ((const double2*)part)[g] : double2{0.0, 0.0};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      d += x[u].x;
+      w += x[u].y;
+    }
   }
   sd[tid] = d;
   sw[tid] = w;
@@ -386,13 +457,33 @@ hipError_t launch_quantize(const float* W, int64_t nblocks, bool dq, uint8_t* co
   QStage o1{codes, dq ? nullptr : (float*)absmax, dq ? (uint8_t*)absmax : nullptr, dqs};
   QStage o2{codes2, dq ? nullptr : (float*)absmax2, dq ? (uint8_t*)absmax2 : nullptr, dqs2};
   const dim3 gr((unsigned)ng), bl(256);
+  double* const np = nullptr;
   if (codes2) {
-    if (dq) hipLaunchKernelGGL((k_quantize<true, true>), gr, bl, 0, st, W, nblocks, o1, o2, e, c);
-    else hipLaunchKernelGGL((k_quantize<false, true>), gr, bl, 0, st, W, nblocks, o1, o2, e, c);
+    if (dq) hipLaunchKernelGGL((k_quantize<true, true, 0>), gr, bl, 0, st, W, nblocks, o1, o2, np, e, c);
+    else hipLaunchKernelGGL((k_quantize<false, true, 0>), gr, bl, 0, st, W, nblocks, o1, o2, np, e, c);
   } else {
-    if (dq) hipLaunchKernelGGL((k_quantize<true, false>), gr, bl, 0, st, W, nblocks, o1, o2, e, c);
-    else hipLaunchKernelGGL((k_quantize<false, false>), gr, bl, 0, st, W, nblocks, o1, o2, e, c);
+    if (dq) hipLaunchKernelGGL((k_quantize<true, false, 0>), gr, bl, 0, st, W, nblocks, o1, o2, np, e, c);
+    else hipLaunchKernelGGL((k_quantize<false, false, 0>), gr, bl, 0, st, W, nblocks, o1, o2, np, e, c);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_error(const float* W, int64_t nblocks, bool dq, uint8_t* codes, void* absmax, float* dqs,
+                                 bool err_dq, double* part, double* err, const NF4Enc& e, const NF4Consts& c,
+                                 hipStream_t st) {
+  const int64_t ng = (nblocks + 255) / 256;
+  if (err_dq && !dq) return hipErrorInvalidValue;
+  if (ng > 0) {
+    QStage o1{codes, dq ? nullptr : (float*)absmax, dq ? (uint8_t*)absmax : nullptr, dqs};
+    const QStage o2{nullptr, nullptr, nullptr, nullptr};
+    const dim3 gr((unsigned)ng), bl(256);
+    if (err_dq) hipLaunchKernelGGL((k_quantize<true, false, 2>), gr, bl, 0, st, W, nblocks, o1, o2, part, e, c);
+    else if (dq) hipLaunchKernelGGL((k_quantize<true, false, 1>), gr, bl, 0, st, W, nblocks, o1, o2, part, e, c);
+    else hipLaunchKernelGGL((k_quantize<false, false, 1>), gr, bl, 0, st, W, nblocks, o1, o2, part, e, c);
+    hipError_t r = hipGetLastError();
+    if (r != hipSuccess) return r;
+  }
+  hipLaunchKernelGGL(k_error_final, dim3(1), dim3(256), 0, st, part, ng, err);
   return hipGetLastError();
 }
 

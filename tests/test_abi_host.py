@@ -206,6 +206,33 @@ def test_error_and_topk_validation():
     assert lib.nf4_topk(v(C), 10, 0, None, None) == nf4.NF4_OK
 
 
+def test_quantize_error_validation():
+    v = ctypes.c_void_p
+
+    def call(d, W=C, edq=0, err=E, ws=D, wsb=1 << 20):
+        return lib.nf4_quantize_error(v(W), ctypes.byref(d) if d is not None else None, edq, v(err), v(ws), wsb,
+                                      None)
+
+    assert call(None) == nf4.NF4_ERR_NULL
+    assert call(desc(cols=100)) == nf4.NF4_ERR_SHAPE
+    assert call(desc(), edq=256) == nf4.NF4_ERR_ARG                      # no double quant to measure with
+    assert call(desc(dq=256, dqs=F), edq=128) == nf4.NF4_ERR_ARG
+    d = desc(rows=128, cols=128)
+    r = desc(rows=128, cols=128, codes=G, absmax=H)
+    d.residual = ctypes.pointer(r)
+    assert call(d) == nf4.NF4_ERR_ARG                                    # one stage only
+    assert call(desc(), err=0) == nf4.NF4_ERR_NULL
+    assert call(desc(), W=0) == nf4.NF4_ERR_NULL
+    assert call(desc(), ws=0, wsb=0) == nf4.NF4_ERR_WORKSPACE
+    assert call(desc(), wsb=8) == nf4.NF4_ERR_WORKSPACE
+    assert call(desc(), W=C + 4) == nf4.NF4_ERR_ALIGN
+    assert call(desc(), err=E + 8) == nf4.NF4_ERR_ALIGN
+    assert call(desc(), err=C + 16) == nf4.NF4_ERR_ALIAS                 # err inside W
+    assert call(desc(), ws=A) == nf4.NF4_ERR_ALIAS                       # workspace over the codes
+    assert call(desc(), err=D + 16) == nf4.NF4_ERR_ALIAS                 # err inside the workspace
+    assert call(desc(codes=C + 64)) == nf4.NF4_ERR_ALIAS
+
+
 def test_stack_validation():
     v = ctypes.c_void_p
     d = desc(rows=128, cols=128)

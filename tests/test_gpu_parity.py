@@ -157,6 +157,36 @@ def test_layer_error(dq):
     assert float(nf4.layer_error(dev(np.zeros((4, 128), np.float32)), dq).cpu()[0]) == 0.0
 
 
+@pytest.mark.parametrize("codebook", ["nf4", "int4", "fp4"])
+@pytest.mark.parametrize("dq,err_dq", [(0, 0), (256, 0), (256, 256)])
+def test_quantize_error_one_pass(codebook, dq, err_dq):
+    """nf4_quantize_error: codes and scales bit-exact against the oracle, and the error bit for bit what
+    nf4_layer_error returns (so within the same bound of the oracle's)."""
+    rng = np.random.default_rng(5)
+    cases = [synth.layer_inputs(synth.C1)["W"], edge_weights(codebook),
+             (rng.standard_t(4, (7, 64 * 37)) * 0.03).astype(np.float32),       # ragged last group
+             np.zeros((4, 128), np.float32)]
+    for W in cases:
+        say(f"  {codebook} dq={dq} err_dq={err_dq} shape={W.shape}")
+        Wd = dev(W)
+        q, err = nf4.quantize_error(Wd, dq, err_dq, codebook=codebook)
+        check_quant(q, oracle.quantize(W, 64, dq, codebook))
+        sep = nf4.layer_error(Wd, err_dq, codebook=codebook)
+        got, want_sep = float(err.cpu()[0]), float(sep.cpu()[0])
+        assert np.float64(got).view(np.uint64) == np.float64(want_sep).view(np.uint64), (got, want_sep)
+        want = oracle.layer_error(W, 64, err_dq, codebook)
+        assert abs(got - want) <= 1e-6 * want, (got, want)
+    # into an existing weight, twice in a row (the second call overwrites the first's outputs)
+    W1 = synth.layer_inputs(synth.C1)["W"]
+    W2 = (rng.standard_normal(W1.shape) * 0.05).astype(np.float32)
+    q = nf4.NF4Weight(W1.shape[0], W1.shape[1], dq, DEV, codebook)
+    for W in (W1, W2):
+        _, err = nf4.quantize_error(dev(W), out=q, err_dq_group=err_dq)
+        check_quant(q, oracle.quantize(W, 64, dq, codebook))
+        assert abs(float(err.cpu()[0]) - oracle.layer_error(W, 64, err_dq, codebook)) <= \
+            1e-6 * oracle.layer_error(W, 64, err_dq, codebook)
+
+
 def test_topk():
     rng = np.random.default_rng(5)
     for n, k in ((280, 8), (144, 29), (1000, 1000), (5, 1), (3000, 17)):
@@ -296,6 +326,12 @@ def test_layer_c2_full():
     say("c2 4096x4096 r=16 M=2048, double quant")
     d = synth.layer_inputs(synth.C2)
     check_layer(d, d["s"], d["dq_group"])
+    # the step's one-pass quantize + error at this size (codes with 8-bit scales, error with plain absmax)
+    q, err = nf4.quantize_error(dev(d["W"]), d["dq_group"], 0)
+    check_quant(q, oracle.quantize(d["W"], 64, d["dq_group"]))
+    got, want = float(err.cpu()[0]), oracle.layer_error(d["W"], 64, 0)
+    say(f"  one-pass error {got:.12g} oracle {want:.12g}")
+    assert abs(got - want) <= 1e-6 * want
 
 
 # ---------------------------------------------------------------------------
