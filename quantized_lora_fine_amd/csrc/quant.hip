@@ -427,6 +427,22 @@ __global__ __launch_bounds__(256) void k_error_final(const double* __restrict__ 
 __global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ e, int n, int k,
                                                int* __restrict__ idx) {
   __shared__ double tile[1024];
+  if (n <= 1024) {
+    // one tile: every error is read from global memory once
+    const int i = threadIdx.x;
+    if (i < n) tile[i] = e[i];
+    __syncthreads();
+    if (i < n) {
+      const double ei = tile[i];
+      int rank = 0;
+      for (int j = 0; j < n; ++j) {
+        const double ej = tile[j];
+        rank += (ej > ei || (ej == ei && j < i)) ? 1 : 0;
+      }
+      if (rank < k) idx[rank] = i;
+    }
+    return;
+  }
   for (int base = 0; base < n; base += 1024) {
     const int i = base + threadIdx.x;
     const double ei = (i < n) ? e[i] : 0.0;

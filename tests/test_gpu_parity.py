@@ -189,7 +189,7 @@ def test_quantize_error_one_pass(codebook, dq, err_dq):
 
 def test_topk():
     rng = np.random.default_rng(5)
-    for n, k in ((280, 8), (144, 29), (1000, 1000), (5, 1), (3000, 17)):
+    for n, k in ((280, 8), (144, 29), (1000, 1000), (5, 1), (3000, 17), (1, 1), (1024, 5), (1025, 3)):
         e = rng.integers(0, 40, n).astype(np.float64) / 13.0
         got = nf4.topk(dev(e), k).cpu().numpy().tolist()
         assert got == oracle.topk(e, k), (n, k)
