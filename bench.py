@@ -77,6 +77,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--power-probe", action="store_true",
+                    help="c2: also sample socket power and the shader clock (amd-smi, rocm-smi in a child "
+                         "process) while the forward GEMM runs back to back, and while a spin kernel runs")
     ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c5", "c4-stack"],
                     help="c2: the 4096x4096 layer (default); c3: the three 7B-shaped MLP linears; c5: the "
                          "70B-shaped up projection; c4-stack: the 280-linear 14B-shaped stack with AQLoRA's "
@@ -274,6 +277,11 @@ def main():
     roofline = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
 
+    power = None
+    if args.power_probe:
+        power = {"fwd_gemm_back_to_back": power_probe(lambda: nf4.matmul(q, X, False, A2f, B2f, out=Cf), torch),
+                 "spin_kernel": power_probe(lambda: torch.cuda._sleep(100000), torch)}
+
     if args.calib_copy:
         src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -304,7 +312,43 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if power is not None:
+        out["power_probe"] = power
     print(json.dumps(out), flush=True)
+
+
+def power_probe(fn, torch, secs: float = 8.0):
+    """Launch `fn` back to back for `secs` seconds; halfway through, read the
+    socket power (amd-smi) and the shader clock (rocm-smi) from a child process.
+    Returns the readings and the mean time per launch (None for a reading the
+    tools do not report)."""
+    import re
+    import subprocess
+    t0 = time.perf_counter()
+    proc, n = None, 0
+    while time.perf_counter() - t0 < secs:
+        for _ in range(50):
+            fn()
+        torch.cuda.synchronize()
+        n += 50
+        if proc is None and time.perf_counter() - t0 > secs / 2:
+            try:
+                proc = subprocess.Popen(["sh", "-c", "amd-smi metric -p; rocm-smi --showclocks"],
+                                        stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+            except OSError:
+                proc = False
+    elapsed = time.perf_counter() - t0
+    text = ""
+    if proc:
+        try:
+            text = proc.communicate(timeout=60)[0]
+        except subprocess.TimeoutExpired:
+            proc.kill()
+            text = proc.communicate()[0]
+    pw = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", text)
+    sc = re.search(r"sclk clock level:[^(]*\((\d+)\s*Mhz\)", text)
+    return {"socket_power_w": float(pw.group(1)) if pw else None, "sclk_mhz": int(sc.group(1)) if sc else None,
+            "us_per_launch": round(1e6 * elapsed / max(n, 1), 2), "launches": n}
 
 
 def bench_layers(args):
