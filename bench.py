@@ -176,57 +176,36 @@ def main():
     B2b[:, :r] = L1
     Cf = torch.empty(M, o, dtype=torch.bfloat16, device=dev)
     Cb = torch.empty(M, h, dtype=torch.bfloat16, device=dev)
-    kernels = {}
-    for name, fn, flops in (
-        ("nf4_gemm_fwd", lambda: nf4.matmul(q, X, False, A2f, B2f, out=Cf), 2.0 * M * h * o + 2.0 * M * r * o),
-        ("nf4_gemm_dx", lambda: nf4.matmul(q, dY, True, A2b, B2b, out=Cb), 2.0 * M * h * o + 2.0 * M * r * h),
-    ):
-        for _ in range(args.warmup):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = 1e3 * e0.elapsed_time(e1) / args.steps
-        kernels[name] = {"us": round(us, 3), "tflops": round(flops / (us * 1e-6) / 1e12, 1),
-                         "flops_per_launch": flops}
-    # HBM-bound passes: algorithmic bytes per launch
+    # Standalone kernel timings: 7 interleaved repetitions across these ops, each a
+    # window of `steps` back-to-back launches between HIP events on the launch
+    # stream; `us` is the mean of the fastest half, with the median and range.
     n = o * h
     q_bytes = 4 * n + n // 2 + n // 64 + 4 * (n // 64 // 256)
     e_bytes = 4 * n
-    kernels["quantize_error_dq"] = {"us": round(1e3 * op_ms["quantize+error"], 3),
-                                    "GBps": round(q_bytes / (op_ms["quantize+error"] * 1e-3) / 1e9, 1),
-                                    "bytes": q_bytes}
-    # the two passes on their own (each reads W once)
-    for name, fn, nbytes in (("quantize_dq", lambda: nf4.quantize(W, 256, out=q), q_bytes),
-                             ("layer_error", lambda: nf4.layer_error(W, 0, out=err, ws=ws_e), e_bytes)):
-        for _ in range(args.warmup):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = 1e3 * e0.elapsed_time(e1) / args.steps
-        kernels[name] = {"us": round(us, 3), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes": nbytes}
-
-    # merge after training (not part of the step): NF4 base -> bf16, fp32 base -> bf16
     Wm = torch.empty(o, h, dtype=torch.bfloat16, device=dev)
-    for name, src, nbytes in (("merge_nf4_to_bf16", q, n // 2 + n // 64 + 4 * (n // 64 // 256) + 2 * n),
-                              ("merge_fp32_to_bf16", W, 6 * n)):
-        for _ in range(args.warmup):
-            nf4.merge(src, L1, L2, s, bf16=True, out=Wm)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            nf4.merge(src, L1, L2, s, bf16=True, out=Wm)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = 1e3 * e0.elapsed_time(e1) / args.steps
-        kernels[name] = {"us": round(us, 3), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes": nbytes}
+    work = {
+        "nf4_gemm_fwd": (lambda: nf4.matmul(q, X, False, A2f, B2f, out=Cf), "flops", 2.0 * M * h * o + 2.0 * M * r * o),
+        "nf4_gemm_dx": (lambda: nf4.matmul(q, dY, True, A2b, B2b, out=Cb), "flops", 2.0 * M * h * o + 2.0 * M * r * h),
+        "quantize_error_dq": (lambda: nf4.quantize_error(W, 256, 0, out=q, err=err, ws=ws_e), "bytes", q_bytes),
+        # the two passes on their own (each reads W once)
+        "quantize_dq": (lambda: nf4.quantize(W, 256, out=q), "bytes", q_bytes),
+        "layer_error": (lambda: nf4.layer_error(W, 0, out=err, ws=ws_e), "bytes", e_bytes),
+        # merge after training (not part of the step): NF4 base -> bf16, fp32 base -> bf16
+        "merge_nf4_to_bf16": (lambda: nf4.merge(q, L1, L2, s, bf16=True, out=Wm), "bytes",
+                              n // 2 + n // 64 + 4 * (n // 64 // 256) + 2 * n),
+        "merge_fp32_to_bf16": (lambda: nf4.merge(W, L1, L2, s, bf16=True, out=Wm), "bytes", 6 * n),
+    }
+    stats = interleaved_times({k: v[0] for k, v in work.items()}, args.steps, 7, stream, torch)
+    kernels = {}
+    for name, (_, kind, amount) in work.items():
+        st = stats[name]
+        kernels[name] = dict(st)
+        if kind == "flops":
+            kernels[name].update(tflops=round(amount / (st["us"] * 1e-6) / 1e12, 1), flops_per_launch=amount)
+        else:
+            kernels[name].update(GBps=round(amount / (st["us"] * 1e-6) / 1e9, 1), bytes=amount)
+    kernels["timing"] = (f"7 interleaved repetitions of {args.steps} back-to-back launches per op (HIP events on "
+                         f"the launch stream); us = mean of the fastest half")
 
     # the same weights at identical storage in the other 4-bit codebooks: reconstruction error and quantize time
     codebooks = {}
@@ -315,6 +294,33 @@ def main():
     if power is not None:
         out["power_probe"] = power
     print(json.dumps(out), flush=True)
+
+
+def interleaved_times(fns, calls, reps, stream, torch):
+    """Per-launch time of each op in `fns`: `reps` rounds, each timing every op
+    in turn over `calls` back-to-back launches (after 2 untimed ones) with HIP
+    events on `stream`.  Returns, per op, the mean of the fastest half of the
+    rounds (`us`), their median and their range, in microseconds."""
+    import statistics
+    times = {k: [] for k in fns}
+    for _ in range(reps):
+        for name, fn in fns.items():
+            for _ in range(2):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(calls):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[name].append(1e3 * e0.elapsed_time(e1) / calls)
+    out = {}
+    for name, t in times.items():
+        t = sorted(t)
+        fast = t[:(len(t) + 1) // 2]
+        out[name] = {"us": round(sum(fast) / len(fast), 3), "median_us": round(statistics.median(t), 3),
+                     "min_us": round(t[0], 3), "max_us": round(t[-1], 3)}
+    return out
 
 
 def power_probe(fn, torch, secs: float = 8.0):
