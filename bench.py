@@ -300,7 +300,9 @@ def interleaved_times(fns, calls, reps, stream, torch):
     """Per-launch time of each op in `fns`: `reps` rounds, each timing every op
     in turn over `calls` back-to-back launches (after 2 untimed ones) with HIP
     events on `stream`.  Returns, per op, the mean of the fastest half of the
-    rounds (`us`), their median and their range, in microseconds."""
+    rounds (`us`), their median and their range, in microseconds.  Seven
+    interleaved runs and the fastest half follow the timing protocol of the
+    AQLoRA page (section 4, "Timing protocol")."""
     import statistics
     times = {k: [] for k in fns}
     for _ in range(reps):
