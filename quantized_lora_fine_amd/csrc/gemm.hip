@@ -39,6 +39,10 @@
 //     that the 16-byte MFMA fragment reads are bank-conflict free.
 //   * Workgroup ids are remapped so the tiles that run together on one XCD
 //     share the same rows of A (its L2 keeps that panel).
+//   * The adapter columns (R <= 64) are multiplied first: each consumer wave
+//     loads its tail fragments straight into registers while the producers
+//     dequantize the first tiles.  The bf16 result tile goes through LDS so
+//     that every wave stores whole 128-byte lines.
 #include <type_traits>
 
 #include "common.hpp"
@@ -153,6 +157,105 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
     const int nb = wn * 64 + ni * 32 + 16 * (g & 1);
     b_off[ni] = (uint32_t)(lds_off_kn(8 * (g >> 1) + e, (nb >> 3) + (q >> 1)) + 8 * (q & 1));
   }
+  // ---- adapter tail: R extra K columns from A2 [M][R] and B2 ([N][R], or [R][N]
+  // when b2kn > 0), in chunks of at most 64: each thread loads 4 A2 pieces and
+  // 2 B2 pieces of 16 bytes, stores them in the A / B tile layouts, and the
+  // consumer waves multiply them like a K step (R > 64, after the main loop).
+  // With R <= 64 each consumer wave instead loads its own MFMA fragments straight
+  // into registers during the prologue (tail_frags) and multiplies them while the
+  // producers dequantize the first tiles.
+  const int tail_nrows = (N - n0) < GBN ? (N - n0) : GBN;
+  const __amdgpu_buffer_rsrc_t a2r = make_rsrc(p.A2 + m0 * p.R, (uint32_t)(arows * p.R * 2));
+  const __amdgpu_buffer_rsrc_t b2r = p.b2kn ? make_rsrc(p.B2, (uint32_t)((int64_t)p.b2kn * N * 2))
+                                            : make_rsrc(p.B2 + (int64_t)n0 * p.R, (uint32_t)(tail_nrows * p.R * 2));
+  auto tail_load = [&](int c0, u32x4 (&ta)[4], u32x4 (&tb)[2]) {
+    const int width = min(GBK, p.R - c0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (tid >> 3) + 64 * i;
+      const int kc = tid & 7;
+      const uint32_t off = kc * 8 < width ? (uint32_t)((r * p.R + c0 + kc * 8) * 2) : kOOB;
+      ta[i] = __builtin_amdgcn_raw_buffer_load_b128(a2r, off, 0, 0);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      uint32_t off;
+      if (p.b2kn) {
+        // k-major B2: 64 tail rows x 128 columns into the [k][n] layout
+        const int e = tid + 512 * jj;
+        const int kr = e >> 4, slot = e & 15;
+        const bool ok = kr < width && n0 + slot * 8 < N;
+        off = ok ? (uint32_t)(((int64_t)(c0 + kr) * N + n0 + slot * 8) * 2) : kOOB;
+      } else {
+        const int r = tid >> 2;
+        const int kc = (tid & 3) * 2 + jj;
+        off = kc * 8 < width ? (uint32_t)((r * p.R + c0 + kc * 8) * 2) : kOOB;
+      }
+      tb[jj] = __builtin_amdgcn_raw_buffer_load_b128(b2r, off, 0, 0);
+    }
+  };
+  auto tail_store = [&](uint8_t* Ab, uint8_t* Bb, const u32x4 (&ta)[4], const u32x4 (&tb)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(u32x4*)(Ab + lds_off((tid >> 3) + 64 * i, tid & 7)) = ta[i];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      if (p.b2kn) {
+        const int e = tid + 512 * jj;
+        *(u32x4*)(Bb + lds_off_kn(e >> 4, e & 15)) = tb[jj];
+      } else {
+        *(u32x4*)(Bb + lds_off(tid >> 2, (tid & 3) * 2 + jj)) = tb[jj];
+      }
+    }
+  };
+  // fragments of K16 group kk of the tail for this consumer wave: A2 rows
+  // wm*128 + mi*32 + lane%32 and B2 rows (or k-major columns) wn*64 + ni*32 + lane%32,
+  // 8 consecutive k from 8*(2*kk + lane/32); rows past M or the tile read zero
+  // through the ranges, columns past N are never stored
+  auto tail_frags = [&](int kk, bf16x8 (&fa)[4], bf16x8 (&fb)[2]) {
+    const int k0 = 16 * kk + 8 * (lane >> 5);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int row = wm * 128 + mi * 32 + (lane & 31);
+      fa[mi] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(a2r, (uint32_t)((row * p.R + k0) * 2), 0, 0));
+    }
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      if (p.b2kn) {
+        const uint32_t n = (uint32_t)(n0 + wn * 64 + ni * 32 + (lane & 31));
+        u32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(b2r, ((uint32_t)(k0 + 2 * j) * (uint32_t)N + n) * 2, 0, 0);
+          const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(b2r, ((uint32_t)(k0 + 2 * j + 1) * (uint32_t)N + n) * 2, 0, 0);
+          v[j] = lo | (hi << 16);
+        }
+        fb[ni] = __builtin_bit_cast(bf16x8, v);
+      } else {
+        const int row = wn * 64 + ni * 32 + (lane & 31);
+        fb[ni] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(b2r, (uint32_t)((row * p.R + k0) * 2), 0, 0));
+      }
+    }
+  };
+  auto tail_mma = [&](const uint8_t* Ab, const uint8_t* Bb, int width) {
+    for (int kk = 0; kk < (width >> 4); ++kk) {
+      const int chunk = kk * 2 + (lane >> 5);
+      bf16x8 fa[4], fb[2];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) fa[mi] = *(const bf16x8*)(Ab + lds_off(wm * 128 + mi * 32 + (lane & 31), chunk));
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        if (p.b2kn) fb[ni] = lds_tr8(const_cast<uint8_t*>(Bb) + kk * 4096 + b_off[ni], 256);
+        else fb[ni] = *(const bf16x8*)(Bb + lds_off(wn * 64 + ni * 32 + (lane & 31), chunk));
+      }
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ni], fa[mi], acc[mi][ni], 0, 0, 0);
+    }
+  };
+  const bool early_tail = p.R > 0 && p.R <= GBK;
+
   if (producer) {
     // ================= producer waves =================
     const int pw = wave - 4;
@@ -401,7 +504,24 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
       if constexpr (kReads < 8) __builtin_amdgcn_sched_group_barrier(0x008, 8 - kReads, 0);
     };
     Frags f0, f1;
-    __syncthreads();  // (1)
+    {
+      // the adapter tail (R <= 64): group 0's loads go out before barrier (1),
+      // its MFMAs (and the later groups') run before barrier (2)
+      bf16x8 tfa[4], tfb[2];
+      if (early_tail) tail_frags(0, tfa, tfb);
+      __syncthreads();  // (1)
+      if (early_tail) {
+        for (int kk = 0;;) {
+#pragma unroll
+          for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfb[ni], tfa[mi], acc[mi][ni], 0, 0, 0);
+          if (++kk >= (p.R >> 4)) break;
+          tail_frags(kk, tfa, tfb);
+        }
+      }
+    }
     __syncthreads();  // (2)
     load_frags(0, 0, f0);
     // step s: tile s (buffer s%3) is published and f0 holds its first K16
@@ -440,88 +560,51 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
   }
   __syncthreads();
 
-  // ---- adapter tail: R extra K columns from A2 [M][R] and B2 [N][R] (loads by all waves) ----
-  if (p.R > 0) {
-    const __amdgpu_buffer_rsrc_t a2 = make_rsrc(p.A2 + m0 * p.R, (uint32_t)(arows * p.R * 2));
-    const int nrows = (N - n0) < GBN ? (N - n0) : GBN;
-    const __amdgpu_buffer_rsrc_t b2 =
-        p.b2kn ? make_rsrc(p.B2, (uint32_t)((int64_t)p.b2kn * N * 2))
-               : make_rsrc(p.B2 + (int64_t)n0 * p.R, (uint32_t)(nrows * p.R * 2));
+  // ---- adapter tail for R > 64: chunks through buffers 0 after the main loop ----
+  if (p.R > 0 && !early_tail) {
     for (int c0 = 0; c0 < p.R; c0 += GBK) {
-      const int width = min(GBK, p.R - c0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = (tid >> 3) + 64 * i;
-        const int kc = tid & 7;
-        const uint32_t off = kc * 8 < width ? (uint32_t)((r * p.R + c0 + kc * 8) * 2) : kOOB;
-        *(u32x4*)(As0 + lds_off(r, kc)) = __builtin_amdgcn_raw_buffer_load_b128(a2, off, 0, 0);
-      }
-      if (p.b2kn) {
-        // k-major B2: 64 tail rows x 128 columns into the [k][n] layout
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int e = tid + 512 * jj;
-          const int kr = e >> 4, slot = e & 15;
-          const bool ok = kr < width && n0 + slot * 8 < N;
-          const uint32_t off = ok ? (uint32_t)(((int64_t)(c0 + kr) * N + n0 + slot * 8) * 2) : kOOB;
-          *(u32x4*)(Bs0 + lds_off_kn(kr, slot)) = __builtin_amdgcn_raw_buffer_load_b128(b2, off, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int r = tid >> 2;
-          const int kc = (tid & 3) * 2 + jj;
-          const uint32_t off = kc * 8 < width ? (uint32_t)((r * p.R + c0 + kc * 8) * 2) : kOOB;
-          *(u32x4*)(Bs0 + lds_off(r, kc)) = __builtin_amdgcn_raw_buffer_load_b128(b2, off, 0, 0);
-        }
-      }
+      u32x4 xa[4], xb[2];
+      tail_load(c0, xa, xb);
+      tail_store(As0, Bs0, xa, xb);
       __syncthreads();
-      if (!producer) {
-        for (int kk = 0; kk < (width >> 4); ++kk) {
-          const int chunk = kk * 2 + (lane >> 5);
-          bf16x8 fa[4], fb[2];
-#pragma unroll
-          for (int mi = 0; mi < 4; ++mi)
-            fa[mi] = *(const bf16x8*)(As0 + lds_off(wm * 128 + mi * 32 + (lane & 31), chunk));
-#pragma unroll
-          for (int ni = 0; ni < 2; ++ni) {
-            if (p.b2kn) {
-              fb[ni] = lds_tr8(Bs0 + kk * 4096 + b_off[ni], 256);
-            } else {
-              fb[ni] = *(const bf16x8*)(Bs0 + lds_off(wn * 64 + ni * 32 + (lane & 31), chunk));
-            }
-          }
-#pragma unroll
-          for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ni], fa[mi], acc[mi][ni], 0, 0, 0);
-        }
-      }
+      if (!producer) tail_mma(As0, Bs0, min(GBK, p.R - c0));
       __syncthreads();
     }
   }
 
-  // ---- epilogue (consumers): D[n][m]; lane holds m = l%32, n = 8*(v/4) + 4*(l/32) + v%4 ----
+  // ---- epilogue: D[n][m], lane holds m = l%32, n = 8*(v/4) + 4*(l/32) + v%4.  The
+  // consumers write the bf16 tile to LDS (A buffer 0: rows 0..127, buffer 1: rows
+  // 128..255; 256-byte rows whose 16-byte chunks are XOR-swizzled by row % 16),
+  // then all waves store it as contiguous 16-byte pieces, 4 rows per wave store. ----
   if (!producer) {
+    uint8_t* stg = wm == 0 ? As0 : As1;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
-      const int64_t m = m0 + wm * 128 + mi * 32 + (lane & 31);
-      if (m < M) {
+      const int row = mi * 32 + (lane & 31);
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
+      for (int ni = 0; ni < 2; ++ni) {
 #pragma unroll
-          for (int gg = 0; gg < 4; ++gg) {
-            const int n = n0 + wn * 64 + ni * 32 + 8 * gg + 4 * (lane >> 5);
-            if (n < N) {
-              uint2 o;
-              o.x = pack_bf16x2(acc[mi][ni][4 * gg + 0], acc[mi][ni][4 * gg + 1]);
-              o.y = pack_bf16x2(acc[mi][ni][4 * gg + 2], acc[mi][ni][4 * gg + 3]);
-              *(uint2*)(p.C + m * N + n) = o;
-            }
-          }
+        for (int gg = 0; gg < 4; ++gg) {
+          const int col = wn * 64 + ni * 32 + 8 * gg + 4 * (lane >> 5);
+          uint2 o;
+          o.x = pack_bf16x2(acc[mi][ni][4 * gg + 0], acc[mi][ni][4 * gg + 1]);
+          o.y = pack_bf16x2(acc[mi][ni][4 * gg + 2], acc[mi][ni][4 * gg + 3]);
+          *(uint2*)(stg + row * 256 + (((col >> 3) ^ (row & 15)) << 4) + ((col >> 2) & 1) * 8) = o;
         }
       }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int e = tid + 512 * it;
+    const int row = e >> 4, piece = e & 15;
+    const int64_t m = m0 + row;
+    const int n = n0 + piece * 8;
+    if (m < M && n < N) {
+      const int r = row & 127;
+      const uint8_t* stg = row < 128 ? As0 : As1;
+      *(u32x4*)(p.C + m * N + n) = *(const u32x4*)(stg + r * 256 + ((piece ^ (r & 15)) << 4));
     }
   }
 }
