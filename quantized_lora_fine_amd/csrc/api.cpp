@@ -419,11 +419,12 @@ nf4_status layer_bwd(const WSrc& W, const uint16_t* X, const uint16_t* dY, int64
   // dL2 = s T^T dY  ([r][o]),  dL1 = X^T G  (stored [h][r])
   TnArgs t2{tsrc, ldt, r, dY, M, (int)o, p.ms2, p.mr2, p2, cnt + p.cnt_2, s, 0, dL2};
   TnArgs t1{g, p.RP, r, X, M, (int)h, p.ms1, p.mr1, p1, cnt + p.cnt_1, 1.0f, 1, dL1};
-  NF4_TRY(launch_skinny_tn2(t2, &t1, p.RP, hs));
-  // dX = dY w_hat + G L1^T
+  // dX = dY w_hat + G L1^T, before the TN products: it reads dY right after G's
+  // product has brought it into the caches, and the TN products then find dY there
   if (dX) {
     NF4_TRY(gemm(MODE_DX, W, dY, g, l1b, p.RP, 0, dX, M, hs));
   }
+  NF4_TRY(launch_skinny_tn2(t2, &t1, p.RP, hs));
   return NF4_OK;
 }
 

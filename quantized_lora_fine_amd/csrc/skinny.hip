@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void k_skinny_nt(NtArgs p) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (kv && aval[a]) v = __builtin_nontemporal_load((const u32x4*)(arow[a] + k + kq));
+        if (kv && aval[a]) v = *(const u32x4*)(arow[a] + k + kq);
         af[u][a] = __builtin_bit_cast(bf16x8, v);
       }
 #pragma unroll
@@ -273,7 +273,9 @@ __global__ __launch_bounds__(1024) void k_skinny_nt_rows(NtArgs p) {
 #pragma unroll
       for (int a = 0; a < FRA; ++a) {
         u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (kv && aval[a]) v = __builtin_nontemporal_load((const u32x4*)(arow[a] + k + kq));
+        // ordinary (cacheable) loads: the fused GEMM that follows reads the same
+        // rows of X or dY, and streaming loads would push them out of the caches
+        if (kv && aval[a]) v = *(const u32x4*)(arow[a] + k + kq);
         af[u][a] = __builtin_bit_cast(bf16x8, v);
       }
       if constexpr (BKN) {
@@ -391,7 +393,7 @@ __global__ __launch_bounds__(256) void k_skinny_tn(TnArgs p) {
       const int row = (tid >> 3) + 32 * i;
       const int col = n0 + (tid & 7) * 8;
       u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (m + row < m_hi && col < N) v = __builtin_nontemporal_load((const u32x4*)(p.Q + (m + row) * N + col));
+      if (m + row < m_hi && col < N) v = *(const u32x4*)(p.Q + (m + row) * N + col);
       qreg[i] = v;
     }
 #pragma unroll
@@ -539,7 +541,8 @@ __device__ __forceinline__ void tn_cols_band(const TnArgs& p, int bid, int nwg, 
     for (int i = 0; i < QL; ++i) {
       const int64_t m = m0 + QTL * i + lane / QPR;
       u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (c < nchunk && m < M && qok) v = __builtin_nontemporal_load((const u32x4*)(p.Q + m * N + qcol));
+      // ordinary (cacheable) loads, as in the NT products: Q is X or dY
+      if (c < nchunk && m < M && qok) v = *(const u32x4*)(p.Q + m * N + qcol);
       qr[slot][i] = v;
     }
 #pragma unroll
