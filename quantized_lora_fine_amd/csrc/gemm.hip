@@ -3,7 +3,8 @@
 //   C[M][N] = A[M][K] * B[N][K]^T  +  A2[M][R] * B2[N][R]^T      (fp32 accumulate)
 //
 // Forward  (MODE_FWD): A = X [M][h], B = w_hat(W_st) with W_st [o][h]
-//                      (N = o, K = h), tail A2 = s*T [M][R], B2 = L2^T [o][R].
+//                      (N = o, K = h), tail A2 = s*T [M][R], B2 = L2^T [o][R]
+//                      or L2 as stored, [R][o] (b2kn > 0).
 // Input grad (MODE_DX): A = dY [M][o], B = w_hat(W_st)^T (N = h, K = o),
 //                      tail A2 = G [M][R], B2 = L1 [h][R].
 //
