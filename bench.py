@@ -35,10 +35,16 @@ GEMM_SOURCES = ["quantized_lora_fine_amd/csrc/gemm.hip", "quantized_lora_fine_am
 
 
 def kernel_source_hash() -> str:
+    """Hash of the fused GEMM's code (comments, trailing spaces and blank lines
+    left out, so an edit to comments alone keeps the stored counters valid)."""
+    import re
     h = hashlib.sha256()
     for p in GEMM_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            for line in f:
+                code = re.sub(r"//.*", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
