@@ -42,16 +42,4 @@ __device__ __forceinline__ bf16x8 lds_tr8(uint8_t* lo, int row_bytes) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Max over the 16 lanes of a DPP row (lanes 16k .. 16k+15) of non-negative
-// fp32 values given as bit patterns (for which unsigned order is float order);
-// every lane of the row receives the result.  bound_ctrl reads 0 (the
-// identity) outside the row, and each step fuses into one v_max_u32_dpp.
-__device__ __forceinline__ uint32_t row16_max_bits(uint32_t x) {
-  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
-  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
-  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, true));  // row_half_mirror
-  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, true));  // row_mirror
-  return x;
-}
-
 }  // namespace nf4k

@@ -3,11 +3,13 @@
 // The weight is a row-major fp32 [rows][cols] array with cols % 64 == 0, so
 // block b is the 64 consecutive floats starting at element 64*b and no block
 // crosses a row.  One workgroup (256 threads, 4 wave64s) owns one group of 256
-// consecutive blocks (16,384 weights): each wave streams 64 blocks in 16
-// rounds; in a round the 16 lanes of a DPP row read one block as 16 x float4
-// (the wave reads 1 KiB contiguous), so loads are fully coalesced, the block
-// absmax is a 4-step DPP max inside the row, and the double-quantization
-// group max needs no second pass over HBM.
+// consecutive blocks (16,384 weights): each wave streams 64 blocks in 8
+// rounds of 8 blocks; in a round the 8 lanes of a half DPP row hold one block,
+// two float4 each (elements 4l..4l+3 and 32+4l..32+4l+3 of lane l), so each of
+// the round's two loads reads whole 128-byte lines, the block absmax is a
+// 3-step DPP max inside the half row, the per-block setup is paid once per 8
+// weights of a lane, and the double-quantization group max needs no second
+// pass over HBM.
 //
 // Format ("QLoRA: How to fine-tune large language models with less memory",
 // sections "1. NormalFloat" and "2. Double quantization"): 4-bit codes, two
@@ -28,14 +30,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcFlags);
 }
 
-// The 16 rounds of one wave: round i covers blocks lb = wave*64 + 4i + sub of
-// the group (sub = lane/16), lane l16 of the DPP row holding elements
-// 4*l16 .. 4*l16+3.  Reads past the group's last block return zero.
-__device__ __forceinline__ void load_group(__amdgpu_buffer_rsrc_t wr, int wave, int sub, int l16, floatx4 v[16]) {
+// The 8 rounds of one wave: round i covers blocks lb = wave*64 + 8i + sub of
+// the group (sub = lane/8); lane l8 = lane%8 holds quads l8 and 8 + l8 of its
+// block (elements 4*l8 .. +3 in v[i][0], 32 + 4*l8 .. +3 in v[i][1]).  Reads
+// past the group's last block return zero.
+__device__ __forceinline__ void load_group(__amdgpu_buffer_rsrc_t wr, int wave, int sub, int l8, floatx4 (&v)[8][2]) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int lb = wave * 64 + 4 * i + sub;
-    v[i] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(wr, (lb * 64 + l16 * 4) * 4, 0, kNT));
+  for (int i = 0; i < 8; ++i) {
+    const int lb = wave * 64 + 8 * i + sub;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      v[i][h] = __builtin_bit_cast(floatx4,
+                                   __builtin_amdgcn_raw_buffer_load_b128(wr, (lb * 64 + (8 * h + l8) * 4) * 4, 0, kNT));
   }
 }
 
@@ -97,9 +103,16 @@ __device__ __forceinline__ uint32_t encode4(floatx4 v, const BlockEnc& b, float 
   return p;
 }
 
-__device__ __forceinline__ float block_absmax(floatx4 v) {
-  const u32x4 u = __builtin_bit_cast(u32x4, v) & 0x7FFFFFFFu;
-  return __builtin_bit_cast(float, row16_max_bits(max(max(u.x, u.y), max(u.z, u.w))));
+// absmax of a block held by 8 lanes (two float4 each): an integer max of the
+// |w| bit patterns, then a max across the half DPP row
+__device__ __forceinline__ float block_absmax(const floatx4 (&v)[2]) {
+  const u32x4 a = __builtin_bit_cast(u32x4, v[0]) & 0x7FFFFFFFu;
+  const u32x4 b = __builtin_bit_cast(u32x4, v[1]) & 0x7FFFFFFFu;
+  uint32_t x = max(max(max(a.x, a.y), max(a.z, a.w)), max(max(b.x, b.y), max(b.z, b.w)));
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, true));  // row_half_mirror
+  return __builtin_bit_cast(float, x);
 }
 
 // max over the 256 threads of the workgroup (every thread gets it)
@@ -179,8 +192,8 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int sub = lane >> 4;
-  const int l16 = lane & 15;
+  const int sub = lane >> 3;
+  const int l8 = lane & 7;
   const int64_t g = blockIdx.x;
   const int64_t gb0 = g * 256;
   const uint32_t nb = (uint32_t)min((int64_t)256, nblocks - gb0);  // blocks in this group
@@ -188,25 +201,25 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
   enc_to_lds<false>(enc, etab, tid);
   if ((RES || ERR) && tid < 16) tab[tid] = cst.table[tid];
 
-  floatx4 v[16];
-  load_group(wr, wave, sub, l16, v);
+  floatx4 v[8][2];
+  load_group(wr, wave, sub, l8, v);
   __syncthreads();  // encoder tables
 
-  float amax[16];
-  uint32_t packed[16];
+  float amax[8];
+  uint32_t packed[8];  // round i: quad l8's codes in bits 0..15, quad 8 + l8's in 16..31
   double dsum = 0.0, wsum = 0.0;
-  // lane l16 of row `sub` owns the block of round l16: lb = wave*64 + 4*l16 + sub
-  const int mylb = wave * 64 + 4 * l16 + sub;
+  // lane l8 of half row `sub` owns the block of round l8: lb = wave*64 + 8*l8 + sub
+  const int mylb = wave * 64 + 8 * l8 + sub;
   // (absmax bit patterns are non-negative integers: an integer max over the
-  // rounds, the others masked to 0, picks round l16's value bit for bit)
+  // rounds, the others masked to 0, picks round l8's value bit for bit)
   auto my_amax = [&]() -> float {
     uint32_t mb = 0u;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mb = max(mb, (l16 == i) ? __builtin_bit_cast(uint32_t, amax[i]) : 0u);
+    for (int i = 0; i < 8; ++i) mb = max(mb, (l8 == i) ? __builtin_bit_cast(uint32_t, amax[i]) : 0u);
     return __builtin_bit_cast(float, mb);
   };
-  // double-quantization step of the group, S = fl32(max absmax / 255): the 16
-  // rows of this lane's round, then lanes, then waves
+  // double-quantization step of the group, S = fl32(max absmax / 255): the 8
+  // rounds of this lane's half row, then the other half rows, then waves
   auto group_step = [&](float mine) -> float {
     float gm = mine;
     gm = fmaxf(gm, __shfl_xor(gm, 1));
@@ -223,21 +236,28 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
     if constexpr (ERR == 2) {
       // the error with 8-bit scales needs S before any round: block maxima first
 #pragma unroll
-      for (int i = 0; i < 16; ++i) amax[i] = block_absmax(v[i]);
+      for (int i = 0; i < 8; ++i) amax[i] = block_absmax(v[i]);
       S = group_step(my_amax());
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
       // with the error, one round at a time keeps the fp64 temporaries short-lived
       if constexpr (ERR != 0) __builtin_amdgcn_sched_barrier(0);
       const float m = (ERR == 2) ? amax[i] : block_absmax(v[i]);
       amax[i] = m;
-      packed[i] = encode4(v[i], block_enc(m), enc.bscale, enc.boffset, etab);
-      if constexpr (ERR == 1) error_round(v[i], packed[i], m, tab, dsum, wsum);
-      if constexpr (ERR == 2)
-        error_round(v[i], packed[i], (S > 0.f) ? fminf(255.f, rintf(m / S)) * S : 0.f, tab, dsum, wsum);
-      const int lb = wave * 64 + 4 * i + sub;
-      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)packed[i], cr, lb * 32 + l16 * 2, 0, kNT);
+      const BlockEnc be = block_enc(m);
+      packed[i] = encode4(v[i][0], be, enc.bscale, enc.boffset, etab) |
+                  (encode4(v[i][1], be, enc.bscale, enc.boffset, etab) << 16);
+      if constexpr (ERR != 0) {
+        const float sc = (ERR == 1) ? m : ((S > 0.f) ? fminf(255.f, rintf(m / S)) * S : 0.f);
+        error_round(v[i][0], packed[i] & 0xFFFFu, sc, tab, dsum, wsum);
+        error_round(v[i][1], packed[i] >> 16, sc, tab, dsum, wsum);
+      }
+      const int lb = wave * 64 + 8 * i + sub;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(packed[i] >> (16 * h)), cr, lb * 32 + (8 * h + l8) * 2,
+                                              0, kNT);
     }
     const float mine = my_amax();
     if constexpr (!DQ) {
@@ -258,13 +278,17 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
   if constexpr (RES) {
     // residual of the first stage, in place: r = fl32(w - fl32(table[c] * a_hat))
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
       float sc = amax[i];
       if constexpr (DQ) sc = (S1 > 0.f) ? fminf(255.f, rintf(amax[i] / S1)) * S1 : 0.f;
-      v[i].x = v[i].x - tab[packed[i] & 15u] * sc;
-      v[i].y = v[i].y - tab[(packed[i] >> 4) & 15u] * sc;
-      v[i].z = v[i].z - tab[(packed[i] >> 8) & 15u] * sc;
-      v[i].w = v[i].w - tab[(packed[i] >> 12) & 15u] * sc;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t pk = packed[i] >> (16 * h);
+        v[i][h].x = v[i][h].x - tab[pk & 15u] * sc;
+        v[i][h].y = v[i][h].y - tab[(pk >> 4) & 15u] * sc;
+        v[i][h].z = v[i][h].z - tab[(pk >> 8) & 15u] * sc;
+        v[i][h].w = v[i][h].w - tab[(pk >> 12) & 15u] * sc;
+      }
     }
     __syncthreads();  // the first stage's group-max slots are read before the second stage reuses them
     stage(o2);
@@ -330,58 +354,64 @@ __global__ __launch_bounds__(256) void k_error_partial(const float* __restrict__
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int sub = lane >> 4;
-  const int l16 = lane & 15;
+  const int sub = lane >> 3;
+  const int l8 = lane & 7;
   const int64_t g = blockIdx.x;
   const int64_t gb0 = g * 256;
   const uint32_t nb = (uint32_t)min((int64_t)256, nblocks - gb0);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(W + gb0 * 64, nb * 256);
   enc_to_lds<true>(enc, etab, tid);
 
-  floatx4 v[16];
-  load_group(wr, wave, sub, l16, v);
-  float amax[16];
+  floatx4 v[8][2];
+  load_group(wr, wave, sub, l8, v);
+  float amax[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) amax[i] = block_absmax(v[i]);
+  for (int i = 0; i < 8; ++i) amax[i] = block_absmax(v[i]);
   float S = 0.f;
   if constexpr (DQ) {
+    // the 8 rounds of this half row, the other half rows of the wave, then waves
     float gm = amax[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) gm = fmaxf(gm, amax[i]);
+    for (int i = 1; i < 8; ++i) gm = fmaxf(gm, amax[i]);
+    gm = fmaxf(gm, __shfl_xor(gm, 8));
     S = group_max(gm, lane, wave) / 255.0f;  // its barrier also publishes the encoder table
   } else {
     __syncthreads();  // publishes the encoder table
   }
 
   // dequantization scale of each round's block
-  float sc[16];
+  float sc[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 8; ++i) {
     sc[i] = amax[i];
     if constexpr (DQ) sc[i] = (S > 0.f) ? fminf(255.f, rintf(amax[i] / S)) * S : 0.f;
   }
   double dsum = 0.0, wsum = 0.0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    // one round at a time; the 4 squares of a round are added pairwise before
-    // joining the running sums, so the serial chain is 16 steps, not 64
+  for (int i = 0; i < 8; ++i) {
+    // one round at a time, its two quads in order; the 4 squares of a quad are
+    // added pairwise before joining the running sums (the order of the one-pass
+    // quantize + error kernel)
     __builtin_amdgcn_sched_barrier(0);
-    const float w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
     const BlockEnc be = block_enc(amax[i]);
-    double d2[4], w2[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      EncEntry en;
-      const bool up = above(w4[e], be, enc.bscale, enc.boffset, etab, en);
-      const float wh = __builtin_bit_cast(float, up ? en.hi : en.lo) * sc[i];
-      // fp64 from here on: squares of fp32 weights can leave the fp32 range
-      const double wd = (double)w4[e];
-      const double d = wd - (double)wh;
-      d2[e] = d * d;
-      w2[e] = wd * wd;
+    for (int h = 0; h < 2; ++h) {
+      const float w4[4] = {v[i][h].x, v[i][h].y, v[i][h].z, v[i][h].w};
+      double d2[4], w2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        EncEntry en;
+        const bool up = above(w4[e], be, enc.bscale, enc.boffset, etab, en);
+        const float wh = __builtin_bit_cast(float, up ? en.hi : en.lo) * sc[i];
+        // fp64 from here on: squares of fp32 weights can leave the fp32 range
+        const double wd = (double)w4[e];
+        const double d = wd - (double)wh;
+        d2[e] = d * d;
+        w2[e] = wd * wd;
+      }
+      dsum += (d2[0] + d2[1]) + (d2[2] + d2[3]);
+      wsum += (w2[0] + w2[1]) + (w2[2] + w2[3]);
     }
-    dsum += (d2[0] + d2[1]) + (d2[2] + d2[3]);
-    wsum += (w2[0] + w2[1]) + (w2[2] + w2[3]);
   }
   error_group_out(dsum, wsum, lane, wave, tid, g, part);
 }
