@@ -178,7 +178,10 @@ nf4_status nf4_workspace_bytes(int32_t op, int64_t M, int64_t rows, int64_t cols
  * NF4 weight dequantized to bf16 inside the matmul (never written out) and
  * fp32 accumulation.  s is alpha/r ("LoRA: Fine-tuning a model by learning a
  * small update", the algebra section; rsLoRA callers pass alpha/sqrt(r)).
- *   W    : quantized [o][h], h % 64 == 0, o % 64 == 0.
+ *   W    : quantized [o][h], h % 64 == 0, o % 64 == 0, h and o at most
+ *          4194304 and o * h at most 2^32 (the fused kernels address a
+ *          256-row activation tile and the packed codes through 32-bit buffer
+ *          ranges); larger weights are rejected with NF4_ERR_SHAPE.
  *   X    : bf16 [M][h]; M >= 0 (M == 0 does nothing).
  *   L1   : bf16 [h][r];  L2 : bf16 [r][o];  1 <= r <= 256.
  *   Y    : bf16 [M][o] output.

@@ -219,9 +219,14 @@ void tensor_ranges(const nf4_tensor* q, Range out[6]) {
   out[5] = rng(r ? r->dq_scale : nullptr, r ? db : 0);
 }
 
+// The fused GEMM reads a 256-row tile of the activations (256 * K * 2 bytes)
+// and, for the input gradient, all packed codes (rows * cols / 2 bytes)
+// through 32-bit buffer ranges: both stay below 4 GiB with these limits.
+constexpr int64_t kMaxLayerDim = (int64_t)1 << 22;
+constexpr int64_t kMaxLayerWeights = (int64_t)1 << 32;
 nf4_status layer_shape(int64_t rows, int64_t cols) {
   if (rows <= 0 || cols <= 0 || rows % kBlock != 0 || cols % kBlock != 0) return NF4_ERR_SHAPE;
-  if (rows > INT32_MAX / 2 || cols > INT32_MAX / 2) return NF4_ERR_SHAPE;
+  if (rows > kMaxLayerDim || cols > kMaxLayerDim || rows * cols > kMaxLayerWeights) return NF4_ERR_SHAPE;
   return NF4_OK;
 }
 
@@ -584,8 +589,8 @@ nf4_status nf4_matmul(const nf4_tensor* W, int32_t transpose, const uint16_t* A,
                       const uint16_t* B2, int32_t R, uint16_t* C, void* stream) {
   nf4_status st = check_tensor(W);
   if (st != NF4_OK) return st;
-  if (W->rows % kBlock != 0 || W->rows <= 0 || W->cols <= 0) return NF4_ERR_SHAPE;
-  if (W->rows > INT32_MAX / 2 || W->cols > INT32_MAX / 2) return NF4_ERR_SHAPE;
+  st = layer_shape(W->rows, W->cols);
+  if (st != NF4_OK) return st;
   if (transpose != 0 && transpose != 1) return NF4_ERR_ARG;
   if (M < 0 || M > ((int64_t)1 << 31) || R < 0 || R > 256 || R % 16 != 0) return NF4_ERR_SHAPE;
   if (M == 0) return NF4_OK;

@@ -145,6 +145,13 @@ def test_fwd_validation():
     assert fwd_call(d, T=F + 64) == nf4.NF4_ERR_ALIAS                     # T inside Y
     assert fwd_call(d, ws=A) == nf4.NF4_ERR_ALIAS                         # workspace over the codes
     assert fwd_call(d, M=0) == nf4.NF4_OK                                 # empty batch: nothing to do
+    # weights beyond the fused kernels' 32-bit buffer ranges are rejected before any launch
+    assert fwd_call(desc(rows=(1 << 22) + 64, cols=128)) == nf4.NF4_ERR_SHAPE
+    assert fwd_call(desc(rows=128, cols=(1 << 22) + 64)) == nf4.NF4_ERR_SHAPE
+    assert fwd_call(desc(rows=1 << 22, cols=(1 << 10) + 64)) == nf4.NF4_ERR_SHAPE   # rows * cols > 2^32
+    big = desc(rows=(1 << 22) + 64, cols=128)
+    assert lib.nf4_matmul(ctypes.byref(big), 0, ctypes.c_void_p(C), 16, None, None, 0, ctypes.c_void_p(F),
+                          None) == nf4.NF4_ERR_SHAPE
 
 
 def bwd_call(d, X=C, dY=D, M=16, L1=E, L2=F, r=8, T=None, dX=G, dL1=H, dL2=H + 0x1000000, ws=H + 0x2000000,
