@@ -78,8 +78,13 @@ def cpu_baseline(d, s, steps=2):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 200 for c2, 20 for c3 and c5, 5 for c4-stack)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: 300 for c2, about 60 ms of work, after which the "
+                         "step time no longer falls; 3 for c3 and c5, 1 for c4-stack)")
+    ap.add_argument("--kernel-calls", type=int, default=50,
+                    help="c2: back-to-back launches per window of the standalone kernel timings")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
@@ -91,6 +96,11 @@ def main():
                          "70B-shaped up projection; c4-stack: the 280-linear 14B-shaped stack with AQLoRA's "
                          "allocation against QLoRA")
     args = ap.parse_args()
+    steps0, warmup0 = {"c2": (200, 300), "c3": (20, 3), "c5": (20, 3), "c4-stack": (5, 1)}[args.workload]
+    if args.steps is None:
+        args.steps = steps0
+    if args.warmup is None:
+        args.warmup = warmup0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -201,7 +211,7 @@ def main():
                               n // 2 + n // 64 + 4 * (n // 64 // 256) + 2 * n),
         "merge_fp32_to_bf16": (lambda: nf4.merge(W, L1, L2, s, bf16=True, out=Wm), "bytes", 6 * n),
     }
-    stats = interleaved_times({k: v[0] for k, v in work.items()}, args.steps, 7, stream, torch)
+    stats = interleaved_times({k: v[0] for k, v in work.items()}, args.kernel_calls, 7, stream, torch)
     kernels = {}
     for name, (_, kind, amount) in work.items():
         st = stats[name]
@@ -210,7 +220,7 @@ def main():
             kernels[name].update(tflops=round(amount / (st["us"] * 1e-6) / 1e12, 1), flops_per_launch=amount)
         else:
             kernels[name].update(GBps=round(amount / (st["us"] * 1e-6) / 1e9, 1), bytes=amount)
-    kernels["timing"] = (f"7 interleaved repetitions of {args.steps} back-to-back launches per op (HIP events on "
+    kernels["timing"] = (f"7 interleaved repetitions of {args.kernel_calls} back-to-back launches per op (HIP events on "
                          f"the launch stream); us = mean of the fastest half")
 
     # the same weights at identical storage in the other 4-bit codebooks: reconstruction error and quantize time
@@ -407,7 +417,13 @@ def bench_layers(args):
         q_ms = timed(lambda: nf4.quantize(W, 256, out=q))
         Wd = torch.empty(o, h, dtype=torch.bfloat16, device=dev)
         dq_ms = timed(lambda: nf4.dequantize(q, bf16=True, out=Wd))
-        del Wd, W
+        # what plain PyTorch elementwise passes over the same weights reach: an fp32 copy (4 B read + 4 B
+        # written per weight) and the fp32 -> bf16 conversion (4 + 2 B), the practical streaming rates the
+        # quantize (4.5 B) and dequantize (2.5 B) passes are compared with
+        Wc = torch.empty_like(W)
+        cp_ms = timed(lambda: Wc.copy_(W))
+        cv_ms = timed(lambda: Wd.copy_(W))
+        del Wd, W, Wc
         ws_f = nf4.workspace(nf4.NF4_OP_FWD, M, q, r)
         ws_b = nf4.workspace(nf4.NF4_OP_BWD, M, q, r)
         Y = torch.empty(M, o, dtype=torch.bfloat16, device=dev)
@@ -428,7 +444,9 @@ def bench_layers(args):
                     "fwd_bwd_pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
                     "quantize_us": round(1e3 * q_ms, 2), "quantize_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
                     "dequantize_bf16_us": round(1e3 * dq_ms, 2),
-                    "dequantize_GBps": round(dq_bytes / (dq_ms * 1e-3) / 1e9, 1)})
+                    "dequantize_GBps": round(dq_bytes / (dq_ms * 1e-3) / 1e9, 1),
+                    "torch_copy_fp32_GBps": round(8 * n / (cp_ms * 1e-3) / 1e9, 1),
+                    "torch_fp32_to_bf16_GBps": round(6 * n / (cv_ms * 1e-3) / 1e9, 1)})
         print(f"# {cfg.name}: fwd {f_ms:.3f} ms, bwd {b_ms:.3f} ms ({tf:.1f} TFLOP/s); quantize {1e3 * q_ms:.1f} us, "
               f"dequantize {1e3 * dq_ms:.1f} us", file=sys.stderr, flush=True)
         del q, X, L1, L2, dY, Y, T, dX, dL1, dL2, ws_f, ws_b
