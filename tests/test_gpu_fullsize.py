@@ -2,7 +2,8 @@
 
 The layer workloads run at their real shapes in the launch configuration the
 benchmark uses; the oracle checks what it can compute at that size:
-  * codes, scales and dequantized weights over the whole matrix, bit-exact;
+  * codes, scales and dequantized weights over the whole matrix, bit-exact,
+    and the layer error from the same one-pass quantize within 1e-6;
   * Y and dX on sampled token rows (each output row depends only on its own
     input row, so the oracle runs on those rows alone);
   * dL1 and dL2 over all tokens: every token contributes its own term, so the
@@ -73,8 +74,8 @@ def check_layer_fullsize(layer, n_rows=16, chunk=1024):
     d = synth.layer_inputs(layer)
     W, s, dq, M = d["W"], d["s"], d["dq_group"], layer.M
 
-    say("  HIP path: quantize, fwd, bwd")
-    q = nf4.quantize(dev(W), dq)
+    say("  HIP path: quantize + layer error (one pass), fwd, bwd")
+    q, err = nf4.quantize_error(dev(W), dq, dq)
     X, L1, L2, dY = (dev(d[k]) for k in ("X", "L1", "L2", "dY"))
     Y, T = nf4.fwd(q, X, L1, L2, s)
     dX, dL1, dL2 = nf4.bwd(q, X, dY, L1, L2, s, T=T)
@@ -87,6 +88,10 @@ def check_layer_fullsize(layer, n_rows=16, chunk=1024):
     wh = oracle.dequantize(ref)
     assert np.array_equal(nf4.dequantize(q).cpu().numpy().view(np.uint32), wh.view(np.uint32)), "dequantized W"
     del q
+    say("  oracle layer error")
+    got, want = float(err.cpu()[0]), oracle.layer_error(W, 64, dq)
+    say(f"  error: gpu {got:.12g} oracle {want:.12g}")
+    assert abs(got - want) <= 1e-6 * want, (got, want)
 
     rows = sampled_rows(M, n_rows, layer.seed)
     say(f"  oracle rows {rows[:4]}... ({len(rows)} rows)")
