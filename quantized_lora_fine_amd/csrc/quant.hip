@@ -296,8 +296,11 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
 }
 
 // ---------------------------------------------------------------------------
-// dequantize: each thread expands one code dword (8 weights of one block)
+// dequantize: each thread expands code dwords (8 weights of one block each),
+// four per round for bf16 output and one for fp32
 // ---------------------------------------------------------------------------
+constexpr int kDequantWordsBf16 = 4;  // code words per thread and round, bf16 output
+
 template <bool DQ, bool BF16, bool RES>
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes,
                                                     const void* __restrict__ absmax,
@@ -314,26 +317,65 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
     if constexpr (DQ) return (float)((const uint8_t*)am)[blk] * dq[blk >> 8];
     else return ((const float*)am)[blk];
   };
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nwords; t += stride) {
-    const uint32_t w = __builtin_nontemporal_load((const uint32_t*)codes + t);
-    const int64_t blk = t >> 3;
-    const float sc = scale(absmax, dqs, blk);
-    float f[8];
+  if constexpr (BF16) {
+    // A workgroup takes 256 U consecutive code words per round: word
+    // base + 256 j + threadIdx.x for j < U, so each load and store instruction
+    // of a wave covers one contiguous span.  All U words and their scales are
+    // loaded before the first is used: the code stream is small next to the
+    // output, and only loads in flight keep it moving.
+    constexpr int U = kDequantWordsBf16;
+    const int64_t stride = (int64_t)gridDim.x * (256 * U);
+    for (int64_t base = (int64_t)blockIdx.x * (256 * U); base < nwords; base += stride) {
+      uint32_t w[U], w2[U];
+      float sc[U], sc2[U];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = tab[(w >> (4 * e)) & 15u] * sc;
-    if constexpr (RES) {
-      // second stage: w_hat = fl32(w_hat1 + w_hat2)
-      const uint32_t w2 = __builtin_nontemporal_load((const uint32_t*)codes2 + t);
-      const float sc2 = scale(absmax2, dqs2, blk);
+      for (int j = 0; j < U; ++j) {
+        const int64_t t = base + 256 * j + threadIdx.x;
+        const bool in = t < nwords;
+        w[j] = in ? __builtin_nontemporal_load((const uint32_t*)codes + t) : 0u;
+        if constexpr (RES) w2[j] = in ? __builtin_nontemporal_load((const uint32_t*)codes2 + t) : 0u;
+      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = f[e] + tab[(w2 >> (4 * e)) & 15u] * sc2;
+      for (int j = 0; j < U; ++j) {
+        const int64_t t = base + 256 * j + threadIdx.x;
+        const bool in = t < nwords;
+        sc[j] = in ? scale(absmax, dqs, t >> 3) : 0.f;
+        if constexpr (RES) sc2[j] = in ? scale(absmax2, dqs2, t >> 3) : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int64_t t = base + 256 * j + threadIdx.x;
+        if (t >= nwords) break;
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = tab[(w[j] >> (4 * e)) & 15u] * sc[j];
+        if constexpr (RES) {
+          // second stage: w_hat = fl32(w_hat1 + w_hat2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = f[e] + tab[(w2[j] >> (4 * e)) & 15u] * sc2[j];
+        }
+        const u32x4 o = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                         pack_bf16x2(f[6], f[7])};
+        __builtin_nontemporal_store(o, (u32x4*)out + t);
+      }
     }
-    if constexpr (BF16) {
-      const u32x4 o = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                       pack_bf16x2(f[6], f[7])};
-      __builtin_nontemporal_store(o, (u32x4*)out + t);
-    } else {
+  } else {
+    // fp32 output: one word per thread and round.  Each word is two 16-byte
+    // stores that interleave within a line; with more words in flight this
+    // pass got slower (4.4 -> 3.0 TB/s at 45 M weights).
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nwords; t += stride) {
+      const uint32_t w = __builtin_nontemporal_load((const uint32_t*)codes + t);
+      const float sc = scale(absmax, dqs, t >> 3);
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = tab[(w >> (4 * e)) & 15u] * sc;
+      if constexpr (RES) {
+        const uint32_t w2 = __builtin_nontemporal_load((const uint32_t*)codes2 + t);
+        const float sc2 = scale(absmax2, dqs2, t >> 3);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = f[e] + tab[(w2 >> (4 * e)) & 15u] * sc2;
+      }
       floatx4* o = (floatx4*)out + 2 * t;
       __builtin_nontemporal_store((floatx4{f[0], f[1], f[2], f[3]}), o);
       __builtin_nontemporal_store((floatx4{f[4], f[5], f[6], f[7]}), o + 1);
@@ -538,8 +580,10 @@ hipError_t launch_dequantize(const uint8_t* codes, const void* absmax, const flo
                              const NF4Consts& c, hipStream_t st) {
   const int64_t nwords = nweights / 8;
   if (nwords == 0) return hipSuccess;
-  int64_t blocks = (nwords + 255) / 256;
-  if (blocks > 256 * 64) blocks = 256 * 64;
+  const int64_t per = bf16 ? 256 * kDequantWordsBf16 : 256;
+  int64_t blocks = (nwords + per - 1) / per;
+  const int64_t cap = bf16 ? 256 * 32 : 256 * 64;  // 32 or 64 workgroups per CU, then a grid-stride loop
+  if (blocks > cap) blocks = cap;
   const dim3 gr((unsigned)blocks), bl(256);
 #define NF4K_DEQ(D, B, R)                                                                                         \
   hipLaunchKernelGGL((k_dequantize<D, B, R>), gr, bl, 0, st, codes, absmax, dqs, codes2, absmax2, dqs2, nwords, \
