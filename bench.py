@@ -380,7 +380,7 @@ def bench_layers(args):
     MLP, M=8192, r=64) or c5 (a 70B-shaped up projection, M=16384, r=64).  Per
     linear: quantize (8-bit DQ scales) and bf16 dequantize as standalone passes,
     and the fused fwd and bwd, each timed with HIP events over `steps` calls after
-    `warmup`.  The value is the fwd+bwd FLOP of all the linears over their summed
+    `warmup` calls and at least 50 ms of the op's own work.  The value is the fwd+bwd FLOP of all the linears over their summed
     fwd+bwd time.  The CPU oracle is not timed at these sizes (cpu_baseline is
     null); the full-size parity tests check these workloads against it."""
     import torch
@@ -395,8 +395,13 @@ def bench_layers(args):
     print(f"# device {torch.cuda.get_device_name(0)}; workload {args.workload}", file=sys.stderr, flush=True)
 
     def timed(fn):
-        for _ in range(args.warmup):
+        # untimed calls first: `warmup` of them and at least 50 ms of the op's own work (the clock takes
+        # tens of ms to settle after the host-side setup; without this the first op timed the ramp)
+        t_end, n = time.perf_counter() + 0.05, 0
+        while n < args.warmup or time.perf_counter() < t_end:
             fn()
+            torch.cuda.synchronize()
+            n += 1
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(args.steps):
