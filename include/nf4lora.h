@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define NF4LORA_ABI_VERSION 3
+#define NF4LORA_ABI_VERSION 4
 
 typedef enum nf4_status {
   NF4_OK = 0,
@@ -346,6 +346,31 @@ nf4_status nf4_layer_error(const float *W, int64_t rows, int64_t cols, int32_t b
  */
 nf4_status nf4_quantize_error(const float *W, const nf4_tensor *q, int32_t err_dq_group, double *err_dev,
                               void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The profiling pass over a whole model at once: AQLoRA section 3.1 measures
+ * the NF4 reconstruction error of every linear before it ranks them.  For
+ * i < n, err_dev[i] is bit for bit what nf4_layer_error(W[i], rows[i],
+ * cols[i], 64, dq_group, codebook, ...) writes.  Up to 64 linears go into one
+ * launch pair, so n linears cost about 2 n / 64 launches instead of 2 n.
+ *   W:          host array of n device pointers, each fp32 [rows[i]][cols[i]],
+ *               16-byte aligned (NULL allowed only for an empty linear).
+ *   rows, cols: host arrays of n shapes; cols[i] % 64 == 0.
+ *   err_dev:    device double[n], 8-byte aligned.
+ *   ws:         nf4_error_batch_workspace_bytes(rows, cols, n) bytes, 16-byte
+ *               aligned: one 16-byte partial per group of 256 blocks of every
+ *               linear.
+ * The host arrays are read during the call only.  n == 0 does nothing.  ws
+ * and err_dev must not overlap each other or any W[i].
+ * Errors: NF4_ERR_NULL, _SHAPE, _ARG (n < 0, dq_group, codebook), _ALIGN,
+ * _ALIAS, _WORKSPACE, _HIP.
+ */
+nf4_status nf4_layer_error_batch(const float *const *W, const int64_t *rows, const int64_t *cols, int32_t n,
+                                 int32_t dq_group, int32_t codebook, double *err_dev, void *ws, size_t ws_bytes,
+                                 void *stream);
+/* Workspace bytes of nf4_layer_error_batch over these shapes (host output *bytes).
+ * Errors: NF4_ERR_NULL, _SHAPE, _ARG (n < 0). */
+nf4_status nf4_error_batch_workspace_bytes(const int64_t *rows, const int64_t *cols, int32_t n, size_t *bytes);
 
 /*
  * The protected set of AQLoRA's precision allocation (section 3.2): indices

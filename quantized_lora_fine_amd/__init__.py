@@ -69,6 +69,10 @@ _SIGS = {
     "nf4_matmul": ([_T, _i32, _vp, _i64, _vp, _vp, _i32, _vp, _vp], ctypes.c_int),
     "nf4_layer_error": ([_vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _sz, _vp], ctypes.c_int),
     "nf4_quantize_error": ([_vp, _T, _i32, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "nf4_layer_error_batch": ([ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i32, _i32, _i32,
+                               _vp, _vp, _sz, _vp], ctypes.c_int),
+    "nf4_error_batch_workspace_bytes": ([ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i32, ctypes.POINTER(_sz)],
+                                        ctypes.c_int),
     "nf4_codebook_values": ([_i32, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
     "nf4_topk": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
     "nf4_protect_count": ([_f64, _i32], _i32),
@@ -292,6 +296,41 @@ def layer_error(W: torch.Tensor, dq_group: int = 0, out: torch.Tensor | None = N
     _check(_lib.nf4_layer_error(_ptr(W), rows, cols, BLOCK, dq_group, CODEBOOKS[codebook], _ptr(err), _ptr(ws),
                                 ws.numel(), _stream()), "nf4_layer_error")
     return err
+
+
+def _shape_arrays(shapes):
+    n = len(shapes)
+    rows = (_i64 * max(n, 1))(*[r for r, _ in shapes])
+    cols = (_i64 * max(n, 1))(*[c for _, c in shapes])
+    return rows, cols
+
+
+def error_batch_workspace_bytes(shapes) -> int:
+    """nf4_error_batch_workspace_bytes for a list of (rows, cols)."""
+    rows, cols = _shape_arrays(shapes)
+    b = _sz()
+    _check(_lib.nf4_error_batch_workspace_bytes(rows, cols, len(shapes), ctypes.byref(b)),
+           "nf4_error_batch_workspace_bytes")
+    return b.value
+
+
+def layer_error_batch(Ws, dq_group: int = 0, out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                      codebook: str = "nf4") -> torch.Tensor:
+    """nf4_layer_error_batch over a list of cuda fp32 [rows][cols] tensors: a cuda float64 [n] tensor whose
+    entry i equals layer_error(Ws[i], dq_group, codebook=codebook) bit for bit (no host sync)."""
+    for W in Ws:
+        assert W.dtype == torch.float32 and W.is_cuda and W.is_contiguous() and W.dim() == 2
+    n = len(Ws)
+    shapes = [tuple(W.shape) for W in Ws]
+    dev = Ws[0].device if n else torch.device("cuda")
+    err = out if out is not None else torch.empty(max(n, 1), dtype=torch.float64, device=dev)
+    if ws is None:
+        ws = torch.empty(error_batch_workspace_bytes(shapes), dtype=torch.uint8, device=dev)
+    rows, cols = _shape_arrays(shapes)
+    ptrs = (_vp * max(n, 1))(*[W.data_ptr() for W in Ws])
+    _check(_lib.nf4_layer_error_batch(ptrs, rows, cols, n, dq_group, CODEBOOKS[codebook], _ptr(err), _ptr(ws),
+                                      ws.numel(), _stream()), "nf4_layer_error_batch")
+    return err[:n]
 
 
 def quantize_error(W: torch.Tensor, dq_group: int = 0, err_dq_group: int = 0, out: NF4Weight | None = None,

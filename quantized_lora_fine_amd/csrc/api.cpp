@@ -452,6 +452,21 @@ nf4_status plain_product(int mode, const WSrc& w, const uint16_t* A, uint16_t* C
   return hip_status(gemm(mode, w, A, nullptr, nullptr, 0, 0, C, M, (hipStream_t)stream));
 }
 
+// Shapes of a batched error pass: every linear as nf4_layer_error checks it,
+// and the partial slots of all of them (16 bytes each) in *need.
+nf4_status error_batch_shapes(const int64_t* rows, const int64_t* cols, int32_t n, size_t* need) {
+  if (n < 0) return NF4_ERR_ARG;
+  if (n > 0 && (!rows || !cols)) return NF4_ERR_NULL;
+  int64_t slots = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const nf4_status st = check_shape(rows[i], cols[i], kBlock, 0);
+    if (st != NF4_OK) return st;
+    slots += (rows[i] * cols[i] / kBlock + kGroup - 1) / kGroup;
+  }
+  *need = align256((size_t)(slots > 0 ? slots : 1) * 16);
+  return NF4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -627,6 +642,37 @@ nf4_status nf4_layer_error(const float* W, int64_t rows, int64_t cols, int32_t b
     return NF4_ERR_ALIAS;
   return hip_status(launch_error(W, n / kBlock, dq_group != 0, (double*)ws, err_dev, codebook_enc(codebook),
                                  (hipStream_t)stream));
+}
+
+nf4_status nf4_error_batch_workspace_bytes(const int64_t* rows, const int64_t* cols, int32_t n, size_t* bytes) {
+  if (!bytes) return NF4_ERR_NULL;
+  return error_batch_shapes(rows, cols, n, bytes);
+}
+
+nf4_status nf4_layer_error_batch(const float* const* W, const int64_t* rows, const int64_t* cols, int32_t n,
+                                 int32_t dq_group, int32_t codebook, double* err_dev, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  size_t need = 0;
+  nf4_status st = error_batch_shapes(rows, cols, n, &need);
+  if (st != NF4_OK) return st;
+  if (dq_group != 0 && dq_group != kGroup) return NF4_ERR_ARG;
+  if (codebook < 0 || codebook >= kCodebooks) return NF4_ERR_ARG;
+  if (n == 0) return NF4_OK;
+  if (!W || !err_dev) return NF4_ERR_NULL;
+  if (!ws) return NF4_ERR_WORKSPACE;
+  if (ws_bytes < need) return NF4_ERR_WORKSPACE;
+  if (!aligned16(ws) || ((uintptr_t)err_dev & 7u) != 0) return NF4_ERR_ALIGN;
+  const Range wr = rng(ws, need), er = rng(err_dev, (size_t)n * 8);
+  if (overlap(wr, er)) return NF4_ERR_ALIAS;
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t cnt = rows[i] * cols[i];
+    if (cnt > 0 && !W[i]) return NF4_ERR_NULL;
+    if (W[i] && !aligned16(W[i])) return NF4_ERR_ALIGN;
+    const Range in = rng(W[i], (size_t)cnt * 4);
+    if (overlap(in, wr) || overlap(in, er)) return NF4_ERR_ALIAS;
+  }
+  return hip_status(launch_error_batch(W, rows, cols, n, dq_group != 0, (double*)ws, err_dev,
+                                       codebook_enc(codebook), (hipStream_t)stream));
 }
 
 nf4_status nf4_quantize_error(const float* W, const nf4_tensor* q, int32_t err_dq_group, double* err_dev, void* ws,

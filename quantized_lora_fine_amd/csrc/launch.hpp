@@ -25,6 +25,11 @@ hipError_t launch_quantize_error(const float* W, int64_t nblocks, bool dq, uint8
                                  hipStream_t st);
 hipError_t launch_error(const float* W, int64_t nblocks, bool dq, double* part, double* err, const NF4Enc& c,
                         hipStream_t st);
+// launch_error for n linears (W[i], rows[i] x cols[i]) in batches of up to 64:
+// err[i] as launch_error writes it for linear i, bit for bit; part holds one
+// (D, Wn) pair per group of every linear, linear after linear.
+hipError_t launch_error_batch(const float* const* W, const int64_t* rows, const int64_t* cols, int32_t n, bool dq,
+                              double* part, double* err, const NF4Enc& c, hipStream_t st);
 hipError_t launch_topk(const double* e, int n, int k, int* idx, hipStream_t st);
 
 // Weight source of the fused GEMM: NF4 with fp32 absmax, NF4 with 8-bit

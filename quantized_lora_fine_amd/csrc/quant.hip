@@ -133,26 +133,25 @@ struct QStage {
   float* dqs;
 };
 
-// Squared reconstruction error and squared weight of one round (4 weights of
-// one block), added to the running sums: the decoded value fl32(table[c] * sc)
-// in fp32 as the format defines, differences and squares in fp64 (squares of
-// fp32 weights can leave the fp32 range).  The 4 squares are added pairwise
-// before joining the sums, rounds in order: the summation order of the
-// per-group partial sums is fixed.
+// One weight's terms of the error, added to the running sums: the decoded
+// value wh = fl32(table[c] * sc) is fp32 as the format defines; the difference
+// (exact in fp64) and both squares are fp64 (squares of fp32 weights can leave
+// the fp32 range), each square added with one fused multiply-add.  Both error
+// kernels add the weights in the same order (round, quad, element), so their
+// per-group partial sums agree bit for bit.
+__device__ __forceinline__ void error_term(float w, float wh, double& dsum, double& wsum) {
+  const double wd = (double)w;
+  const double d = wd - (double)wh;
+  dsum = fma(d, d, dsum);
+  wsum = fma(wd, wd, wsum);
+}
+
+// error_term over one quad (4 weights of one block) of the one-pass kernel
 __device__ __forceinline__ void error_round(floatx4 v, uint32_t packed, float sc, const float* tab, double& dsum,
                                             double& wsum) {
   const float w4[4] = {v.x, v.y, v.z, v.w};
-  double d2[4], w2[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float wh = tab[(packed >> (4 * e)) & 15u] * sc;
-    const double wd = (double)w4[e];
-    const double d = wd - (double)wh;
-    d2[e] = d * d;
-    w2[e] = wd * wd;
-  }
-  dsum += (d2[0] + d2[1]) + (d2[2] + d2[3]);
-  wsum += (w2[0] + w2[1]) + (w2[2] + w2[3]);
+  for (int e = 0; e < 4; ++e) error_term(w4[e], tab[(packed >> (4 * e)) & 15u] * sc, dsum, wsum);
   // materialise the sums here: otherwise the compiler sinks every round's
   // error arithmetic past the group-max barrier and keeps all 16 rounds live
   asm volatile("" : "+v"(dsum), "+v"(wsum));
@@ -389,20 +388,32 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
 // squares in fp64).  Same block/group mapping as k_quantize; the weights stay in
 // registers between the absmax, group-max and encode/decode steps.
 // ---------------------------------------------------------------------------
+// Up to kErrBatch linears of one batched error pass, passed by value as a
+// kernel argument (1.6 KB): W and its block count per linear, and the first
+// partial slot of each linear relative to the launch (g0[n] = slots in all).
+constexpr int kErrBatch = 64;
+struct ErrBatch {
+  const float* W[kErrBatch];
+  int64_t nblocks[kErrBatch];
+  int64_t g0[kErrBatch + 1];
+  int32_t n;
+};
+
+// One group g of 256 blocks of W: its partial sums go to part[2 slot],
+// part[2 slot + 1].  The encoder table `etab` is filled by the caller before
+// the first group; the group's first barrier publishes it.
 template <bool DQ>
-__global__ __launch_bounds__(256) void k_error_partial(const float* __restrict__ W, int64_t nblocks,
-                                                       double* __restrict__ part, NF4Enc enc) {
-  __shared__ EncEntry etab[kMaxBuckets];
+__device__ __forceinline__ void error_partial_group(const float* __restrict__ W, int64_t nblocks, int64_t g,
+                                                    int64_t slot, double* __restrict__ part, const NF4Enc& enc,
+                                                    const EncEntry* etab) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int sub = lane >> 3;
   const int l8 = lane & 7;
-  const int64_t g = blockIdx.x;
   const int64_t gb0 = g * 256;
   const uint32_t nb = (uint32_t)min((int64_t)256, nblocks - gb0);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(W + gb0 * 64, nb * 256);
-  enc_to_lds<true>(enc, etab, tid);
 
   floatx4 v[8][2];
   load_group(wr, wave, sub, l8, v);
@@ -431,36 +442,52 @@ __global__ __launch_bounds__(256) void k_error_partial(const float* __restrict__
   double dsum = 0.0, wsum = 0.0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    // one round at a time, its two quads in order; the 4 squares of a quad are
-    // added pairwise before joining the running sums (the order of the one-pass
-    // quantize + error kernel)
+    // one round at a time, its two quads in order, each quad's weights in order
+    // (the order of the one-pass quantize + error kernel)
     __builtin_amdgcn_sched_barrier(0);
     const BlockEnc be = block_enc(amax[i]);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const float w4[4] = {v[i][h].x, v[i][h].y, v[i][h].z, v[i][h].w};
-      double d2[4], w2[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         EncEntry en;
         const bool up = above(w4[e], be, enc.bscale, enc.boffset, etab, en);
-        const float wh = __builtin_bit_cast(float, up ? en.hi : en.lo) * sc[i];
-        // fp64 from here on: squares of fp32 weights can leave the fp32 range
-        const double wd = (double)w4[e];
-        const double d = wd - (double)wh;
-        d2[e] = d * d;
-        w2[e] = wd * wd;
+        error_term(w4[e], __builtin_bit_cast(float, up ? en.hi : en.lo) * sc[i], dsum, wsum);
       }
-      dsum += (d2[0] + d2[1]) + (d2[2] + d2[3]);
-      wsum += (w2[0] + w2[1]) + (w2[2] + w2[3]);
     }
   }
-  error_group_out(dsum, wsum, lane, wave, tid, g, part);
+  error_group_out(dsum, wsum, lane, wave, tid, slot, part);
 }
 
-// stage 2: one workgroup sums the per-group partials in a fixed order.
-__global__ __launch_bounds__(256) void k_error_final(const double* __restrict__ part, int64_t ngroups,
-                                                     double* __restrict__ err) {
+template <bool DQ>
+__global__ __launch_bounds__(256) void k_error_partial(const float* __restrict__ W, int64_t nblocks,
+                                                       double* __restrict__ part, NF4Enc enc) {
+  __shared__ EncEntry etab[kMaxBuckets];
+  enc_to_lds<true>(enc, etab, threadIdx.x);
+  error_partial_group<DQ>(W, nblocks, blockIdx.x, blockIdx.x, part, enc, etab);
+}
+
+// The same partial sums for up to kErrBatch linears in one launch, one
+// workgroup per group.  The linears' groups are numbered one after another
+// (linear i owns slots b.g0[i] .. b.g0[i + 1] - 1); lane l of each wave
+// compares slot g with b.g0[l + 1], and the count of the linears that end at
+// or before g is the linear that owns it.
+template <bool DQ>
+__global__ __launch_bounds__(256) void k_error_partial_batch(ErrBatch b, double* __restrict__ part, NF4Enc enc) {
+  __shared__ EncEntry etab[kMaxBuckets];
+  enc_to_lds<true>(enc, etab, threadIdx.x);
+  const int64_t g = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const bool done = lane < b.n && b.g0[lane + 1] <= g;
+  const int i = __builtin_amdgcn_readfirstlane(__builtin_popcountll(__ballot(done)));
+  error_partial_group<DQ>(b.W[i], b.nblocks[i], g - b.g0[i], g, part, enc, etab);
+}
+
+// stage 2: one workgroup sums a linear's per-group partials in a fixed order
+// and writes its error.
+__device__ __forceinline__ void error_final_sum(const double* __restrict__ part, int64_t ngroups,
+                                                double* __restrict__ err) {
   __shared__ double sd[256], sw[256];
   const int tid = threadIdx.x;
   // thread t adds groups t, t + 256, t + 512, ... in that order; the loads of
@@ -491,6 +518,18 @@ __global__ __launch_bounds__(256) void k_error_final(const double* __restrict__ 
     __syncthreads();
   }
   if (tid == 0) err[0] = (sw[0] > 0.0) ? sqrt(sd[0]) / sqrt(sw[0]) : 0.0;
+}
+
+__global__ __launch_bounds__(256) void k_error_final(const double* __restrict__ part, int64_t ngroups,
+                                                     double* __restrict__ err) {
+  error_final_sum(part, ngroups, err);
+}
+
+// one workgroup per linear of a batch
+__global__ __launch_bounds__(256) void k_error_final_batch(ErrBatch b, const double* __restrict__ part,
+                                                           double* __restrict__ err) {
+  const int i = blockIdx.x;
+  error_final_sum(part + 2 * b.g0[i], b.g0[i + 1] - b.g0[i], err + i);
 }
 
 // ---------------------------------------------------------------------------
@@ -618,6 +657,34 @@ hipError_t launch_error(const float* W, int64_t nblocks, bool dq, double* part, 
   }
   hipLaunchKernelGGL(k_error_final, dim3(1), dim3(256), 0, st, part, ng, err);
   return hipGetLastError();
+}
+
+hipError_t launch_error_batch(const float* const* W, const int64_t* rows, const int64_t* cols, int32_t n, bool dq,
+                              double* part, double* err, const NF4Enc& c, hipStream_t st) {
+  int64_t slot = 0;  // first partial slot of the chunk
+  for (int32_t c0 = 0; c0 < n; c0 += kErrBatch) {
+    ErrBatch b{};
+    b.n = min(kErrBatch, n - c0);
+    b.g0[0] = 0;
+    for (int i = 0; i < b.n; ++i) {
+      b.W[i] = W[c0 + i];
+      b.nblocks[i] = rows[c0 + i] * cols[c0 + i] / 64;
+      b.g0[i + 1] = b.g0[i] + (b.nblocks[i] + 255) / 256;
+    }
+    const int64_t slots = b.g0[b.n];
+    if (slots > 0) {
+      const dim3 grid((unsigned)slots);
+      if (dq) hipLaunchKernelGGL(k_error_partial_batch<true>, grid, dim3(256), 0, st, b, part + 2 * slot, c);
+      else hipLaunchKernelGGL(k_error_partial_batch<false>, grid, dim3(256), 0, st, b, part + 2 * slot, c);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_error_final_batch, dim3((unsigned)b.n), dim3(256), 0, st, b, part + 2 * slot, err + c0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    slot += slots;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_topk(const double* e, int n, int k, int* idx, hipStream_t st) {

@@ -35,7 +35,7 @@ def test_exports_match_header():
 
 
 def test_abi_version_and_status_strings():
-    assert nf4.abi_version() == 3
+    assert nf4.abi_version() == 4
     for s in range(8):
         assert nf4.status_str(s)
     assert "unknown" in nf4.status_str(99)
@@ -238,6 +238,48 @@ def test_quantize_error_validation():
     assert call(desc(), ws=A) == nf4.NF4_ERR_ALIAS                       # workspace over the codes
     assert call(desc(), err=D + 16) == nf4.NF4_ERR_ALIAS                 # err inside the workspace
     assert call(desc(codes=C + 64)) == nf4.NF4_ERR_ALIAS
+
+
+def test_error_batch_validation():
+    v = ctypes.c_void_p
+    I64 = ctypes.c_int64
+
+    def arrs(shapes, ptrs):
+        n = len(shapes)
+        return ((v * max(n, 1))(*ptrs), (I64 * max(n, 1))(*[r for r, _ in shapes]),
+                (I64 * max(n, 1))(*[c for _, c in shapes]))
+
+    def call(shapes, ptrs, n=None, dq=0, cb=0, err=E, ws=D, wsb=1 << 20):
+        W, R, K = arrs(shapes, ptrs)
+        return lib.nf4_layer_error_batch(W, R, K, len(shapes) if n is None else n, dq, cb, v(err), v(ws), wsb, None)
+
+    def wsb(shapes):
+        _, R, K = arrs(shapes, [0] * len(shapes))
+        b = ctypes.c_size_t()
+        st = lib.nf4_error_batch_workspace_bytes(R, K, len(shapes), ctypes.byref(b))
+        return st, b.value
+
+    two = [(128, 128), (64, 4096)]
+    # 128*128/64 = 256 blocks = 1 group; 64*4096/64 = 4096 blocks = 16 groups: 17 slots of 16 bytes
+    assert wsb(two) == (nf4.NF4_OK, 512)
+    assert wsb([(128, 100)])[0] == nf4.NF4_ERR_SHAPE
+    assert lib.nf4_error_batch_workspace_bytes(None, None, 1, ctypes.byref(ctypes.c_size_t())) == nf4.NF4_ERR_NULL
+    assert lib.nf4_error_batch_workspace_bytes(None, None, 0, None) == nf4.NF4_ERR_NULL
+    assert call([], [], n=0) == nf4.NF4_OK                                 # nothing to do
+    assert call(two, [A, B], n=-1) == nf4.NF4_ERR_ARG
+    assert call(two, [A, B], dq=128) == nf4.NF4_ERR_ARG
+    assert call(two, [A, B], cb=7) == nf4.NF4_ERR_ARG
+    assert call([(128, 128), (64, 100)], [A, B]) == nf4.NF4_ERR_SHAPE
+    assert call(two, [A, 0]) == nf4.NF4_ERR_NULL                           # a non-empty linear without W
+    assert call(two, [A, B], err=0) == nf4.NF4_ERR_NULL
+    assert call(two, [A, B], ws=0, wsb=0) == nf4.NF4_ERR_WORKSPACE
+    assert call(two, [A, B], wsb=511) == nf4.NF4_ERR_WORKSPACE
+    assert call(two, [A, B + 4]) == nf4.NF4_ERR_ALIGN
+    assert call(two, [A, B], ws=D + 8) == nf4.NF4_ERR_ALIGN
+    assert call(two, [A, B], err=E + 4) == nf4.NF4_ERR_ALIGN
+    assert call(two, [A, B], err=B + 64) == nf4.NF4_ERR_ALIAS              # err inside W[1]
+    assert call(two, [A, B], ws=A + 256) == nf4.NF4_ERR_ALIAS              # workspace inside W[0]
+    assert call(two, [A, B], err=D + 8) == nf4.NF4_ERR_ALIAS               # err inside the workspace
 
 
 def test_stack_validation():

@@ -9,7 +9,8 @@ benchmark uses; the oracle checks what it can compute at that size:
   * dL1 and dL2 over all tokens: every token contributes its own term, so the
     oracle's gradients of consecutive token chunks are added up.
 The 280-linear stack checks the per-linear errors of sampled linears against
-the oracle and the top-K selection against the errors it ranks.
+the oracle, the batched pass over all 280 against the per-linear errors bit
+for bit, and the top-K selection against the errors it ranks.
 Tolerances are those of the other parity tests.
 """
 import numpy as np
@@ -134,17 +135,23 @@ def test_c4_stack_error_topk():
     slots = torch.empty(n, 2, dtype=torch.float64, device=DEV)
     ws = torch.empty(nf4.workspace_bytes(nf4.NF4_OP_ERROR, 0, synth.C4_FFN, synth.C4_HIDDEN, 1),
                      dtype=torch.uint8, device=DEV)
-    kept = {}
+    kept, Ws = {}, []
     for lin in stack:
         W = synth.c4_weight(lin, device=DEV)
         nf4.layer_error(W, 0, out=slots[lin.index], ws=ws[: nf4.workspace_bytes(nf4.NF4_OP_ERROR, 0, lin.rows,
                                                                                 lin.cols, 1)])
+        Ws.append(W)   # all 280 weights stay resident (50.75 GB) for the batched pass below
         if lin.index in sample:
             kept[lin.index] = W.cpu().numpy()
         if lin.index % 40 == 39:
             torch.cuda.synchronize()
             say(f"  {lin.index + 1} linears done")
     errors = slots[:, 0].contiguous()
+    say("  the same pass batched (nf4_layer_error_batch, 64 linears per launch pair)")
+    eb = nf4.layer_error_batch(Ws, 0)
+    torch.cuda.synchronize()
+    del Ws
+    assert np.array_equal(eb.cpu().numpy().view(np.uint64), errors.cpu().numpy().view(np.uint64))
     top = nf4.topk(errors, synth.C4_TOPK).cpu().numpy().tolist()
     e = errors.cpu().numpy()
     say(f"  top-{synth.C4_TOPK}: {top}, errors {np.round(e[top], 5).tolist()}")

@@ -187,6 +187,35 @@ def test_quantize_error_one_pass(codebook, dq, err_dq):
             1e-6 * oracle.layer_error(W, 64, err_dq, codebook)
 
 
+@pytest.mark.parametrize("codebook", ["nf4", "int4"])
+@pytest.mark.parametrize("dq", [0, 256])
+def test_layer_error_batch(codebook, dq):
+    """nf4_layer_error_batch over 70 linears (two launch pairs: 64 + 6): every error bit for bit what
+    nf4_layer_error gives that linear; a few also against the oracle."""
+    rng = np.random.default_rng(21)
+    shapes = [(4, 128), (7, 64 * 37), (0, 64), (640, 1280), (1088, 4096), (3, 64)]
+    shapes += [(int(rng.integers(1, 40)), 64 * int(rng.integers(1, 70))) for _ in range(64)]
+    Ws = []
+    for i, (r, c) in enumerate(shapes):
+        W = (rng.standard_t(3 + i % 5, (r, c)) * 0.02).astype(np.float32)
+        if i == 5:
+            W[:] = 0.0                                    # an all-zero linear: error 0
+        Ws.append(W)
+    Wd = [dev(W) for W in Ws]
+    got = nf4.layer_error_batch(Wd, dq, codebook=codebook).cpu().numpy()
+    assert got.shape == (len(shapes),)
+    for i, W in enumerate(Wd):
+        one = nf4.layer_error(W, dq, codebook=codebook).cpu().numpy()[0]
+        assert got.view(np.uint64)[i] == np.float64(one).view(np.uint64), (i, shapes[i], got[i], one)
+    assert got[2] == 0.0 and got[5] == 0.0
+    for i in (0, 1, 3, 4):
+        want = oracle.layer_error(Ws[i], 64, dq, codebook)
+        say(f"  batch {codebook} dq={dq} {shapes[i]}: gpu {got[i]:.12g} oracle {want:.12g}")
+        assert abs(got[i] - want) <= 1e-6 * want
+    # an empty batch does nothing
+    assert nf4.layer_error_batch([], dq).numel() == 0
+
+
 def test_topk():
     rng = np.random.default_rng(5)
     for n, k in ((280, 8), (144, 29), (1000, 1000), (5, 1), (3000, 17), (1, 1), (1024, 5), (1025, 3)):
