@@ -322,8 +322,10 @@ nf4_status nf4_matmul(const nf4_tensor *W, int32_t transpose, const uint16_t *A,
  * (dq_group 256).  This is the ranking quantity of AQLoRA's profiling pass
  * (section 3.1; the page's equation is missing, the relative Frobenius norm
  * is the reading).  codebook as in nf4_tensor (NF4 for the ranking; the
- * others measure the comparison at identical storage).  fp32 per element,
- * fp64 across blocks, fixed reduction order.  err_dev: device double[1].  ws: nf4_workspace_bytes(NF4_OP_ERROR).
+ * others measure the comparison at identical storage).  The decoded value is
+ * fp32 as the format defines; the difference and the squares are fp64, each
+ * square added with a fused multiply-add in a fixed order, and the per-group
+ * sums are added in a fixed order.  err_dev: device double[1].  ws: nf4_workspace_bytes(NF4_OP_ERROR).
  * Errors: NF4_ERR_NULL, _SHAPE, _ARG, _ALIGN, _WORKSPACE, _HIP.
  */
 nf4_status nf4_layer_error(const float *W, int64_t rows, int64_t cols, int32_t block,
