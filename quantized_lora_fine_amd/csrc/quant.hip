@@ -135,8 +135,8 @@ struct QStage {
 
 // One weight's terms of the error, added to the running sums: the decoded
 // value wh = fl32(table[c] * sc) is fp32 as the format defines; the difference
-// (exact in fp64) and both squares are fp64 (squares of fp32 weights can leave
-// the fp32 range), each square added with one fused multiply-add.  Both error
+// of the two fp32 values and both squares are fp64 (squares of fp32 weights can
+// leave the fp32 range), each square added with one fused multiply-add.  Both error
 // kernels add the weights in the same order (round, quad, element), so their
 // per-group partial sums agree bit for bit.
 __device__ __forceinline__ void error_term(float w, float wh, double& dsum, double& wsum) {
@@ -661,15 +661,25 @@ hipError_t launch_error(const float* W, int64_t nblocks, bool dq, double* part, 
 
 hipError_t launch_error_batch(const float* const* W, const int64_t* rows, const int64_t* cols, int32_t n, bool dq,
                               double* part, double* err, const NF4Enc& c, hipStream_t st) {
+  // a launch takes up to kErrBatch linears and at most 2^24 groups (its
+  // 256-thread workgroups then stay within a 32-bit work-item count)
+  constexpr int64_t kMaxSlots = (int64_t)1 << 24;
   int64_t slot = 0;  // first partial slot of the chunk
-  for (int32_t c0 = 0; c0 < n; c0 += kErrBatch) {
+  for (int32_t c0 = 0; c0 < n;) {
     ErrBatch b{};
-    b.n = min(kErrBatch, n - c0);
+    b.n = 0;
     b.g0[0] = 0;
-    for (int i = 0; i < b.n; ++i) {
-      b.W[i] = W[c0 + i];
-      b.nblocks[i] = rows[c0 + i] * cols[c0 + i] / 64;
-      b.g0[i + 1] = b.g0[i] + (b.nblocks[i] + 255) / 256;
+    while (b.n < kErrBatch && c0 + b.n < n) {
+      const int64_t nblocks = rows[c0 + b.n] * cols[c0 + b.n] / 64;
+      const int64_t end = b.g0[b.n] + (nblocks + 255) / 256;
+      if (end > kMaxSlots) {
+        if (b.n == 0) return hipErrorInvalidValue;  // one linear beyond 2^24 groups (2^38 weights)
+        break;
+      }
+      b.W[b.n] = W[c0 + b.n];
+      b.nblocks[b.n] = nblocks;
+      b.g0[b.n + 1] = end;
+      ++b.n;
     }
     const int64_t slots = b.g0[b.n];
     if (slots > 0) {
@@ -683,6 +693,7 @@ hipError_t launch_error_batch(const float* const* W, const int64_t* rows, const 
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     slot += slots;
+    c0 += b.n;
   }
   return hipSuccess;
 }
