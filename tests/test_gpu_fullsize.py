@@ -2,7 +2,7 @@
 
 The layer workloads run at their real shapes in the launch configuration the
 benchmark uses; the oracle checks what it can compute at that size:
-  * codes, scales and dequantized weights over the whole matrix, bit-exact,
+  * codes, scales and dequantized weights (fp32 and bf16) over the whole matrix, bit-exact,
     and the layer error from the same one-pass quantize within 1e-6;
   * Y and dX on sampled token rows (each output row depends only on its own
     input row, so the oracle runs on those rows alone);
@@ -88,7 +88,10 @@ def check_layer_fullsize(layer, n_rows=16, chunk=1024):
     check_quant(q, ref)
     wh = oracle.dequantize(ref)
     assert np.array_equal(nf4.dequantize(q).cpu().numpy().view(np.uint32), wh.view(np.uint32)), "dequantized W"
-    del q
+    # bf16 output: at c5 the dequantize kernel's grid-stride loop takes several rounds
+    whb = nf4.dequantize(q, bf16=True).cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(whb, oracle.dequantize_bf16_bits(ref)), "dequantized W, bf16"
+    del q, whb
     say("  oracle layer error")
     got, want = float(err.cpu()[0]), oracle.layer_error(W, 64, dq)
     say(f"  error: gpu {got:.12g} oracle {want:.12g}")
