@@ -104,7 +104,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only (the layer runs on a single MI355X); "
+        print("bench.py: measures one GPU only (the layer runs on a single MI355X); "
               "multi-GPU runs are not supported", file=sys.stderr)
         sys.exit(2)
 
