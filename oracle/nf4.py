@@ -184,10 +184,25 @@ def dequantize(q: NF4Quant) -> np.ndarray:
     return w.astype(np.float32).reshape(q.rows, q.cols)
 
 
+def bf16_bits(w) -> np.ndarray:
+    """bf16 round-to-nearest-even of fp32 values, as uint16 bit patterns.
+
+    "QLoRA: How to fine-tune large language models with less memory", section
+    "1. NormalFloat": the stored weights are reconstructed into bf16 for the
+    matmul.  bf16 keeps the sign, the 8 exponent bits and the top 7 mantissa
+    bits of fp32; the value is rounded to the nearer of the two neighbouring
+    bf16 values, the one with an even last mantissa bit on an exact tie
+    (IEEE round-to-nearest-even, the rounding the pages leave implicit).
+    Subnormals are kept; values past the largest finite bf16 go to infinity.
+    The library routine (torch's fp32 -> bfloat16 conversion) is one step.
+    """
+    t = torch.from_numpy(np.ascontiguousarray(np.asarray(w, dtype=np.float32))).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
 def dequantize_bf16_bits(q: NF4Quant) -> np.ndarray:
-    """The bf16 operand form of w_hat: round-to-nearest-even of the fp32 value, as uint16 bits."""
-    w = torch.from_numpy(dequantize(q)).to(torch.bfloat16)
-    return w.view(torch.int16).numpy().view(np.uint16)
+    """The bf16 operand form of w_hat: bf16_bits of the fp32 dequantized weight."""
+    return bf16_bits(dequantize(q))
 
 
 def quantize_residual(W, block: int = BLOCK, dq_group: int = 0, codebook: str = "nf4"):
@@ -258,8 +273,11 @@ def topk(errors, k: int) -> list[int]:
     """Indices of the k largest errors, largest first; equal errors -> lower index first.
 
     AQLoRA summary, section 3.2: a fixed top-K cut keeps the highest-error
-    layers at high precision.
+    layers at high precision.  The pages assume finite weights; an error that
+    is NaN (a weight with an Inf or NaN in it) ranks above every number, and
+    NaNs among themselves by index (the reading taken: the layer that cannot
+    be measured is the first one kept out of 4-bit storage).
     """
     e = [float(v) for v in errors]
-    order = sorted(range(len(e)), key=lambda i: (-e[i], i))
+    order = sorted(range(len(e)), key=lambda i: (0, 0.0, i) if math.isnan(e[i]) else (1, -e[i], i))
     return order[:k]

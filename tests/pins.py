@@ -494,6 +494,96 @@ def pin_topk(topk_fn=onf4.topk, seed=17):
     assert got == want
 
 
+def pin_topk_nan(topk_fn=onf4.topk, seed=18):
+    """A NaN error (non-finite weights) ranks above every number, +inf included; NaNs among
+    themselves and equal numbers by index.  Brute force over all pairs."""
+    rng = np.random.default_rng(seed)
+    e = rng.integers(0, 6, 60).astype(np.float64) / 3.0
+    e[[4, 17, 40]] = np.nan
+    e[[9, 33]] = np.inf
+    e[25] = -0.0
+
+    def beats(j, i):
+        nj, ni = math.isnan(e[j]), math.isnan(e[i])
+        if nj != ni:
+            return nj
+        if nj or e[j] == e[i]:
+            return j < i
+        return e[j] > e[i]
+    rank = [sum(1 for j in range(len(e)) if beats(j, i)) for i in range(len(e))]
+    assert sorted(rank) == list(range(len(e)))
+    for k in (1, 3, 5, len(e)):
+        assert topk_fn(e, k) == [rank.index(p) for p in range(k)], k
+
+
+# ---------------------------------------------------------------------------
+# bf16 operand rounding
+# ---------------------------------------------------------------------------
+
+def bf16_nearest_bits(bits: int) -> int:
+    """bf16 bits of the fp32 value with these bits, by exact rational comparison.
+
+    The two bf16 candidates are the fp32 patterns with the low 16 bits cleared
+    (toward zero) and the next one away from zero (2^128 standing in for
+    infinity, as rounding with an unbounded exponent range and then overflowing
+    gives); the nearer wins, and on an exact tie the one whose last bf16
+    mantissa bit is 0.  Infinities map to themselves."""
+    sign, mag = bits & 0x80000000, bits & 0x7FFFFFFF
+    assert mag <= 0x7F800000, "finite or infinite values only"
+    if mag == 0x7F800000:
+        return (sign | mag) >> 16
+
+    def value(m):
+        if m >= 0x7F800000:
+            return Fraction(2) ** 128
+        e, f = m >> 23, m & 0x7FFFFF
+        return Fraction(f, 1 << 23) * Fraction(2) ** -126 if e == 0 else \
+            (1 + Fraction(f, 1 << 23)) * Fraction(2) ** (e - 127)
+    lo = mag & 0xFFFF0000
+    hi = lo + 0x10000
+    v, vl, vh = value(mag), value(lo), value(hi)
+    if v - vl < vh - v or (v - vl == vh - v and (lo >> 16) % 2 == 0):
+        out = lo
+    else:
+        out = hi
+    return (sign | min(out, 0x7F800000)) >> 16
+
+
+# hand-built fp32 patterns: ties to even and to odd, one below and one above a tie, a carry into the
+# exponent, subnormals (including a carry into the smallest normal), +-0, negatives, overflow to inf
+BF16_CASES = [
+    0x3F808000, 0x3F818000, 0x3F807FFF, 0x3F808001, 0x3F7FFFFF, 0x3FFF8000, 0x3F800000,
+    0x00008000, 0x00018000, 0x0000FFFF, 0x007FFFFF, 0x007F8000, 0x00000001, 0x00000000, 0x80000000,
+    0xBF818000, 0xBF808000, 0x80018000, 0x807FFFFF, 0x7F7F7FFF, 0x7F7F8000, 0x7F7FFFFF, 0xFF7F8000,
+    0x7F800000, 0xFF800000, 0x3E9A8000, 0x3E9B8000,
+]
+
+
+def pin_bf16_rounding(bf16_fn=onf4.bf16_bits, dequantize_bf16_fn=onf4.dequantize_bf16_bits,
+                      quantize_fn=onf4.quantize, dequantize_fn=onf4.dequantize, seed=22):
+    """The bf16 form of the dequantized weight is round-to-nearest-even of its fp32 value
+    ("1. NormalFloat": weights reconstructed into bf16): the hand-built cases above, random
+    finite fp32 patterns of every exponent, and the dequantized weights of quantized tensors
+    (with and without double quantization), each against exact rational rounding."""
+    cases = np.array(BF16_CASES, np.uint32)
+    got = bf16_fn(cases.view(np.float32))
+    want = np.array([bf16_nearest_bits(int(b)) for b in cases], np.uint16)
+    assert np.array_equal(got, want), [(hex(c), hex(g), hex(w)) for c, g, w in zip(cases, got, want) if g != w]
+    rng = np.random.default_rng(seed)
+    r = rng.integers(0, 1 << 32, 4000, dtype=np.uint64).astype(np.uint32)
+    r = r[(r & 0x7F800000) != 0x7F800000]           # finite only
+    r[:200] = (r[:200] & 0xFFFF0000) | 0x8000        # exact ties
+    got = bf16_fn(r.view(np.float32))
+    want = np.array([bf16_nearest_bits(int(b)) for b in r], np.uint16)
+    assert np.array_equal(got, want)
+    W = (rng.standard_normal((8, 256)) * 0.02).astype(np.float32)
+    for dq in (0, 256):
+        q = quantize_fn(W, 64, dq)
+        wh = dequantize_fn(q).reshape(-1).view(np.uint32)
+        want = np.array([bf16_nearest_bits(int(b)) for b in wh], np.uint16)
+        assert np.array_equal(dequantize_bf16_fn(q).reshape(-1), want), dq
+
+
 # ---------------------------------------------------------------------------
 # other 4-bit codebooks (int4, fp4) through the same encoder and decoder
 # ---------------------------------------------------------------------------
@@ -600,5 +690,6 @@ ALL_PINS = [
     pin_dq_codes_unchanged, pin_dq_exact, pin_dq_bound, pin_pack, pin_storage,
     pin_fwd_bruteforce, pin_fwd_merge, pin_fwd_special, pin_bwd_finite_diff, pin_bwd_special,
     pin_error_bruteforce, pin_error_zero_on_grid, pin_error_tails, pin_counts, pin_topk,
-    pin_codebook_tables, pin_codebook_encoders, pin_codebook_roundtrip, pin_residual,
+    pin_codebook_tables, pin_codebook_encoders, pin_codebook_roundtrip, pin_residual, pin_bf16_rounding,
+    pin_topk_nan,
 ]

@@ -199,3 +199,22 @@ def test_mistake_residual():
         q1 = oracle.quantize(W, block, dq, codebook)
         return q1, oracle.quantize(W, block, dq, codebook)
     assert _fails(pins.pin_residual, quantize_res_fn=twice)
+
+
+def test_mistake_bf16_truncation():
+    # bf16 by dropping the low 16 bits, or rounding ties away from zero
+    trunc = lambda w: (np.asarray(w, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert _fails(pins.pin_bf16_rounding, bf16_fn=trunc)
+    away = lambda w: ((np.asarray(w, np.float32).view(np.uint32).astype(np.uint64) + 0x8000) >> 16).astype(np.uint16)
+    assert _fails(pins.pin_bf16_rounding, bf16_fn=away)
+    # the bf16 form of the dequantized weight taken by truncation
+    deq_trunc = lambda q: trunc(oracle.dequantize(q))
+    assert _fails(pins.pin_bf16_rounding, dequantize_bf16_fn=deq_trunc)
+
+
+def test_mistake_topk_nan_last():
+    # NaN treated as the smallest error (numpy's argsort places it last)
+    def nan_last(e, k):
+        e = np.asarray(e, np.float64)
+        return [int(i) for i in np.lexsort((np.arange(e.size), -np.nan_to_num(e, nan=-np.inf)))[:k]]
+    assert _fails(pins.pin_topk_nan, nan_last)
