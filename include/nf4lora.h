@@ -44,8 +44,12 @@
 extern "C" {
 #endif
 
-#define NF4LORA_ABI_VERSION 4
+#define NF4LORA_ABI_VERSION 5
 
+/*
+ * Status codes.  Values 0..7 are fixed since the first release of this ABI;
+ * NF4_ERR_NONFINITE was appended later, so it follows NF4_ERR_ARG.
+ */
 typedef enum nf4_status {
   NF4_OK = 0,
   NF4_ERR_NULL = 1,       /* a required pointer is NULL */
@@ -54,7 +58,8 @@ typedef enum nf4_status {
   NF4_ERR_WORKSPACE = 4,  /* workspace NULL or smaller than nf4_workspace_bytes() */
   NF4_ERR_ALIAS = 5,      /* an output buffer overlaps an input buffer */
   NF4_ERR_HIP = 6,        /* a HIP runtime call or kernel launch failed */
-  NF4_ERR_ARG = 7         /* unsupported option (block size, group size, op id) */
+  NF4_ERR_ARG = 7,        /* unsupported option (block size, group size, op id) */
+  NF4_ERR_NONFINITE = 8   /* nf4_check_finite found an infinity or a NaN */
 } nf4_status;
 
 /*
@@ -102,7 +107,7 @@ typedef struct nf4_tensor {
 enum { NF4_CODEBOOK_NF4 = 0, NF4_CODEBOOK_INT4 = 1, NF4_CODEBOOK_FP4 = 2 };
 
 /* Operation ids for nf4_workspace_bytes. */
-enum { NF4_OP_FWD = 1, NF4_OP_BWD = 2, NF4_OP_ERROR = 3 };
+enum { NF4_OP_FWD = 1, NF4_OP_BWD = 2, NF4_OP_ERROR = 3, NF4_OP_CHECK = 4 };
 
 /* ABI version of the loaded library (NF4LORA_ABI_VERSION). */
 int nf4_abi_version(void);
@@ -144,6 +149,26 @@ nf4_status nf4_tensor_bytes(int64_t rows, int64_t cols, int32_t block, int32_t d
                             size_t *codes_bytes, size_t *absmax_bytes, size_t *dq_scale_bytes);
 
 /*
+ * Non-finite input.  The pages define the format for real-valued weights
+ * only; every pass over an fp32 W (nf4_quantize, nf4_quantize_error,
+ * nf4_layer_error, nf4_layer_error_batch, nf4lora_merge) takes finite values
+ * as a precondition and does not check it: an Inf or NaN weight gives
+ * unspecified codes and scales for its block and a NaN error for its layer
+ * (nf4_topk ranks NaN errors first).  The checked mode is this call, made
+ * before the pass:
+ *
+ * nf4_check_finite scans W (device fp32, `count` values) and returns NF4_OK
+ * when every value is finite, NF4_ERR_NONFINITE when any is an infinity or a
+ * NaN.  Unlike every other entry point it SYNCHRONIZES `stream` (it reads its
+ * answer back to the host), so it cannot be captured into a graph.
+ *   ws: nf4_workspace_bytes(NF4_OP_CHECK, ...) bytes (256), 16-byte aligned,
+ *       not overlapping W.
+ * count == 0 returns NF4_OK without a launch.  Errors: NF4_ERR_NULL, _SHAPE
+ * (count < 0), _ALIGN, _ALIAS, _WORKSPACE, _HIP, _NONFINITE.
+ */
+nf4_status nf4_check_finite(const float *W, int64_t count, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Blockwise NF4 quantization of W (device fp32 [rows][cols], finite values)
  * into the buffers of *q ("1. NormalFloat" and "2. Double quantization",
  * QLoRA blog):
@@ -152,8 +177,12 @@ nf4_status nf4_tensor_bytes(int64_t rows, int64_t cols, int32_t block, int32_t d
  *   code = the nearest table value to x, the lower code on an exact tie;
  *   with dq_group = 256, per group: S = fl32(max a_b / 255),
  *   c8 = min(255, round-half-even(fl32(a_b / S))) (0 when S = 0).
- * Codes do not depend on dq_group.  Errors: NF4_ERR_NULL, _SHAPE, _ARG,
- * _ALIGN, _ALIAS, _HIP.
+ * Codes do not depend on dq_group.  rows * cols is at most
+ * (2^24 - 1) * 2^14 (about 2.7e11 weights: one launch of 256-thread
+ * workgroups, one per 16384 weights, stays below 2^32 work-items; the same
+ * bound applies to nf4_quantize_error, nf4_layer_error and each linear of
+ * nf4_layer_error_batch).  Errors: NF4_ERR_NULL, _SHAPE, _ARG, _ALIGN,
+ * _ALIAS, _HIP.
  */
 nf4_status nf4_quantize(const float *W, const nf4_tensor *q, void *stream);
 
@@ -167,7 +196,8 @@ nf4_status nf4_dequantize(const nf4_tensor *q, void *W_out, int32_t out_is_bf16,
 /*
  * Workspace bytes for an operation (host output *bytes).
  *   op = NF4_OP_FWD or NF4_OP_BWD: M tokens, W [rows][cols], rank r;
- *   op = NF4_OP_ERROR: W [rows][cols] (M and r ignored).
+ *   op = NF4_OP_ERROR: W [rows][cols] (M and r ignored);
+ *   op = NF4_OP_CHECK: nf4_check_finite (all sizes ignored).
  * Errors: NF4_ERR_NULL, _SHAPE, _ARG.
  */
 nf4_status nf4_workspace_bytes(int32_t op, int64_t M, int64_t rows, int64_t cols, int32_t r,
@@ -377,7 +407,10 @@ nf4_status nf4_error_batch_workspace_bytes(const int64_t *rows, const int64_t *c
 /*
  * The protected set of AQLoRA's precision allocation (section 3.2): indices
  * of the k largest of n errors (device double[n]), largest first, equal
- * errors ordered by lower index, written to device int32 idx_dev[k].
+ * errors ordered by lower index, written to device int32 idx_dev[k].  A NaN
+ * error (the layer of a non-finite weight) ranks above every number, NaNs
+ * among themselves by index, so the order is total and idx_dev is always a
+ * set of k distinct indices.
  * 0 <= k <= n <= 65536.  Errors: NF4_ERR_NULL, _SHAPE, _ALIGN, _HIP.
  */
 nf4_status nf4_topk(const double *err_dev, int32_t n, int32_t k, int32_t *idx_dev, void *stream);
@@ -388,6 +421,20 @@ nf4_status nf4_topk(const double *err_dev, int32_t n, int32_t k, int32_t *idx_de
  * returns -1 for rho outside [0, 1] or n < 0.
  */
 int32_t nf4_protect_count(double rho, int32_t n);
+
+/*
+ * Measurement aid, not part of the layer: the bf16 matrix-core rate with no
+ * memory or LDS traffic, the ceiling the fused GEMM's MFMA work is compared
+ * with beside the dense peak.  Launches `workgroups` workgroups of 512
+ * threads; every wave issues iters * 8 v_mfma_f32_32x32x16_bf16 (32768 flops
+ * each: 2.62e5 * iters flops per wave; iters rounded up to an even count) on
+ * eight independent accumulators with
+ * pseudo-random bf16 operands, and writes one float per thread to out_dev
+ * (device float[workgroups * 512]) so the work is kept.  Asynchronous.
+ * Errors: NF4_ERR_NULL, _SHAPE (iters < 1, workgroups < 1 or > 2^20), _ALIGN,
+ * _HIP.
+ */
+nf4_status nf4_probe_mfma_peak(int32_t iters, int32_t workgroups, float *out_dev, void *stream);
 
 #ifdef __cplusplus
 }

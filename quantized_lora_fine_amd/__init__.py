@@ -23,8 +23,9 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_WORKSPACE, NF4_ERR_ALIAS, NF4_ERR_HIP, NF4_ERR_ARG = range(8)
-NF4_OP_FWD, NF4_OP_BWD, NF4_OP_ERROR = 1, 2, 3
+(NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_WORKSPACE, NF4_ERR_ALIAS, NF4_ERR_HIP, NF4_ERR_ARG,
+ NF4_ERR_NONFINITE) = range(9)
+NF4_OP_FWD, NF4_OP_BWD, NF4_OP_ERROR, NF4_OP_CHECK = 1, 2, 3, 4
 CODEBOOKS = {"nf4": 0, "int4": 1, "fp4": 2}
 BLOCK = 64
 DQ_GROUP = 256
@@ -75,6 +76,8 @@ _SIGS = {
                                         ctypes.c_int),
     "nf4_codebook_values": ([_i32, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
     "nf4_topk": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
+    "nf4_check_finite": ([_vp, _i64, _vp, _sz, _vp], ctypes.c_int),
+    "nf4_probe_mfma_peak": ([_i32, _i32, _vp, _vp], ctypes.c_int),
     "nf4_protect_count": ([_f64, _i32], _i32),
     "nf4lora_merge": ([_vp, _T, _i64, _i64, _vp, _vp, _i32, _f32, _vp, _i32, _vp], ctypes.c_int),
     "nf4_stack_workspace_bytes": ([_LP, _i32, _i64, ctypes.POINTER(_sz)], ctypes.c_int),
@@ -359,6 +362,24 @@ def matmul(q: NF4Weight, A: torch.Tensor, transpose: bool = False, A2: torch.Ten
     _check(_lib.nf4_matmul(ctypes.byref(q.desc), 1 if transpose else 0, _ptr(_u16(A)), M,
                            _ptr(A2), _ptr(B2), R, _ptr(C), _stream()), "nf4_matmul")
     return C
+
+
+def check_finite(W: torch.Tensor, ws: torch.Tensor | None = None) -> bool:
+    """nf4_check_finite (synchronizes the stream): True when every value of the cuda fp32 W is finite."""
+    assert W.dtype == torch.float32 and W.is_cuda and W.is_contiguous()
+    if ws is None:
+        ws = torch.empty(workspace_bytes(NF4_OP_CHECK, 0, 0, 0, 0), dtype=torch.uint8, device=W.device)
+    st = _lib.nf4_check_finite(_ptr(W), W.numel(), _ptr(ws), ws.numel(), _stream())
+    if st == NF4_ERR_NONFINITE:
+        return False
+    _check(st, "nf4_check_finite")
+    return True
+
+
+def probe_mfma_peak(iters: int, workgroups: int, out: torch.Tensor) -> None:
+    """nf4_probe_mfma_peak: 8 * iters bf16 MFMAs (32x32x16) per wave, 8 waves per workgroup (asynchronous)."""
+    assert out.dtype == torch.float32 and out.is_cuda and out.numel() >= workgroups * 512
+    _check(_lib.nf4_probe_mfma_peak(int(iters), int(workgroups), _ptr(out), _stream()), "nf4_probe_mfma_peak")
 
 
 def topk(errors: torch.Tensor, k: int, out: torch.Tensor | None = None) -> torch.Tensor:

@@ -39,8 +39,8 @@ EXTRA = {"quant.hip": ["-ffp-contract=off"],
          "gemm.hip": ["-ffp-contract=off"],
          "merge.hip": ["-ffp-contract=off"]}
 
-HIP_SOURCES = ["quant.hip", "gemm.hip", "skinny.hip", "merge.hip"]
-CPP_SOURCES = ["api.cpp", "nf4_table.cpp"]
+HIP_SOURCES = ["quant.hip", "gemm.hip", "skinny.hip", "merge.hip", "probe.hip"]
+CPP_SOURCES = ["api.cpp", "nf4_table.cpp", "plan.cpp"]
 
 
 def _run(cmd):

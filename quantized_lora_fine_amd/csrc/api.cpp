@@ -18,6 +18,7 @@ namespace {
 
 constexpr int64_t kBlock = 64;
 constexpr int64_t kGroup = 256;
+constexpr size_t kCheckWorkspace = 256;  // nf4_check_finite: one int flag
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -59,6 +60,12 @@ nf4_status check_shape(int64_t rows, int64_t cols, int32_t block, int32_t dq) {
   if (cols % kBlock != 0) return NF4_ERR_SHAPE;
   if (rows > 0 && cols > (((int64_t)1 << 40) / rows)) return NF4_ERR_SHAPE;
   return NF4_OK;
+}
+
+// The passes over an fp32 W launch one 256-thread workgroup per group of 256
+// blocks: at most kMaxLaunchGroups groups keep a launch below 2^32 work-items.
+nf4_status check_pass_weights(int64_t rows, int64_t cols) {
+  return error_groups(rows, cols) > kMaxLaunchGroups ? NF4_ERR_SHAPE : NF4_OK;
 }
 
 nf4_status check_tensor(const nf4_tensor* q) {
@@ -459,7 +466,8 @@ nf4_status error_batch_shapes(const int64_t* rows, const int64_t* cols, int32_t 
   if (n > 0 && (!rows || !cols)) return NF4_ERR_NULL;
   int64_t slots = 0;
   for (int32_t i = 0; i < n; ++i) {
-    const nf4_status st = check_shape(rows[i], cols[i], kBlock, 0);
+    nf4_status st = check_shape(rows[i], cols[i], kBlock, 0);
+    if (st == NF4_OK) st = check_pass_weights(rows[i], cols[i]);
     if (st != NF4_OK) return st;
     slots += (rows[i] * cols[i] / kBlock + kGroup - 1) / kGroup;
   }
@@ -483,6 +491,7 @@ const char* nf4_status_str(int s) {
     case NF4_ERR_ALIAS: return "NF4_ERR_ALIAS: an output overlaps an input";
     case NF4_ERR_HIP: return "NF4_ERR_HIP: a HIP call or kernel launch failed";
     case NF4_ERR_ARG: return "NF4_ERR_ARG: unsupported option";
+    case NF4_ERR_NONFINITE: return "NF4_ERR_NONFINITE: the weight holds an infinity or a NaN";
     default: return "unknown nf4_status";
   }
 }
@@ -514,6 +523,8 @@ nf4_status nf4_tensor_bytes(int64_t rows, int64_t cols, int32_t block, int32_t d
 
 nf4_status nf4_quantize(const float* W, const nf4_tensor* q, void* stream) {
   nf4_status st = check_tensor(q);
+  if (st != NF4_OK) return st;
+  st = check_pass_weights(q->rows, q->cols);
   if (st != NF4_OK) return st;
   const int64_t n = q->rows * q->cols;
   if (n == 0) return NF4_OK;
@@ -553,6 +564,10 @@ nf4_status nf4_dequantize(const nf4_tensor* q, void* W_out, int32_t out_is_bf16,
 
 nf4_status nf4_workspace_bytes(int32_t op, int64_t M, int64_t rows, int64_t cols, int32_t r, size_t* bytes) {
   if (!bytes) return NF4_ERR_NULL;
+  if (op == NF4_OP_CHECK) {
+    *bytes = kCheckWorkspace;
+    return NF4_OK;
+  }
   if (op == NF4_OP_ERROR) {
     nf4_status st = check_shape(rows, cols, kBlock, 0);
     if (st != NF4_OK) return st;
@@ -629,6 +644,8 @@ nf4_status nf4_layer_error(const float* W, int64_t rows, int64_t cols, int32_t b
                            int32_t codebook, double* err_dev, void* ws, size_t ws_bytes, void* stream) {
   nf4_status st = check_shape(rows, cols, block, dq_group);
   if (st != NF4_OK) return st;
+  st = check_pass_weights(rows, cols);
+  if (st != NF4_OK) return st;
   if (codebook < 0 || codebook >= kCodebooks) return NF4_ERR_ARG;
   if (!err_dev) return NF4_ERR_NULL;
   const int64_t n = rows * cols;
@@ -679,6 +696,8 @@ nf4_status nf4_quantize_error(const float* W, const nf4_tensor* q, int32_t err_d
                               size_t ws_bytes, void* stream) {
   nf4_status st = check_tensor(q);
   if (st != NF4_OK) return st;
+  st = check_pass_weights(q->rows, q->cols);
+  if (st != NF4_OK) return st;
   if (q->residual) return NF4_ERR_ARG;
   if (err_dq_group != 0 && err_dq_group != q->dq_group) return NF4_ERR_ARG;
   if (!err_dev) return NF4_ERR_NULL;
@@ -703,6 +722,22 @@ nf4_status nf4_quantize_error(const float* W, const nf4_tensor* q, int32_t err_d
                                           codebook_consts(q->codebook), (hipStream_t)stream));
 }
 
+nf4_status nf4_check_finite(const float* W, int64_t count, void* ws, size_t ws_bytes, void* stream) {
+  if (count < 0) return NF4_ERR_SHAPE;
+  if (count == 0) return NF4_OK;
+  if (!W) return NF4_ERR_NULL;
+  if (!ws || ws_bytes < kCheckWorkspace) return NF4_ERR_WORKSPACE;
+  if (!aligned16(W) || !aligned16(ws)) return NF4_ERR_ALIGN;
+  if (overlap(rng(W, (size_t)count * 4), rng(ws, kCheckWorkspace))) return NF4_ERR_ALIAS;
+  hipStream_t hs = (hipStream_t)stream;
+  int* flag = (int*)ws;
+  NF4_TRY(launch_check_finite(W, count, flag, hs));
+  int host = 0;
+  NF4_TRY(hipMemcpyAsync(&host, flag, sizeof(int), hipMemcpyDeviceToHost, hs));
+  NF4_TRY(hipStreamSynchronize(hs));
+  return host ? NF4_ERR_NONFINITE : NF4_OK;
+}
+
 nf4_status nf4_topk(const double* err_dev, int32_t n, int32_t k, int32_t* idx_dev, void* stream) {
   if (n < 0 || k < 0 || k > n || n > 65536) return NF4_ERR_SHAPE;
   if (k == 0) return NF4_OK;
@@ -710,6 +745,13 @@ nf4_status nf4_topk(const double* err_dev, int32_t n, int32_t k, int32_t* idx_de
   if (!aligned16(err_dev) || !aligned16(idx_dev)) return NF4_ERR_ALIGN;
   if (overlap(rng(err_dev, (size_t)n * 8), rng(idx_dev, (size_t)k * 4))) return NF4_ERR_ALIAS;
   return hip_status(launch_topk(err_dev, n, k, idx_dev, (hipStream_t)stream));
+}
+
+nf4_status nf4_probe_mfma_peak(int32_t iters, int32_t workgroups, float* out_dev, void* stream) {
+  if (iters < 1 || workgroups < 1 || workgroups > (1 << 20)) return NF4_ERR_SHAPE;
+  if (!out_dev) return NF4_ERR_NULL;
+  if (!aligned16(out_dev)) return NF4_ERR_ALIGN;
+  return hip_status(launch_mfma_peak(iters, workgroups, out_dev, (hipStream_t)stream));
 }
 
 int32_t nf4_protect_count(double rho, int32_t n) {

@@ -31,6 +31,26 @@ hipError_t launch_error(const float* W, int64_t nblocks, bool dq, double* part, 
 hipError_t launch_error_batch(const float* const* W, const int64_t* rows, const int64_t* cols, int32_t n, bool dq,
                               double* part, double* err, const NF4Enc& c, hipStream_t st);
 hipError_t launch_topk(const double* e, int n, int k, int* idx, hipStream_t st);
+// MFMA-only probe: `workgroups` x 512 threads, each wave `iters` rounds of 8
+// v_mfma_f32_32x32x16_bf16; out gets one float per thread.
+hipError_t launch_mfma_peak(int iters, int workgroups, float* out, hipStream_t st);
+// *flag_dev = 1 if any of W[0 .. count) is an infinity or a NaN, else 0.
+hipError_t launch_check_finite(const float* W, int64_t count, int* flag_dev, hipStream_t st);
+
+// The passes over W (quantize, error) run one 256-thread workgroup per group of
+// 256 blocks; a launch holds at most kMaxLaunchGroups groups, so its work-item
+// count (groups * 256) stays below 2^32.  Up to kErrBatch linears share one
+// launch of the batched error pass.
+constexpr int64_t kMaxLaunchGroups = ((int64_t)1 << 24) - 1;
+constexpr int kErrBatch = 64;
+inline int64_t error_groups(int64_t rows, int64_t cols) { return (rows * cols / 64 + 255) / 256; }
+// The next launch of a batched error pass over n linears starts at linear c0
+// and takes the k linears c0 .. c0 + k - 1 (the return value): as many as fit in
+// kErrBatch linears and kMaxLaunchGroups groups.  g0[i] is the first group of
+// linear c0 + i within the launch and g0[k] the launch's group count (g0 has
+// kErrBatch + 1 entries).  Returns 0 when linear c0 alone has more than
+// kMaxLaunchGroups groups.
+int error_batch_chunk(const int64_t* rows, const int64_t* cols, int32_t n, int32_t c0, int64_t* g0);
 
 // Weight source of the fused GEMM: NF4 with fp32 absmax, NF4 with 8-bit
 // double-quantized scales, or a bf16 weight (no quantization).

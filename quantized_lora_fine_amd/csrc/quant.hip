@@ -391,7 +391,6 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
 // Up to kErrBatch linears of one batched error pass, passed by value as a
 // kernel argument (1.6 KB): W and its block count per linear, and the first
 // partial slot of each linear relative to the launch (g0[n] = slots in all).
-constexpr int kErrBatch = 64;
 struct ErrBatch {
   const float* W[kErrBatch];
   int64_t nblocks[kErrBatch];
@@ -533,8 +532,19 @@ __global__ __launch_bounds__(256) void k_error_final_batch(ErrBatch b, const dou
 }
 
 // ---------------------------------------------------------------------------
-// top-K by rank counting: rank(i) = #{j : e_j > e_i or (e_j == e_i and j < i)}
+// top-K by rank counting: rank(i) = #{j : j beats i}.  j beats i when e_j is
+// NaN and e_i is not, or both are NaN and j < i, or both are numbers and
+// e_j > e_i or (e_j == e_i and j < i): a total order in which a NaN error (a
+// weight with an Inf or NaN in it) ranks above every number, so every rank
+// 0 .. n-1 is taken exactly once.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ bool topk_beats(double ej, int j, double ei, int i) {
+  const bool nj = ej != ej, ni = ei != ei;
+  if (nj != ni) return nj;
+  if (nj || ej == ei) return j < i;
+  return ej > ei;
+}
+
 __global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ e, int n, int k,
                                                int* __restrict__ idx) {
   __shared__ double tile[1024];
@@ -546,10 +556,7 @@ __global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ e, int
     if (i < n) {
       const double ei = tile[i];
       int rank = 0;
-      for (int j = 0; j < n; ++j) {
-        const double ej = tile[j];
-        rank += (ej > ei || (ej == ei && j < i)) ? 1 : 0;
-      }
+      for (int j = 0; j < n; ++j) rank += topk_beats(tile[j], j, ei, i) ? 1 : 0;
       if (rank < k) idx[rank] = i;
     }
     return;
@@ -563,14 +570,38 @@ __global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ e, int
       if (t0 + (int)threadIdx.x < n) tile[threadIdx.x] = e[t0 + threadIdx.x];
       __syncthreads();
       const int lim = min(1024, n - t0);
-      for (int jj = 0; jj < lim; ++jj) {
-        const double ej = tile[jj];
-        const int j = t0 + jj;
-        rank += (ej > ei || (ej == ei && j < i)) ? 1 : 0;
-      }
+      for (int jj = 0; jj < lim; ++jj) rank += topk_beats(tile[jj], t0 + jj, ei, i) ? 1 : 0;
     }
     if (i < n && rank < k) idx[rank] = i;
   }
+}
+
+// ---------------------------------------------------------------------------
+// the checked mode's scan: flag = 1 when any weight is an infinity or a NaN
+// (exponent bits all ones).  The flag is cleared by k_flag_clear first; every
+// thread that finds one stores 1 (all stores write the same value).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_flag_clear(int* __restrict__ flag) {
+  if (threadIdx.x == 0) flag[0] = 0;
+}
+
+__global__ __launch_bounds__(256) void k_check_finite(const float* __restrict__ W, int64_t count,
+                                                      int* __restrict__ flag) {
+  const int64_t n4 = count >> 2;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  bool bad = false;
+  for (int64_t t = t0; t < n4; t += stride) {
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)W + t);
+    const u32x4 ex = v & 0x7F800000u;
+    bad |= (ex.x == 0x7F800000u) | (ex.y == 0x7F800000u) | (ex.z == 0x7F800000u) | (ex.w == 0x7F800000u);
+  }
+  // the last count % 4 weights
+  if (t0 < (count & 3)) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, W[n4 * 4 + t0]);
+    bad |= (b & 0x7F800000u) == 0x7F800000u;
+  }
+  if (bad) flag[0] = 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -581,6 +612,7 @@ hipError_t launch_quantize(const float* W, int64_t nblocks, bool dq, uint8_t* co
                            hipStream_t st) {
   const int64_t ng = (nblocks + 255) / 256;
   if (ng == 0) return hipSuccess;
+  if (ng > kMaxLaunchGroups) return hipErrorInvalidValue;
   QStage o1{codes, dq ? nullptr : (float*)absmax, dq ? (uint8_t*)absmax : nullptr, dqs};
   QStage o2{codes2, dq ? nullptr : (float*)absmax2, dq ? (uint8_t*)absmax2 : nullptr, dqs2};
   const dim3 gr((unsigned)ng), bl(256);
@@ -600,6 +632,7 @@ hipError_t launch_quantize_error(const float* W, int64_t nblocks, bool dq, uint8
                                  hipStream_t st) {
   const int64_t ng = (nblocks + 255) / 256;
   if (err_dq && !dq) return hipErrorInvalidValue;
+  if (ng > kMaxLaunchGroups) return hipErrorInvalidValue;
   if (ng > 0) {
     QStage o1{codes, dq ? nullptr : (float*)absmax, dq ? (uint8_t*)absmax : nullptr, dqs};
     const QStage o2{nullptr, nullptr, nullptr, nullptr};
@@ -646,6 +679,7 @@ hipError_t launch_dequantize(const uint8_t* codes, const void* absmax, const flo
 hipError_t launch_error(const float* W, int64_t nblocks, bool dq, double* part, double* err,
                         const NF4Enc& c, hipStream_t st) {
   const int64_t ng = (nblocks + 255) / 256;
+  if (ng > kMaxLaunchGroups) return hipErrorInvalidValue;
   if (ng > 0) {
     if (dq) {
       hipLaunchKernelGGL(k_error_partial<true>, dim3((unsigned)ng), dim3(256), 0, st, W, nblocks, part, c);
@@ -661,25 +695,14 @@ hipError_t launch_error(const float* W, int64_t nblocks, bool dq, double* part, 
 
 hipError_t launch_error_batch(const float* const* W, const int64_t* rows, const int64_t* cols, int32_t n, bool dq,
                               double* part, double* err, const NF4Enc& c, hipStream_t st) {
-  // a launch takes up to kErrBatch linears and at most 2^24 groups (its
-  // 256-thread workgroups then stay within a 32-bit work-item count)
-  constexpr int64_t kMaxSlots = (int64_t)1 << 24;
   int64_t slot = 0;  // first partial slot of the chunk
   for (int32_t c0 = 0; c0 < n;) {
     ErrBatch b{};
-    b.n = 0;
-    b.g0[0] = 0;
-    while (b.n < kErrBatch && c0 + b.n < n) {
-      const int64_t nblocks = rows[c0 + b.n] * cols[c0 + b.n] / 64;
-      const int64_t end = b.g0[b.n] + (nblocks + 255) / 256;
-      if (end > kMaxSlots) {
-        if (b.n == 0) return hipErrorInvalidValue;  // one linear beyond 2^24 groups (2^38 weights)
-        break;
-      }
-      b.W[b.n] = W[c0 + b.n];
-      b.nblocks[b.n] = nblocks;
-      b.g0[b.n + 1] = end;
-      ++b.n;
+    b.n = error_batch_chunk(rows, cols, n, c0, b.g0);
+    if (b.n == 0) return hipErrorInvalidValue;  // one linear beyond kMaxLaunchGroups groups
+    for (int i = 0; i < b.n; ++i) {
+      b.W[i] = W[c0 + i];
+      b.nblocks[i] = rows[c0 + i] * cols[c0 + i] / 64;
     }
     const int64_t slots = b.g0[b.n];
     if (slots > 0) {
@@ -696,6 +719,17 @@ hipError_t launch_error_batch(const float* const* W, const int64_t* rows, const 
     c0 += b.n;
   }
   return hipSuccess;
+}
+
+hipError_t launch_check_finite(const float* W, int64_t count, int* flag_dev, hipStream_t st) {
+  hipLaunchKernelGGL(k_flag_clear, dim3(1), dim3(64), 0, st, flag_dev);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || count == 0) return e;
+  int64_t blocks = ((count >> 2) + 255) / 256;
+  if (blocks > 256 * 16) blocks = 256 * 16;  // 16 workgroups per CU, then a grid-stride loop
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_check_finite, dim3((unsigned)blocks), dim3(256), 0, st, W, count, flag_dev);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(const double* e, int n, int k, int* idx, hipStream_t st) {

@@ -77,6 +77,31 @@ __device__ __forceinline__ float sum_partials(const float* part, int64_t slab, i
 // (vmcnt 0) before the barrier, so they are complete before thread 0 counts
 // this workgroup.  Returns true in the last workgroup of a tile, which then
 // reads every split's partial with ld_shared_partial.
+//
+// Why no release/acquire pair.  In the C++/HIP memory model the partials
+// would be published by a release on the counter increment and read after an
+// acquire by the last arrival.  At agent scope on this chip a release is a
+// write-back of the whole L2 of the issuing XCD and an acquire an invalidate
+// of it, per workgroup: that made these kernels about 5x slower.  The
+// exchange instead relies on three properties of the hardware, each kept in
+// this function and its two helpers:
+//   1. every partial is written and read only with agent-scope atomic stores
+//      and loads (st_/ld_shared_partial), which are coherent across XCDs: the
+//      stores write through the XCD's L2 and the loads do not hit a stale L2
+//      line;
+//   2. s_waitcnt vmcnt(0) before the barrier waits for the acknowledgement of
+//      each thread's stores, which arrives only once the store is visible at
+//      the agent coherence point, so every partial of the workgroup is visible
+//      before thread 0 issues the increment (the signal fence keeps the
+//      compiler from moving the stores past it);
+//   3. the increment is an agent-scope atomic on one counter; the workgroup
+//      that reads nsplit - 1 is ordered after every other increment, hence
+//      after every other workgroup's partials, and its partial loads are
+//      issued only after the increment returned (they depend on s_last
+//      through the barrier and the branch).
+// A change of architecture or of the scopes above needs this argument
+// redone; with a true release/acquire the code would stay correct at the
+// cost above.
 __device__ __forceinline__ bool last_arrival(unsigned* cnt, int nsplit) {
   __shared__ int s_last;
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -648,37 +673,6 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// split-K factor for an NT skinny product over M rows (64 rows per
-// workgroup): about 512 workgroups, each K range a multiple of 128.
-void plan_nt(int64_t M, int K, int* ksplit, int* krange) {
-  const int64_t mblocks = (M + 63) / 64;
-  int64_t ks = (512 + mblocks - 1) / (mblocks > 0 ? mblocks : 1);
-  const int64_t kmax = (K + 127) / 128;
-  if (ks > kmax) ks = kmax;
-  if (ks < 1) ks = 1;
-  int kr = (int)(((K + ks - 1) / ks + 127) / 128 * 128);
-  ks = (K + kr - 1) / kr;
-  *ksplit = (int)ks;
-  *krange = kr;
-}
-
-// split-M factor for a TN skinny product with N output columns (64 per
-// workgroup): about 512 workgroups, token ranges a multiple of 256 (a whole
-// number of chunks for every rank).
-void plan_tn(int64_t M, int N, int* msplit, int64_t* mrange) {
-  const int64_t nblocks = (N + 63) / 64;
-  int64_t ms = (512 + nblocks - 1) / nblocks;
-  const int64_t mmax = (M + 255) / 256;
-  if (ms > mmax) ms = mmax;
-  if (ms < 1) ms = 1;
-  int64_t mr = ((M + ms - 1) / ms + 255) / 256 * 256;
-  if (mr < 256) mr = 256;
-  ms = (M + mr - 1) / mr;
-  if (ms < 1) ms = 1;
-  *msplit = (int)ms;
-  *mrange = mr;
-}
-
 #define NF4K_RP_SWITCH(RP, LAUNCH) \
   switch (RP) {                    \
     case 16: LAUNCH(16); break;    \
@@ -699,16 +693,6 @@ void plan_tn(int64_t M, int N, int* msplit, int64_t* mrange) {
     case 256: LAUNCH(256); break;  \
     default: return hipErrorInvalidValue; \
   }
-
-// whole-K workgroups when the rank is small and there are rows enough for them
-bool skinny_nt_whole(int64_t M, int RP) {
-  if (RP > 64) return false;
-  const int rw = RP <= 16 ? 8 : (RP <= 32 ? 16 : 32);
-  return (M + rw - 1) / rw >= 64;
-}
-
-// all tokens per workgroup when the rank is small and the token count is not tiny
-bool skinny_tn_whole(int64_t M, int RP) { return RP <= 64 && M >= 512; }
 
 hipError_t launch_skinny_nt(const NtArgs& a, int RP, hipStream_t st) {
   if (a.M == 0) return hipSuccess;

@@ -35,9 +35,10 @@ def test_exports_match_header():
 
 
 def test_abi_version_and_status_strings():
-    assert nf4.abi_version() == 4
-    for s in range(8):
-        assert nf4.status_str(s)
+    assert nf4.abi_version() == 5
+    for s in range(9):
+        assert nf4.status_str(s) and "unknown" not in nf4.status_str(s)
+    assert "NONFINITE" in nf4.status_str(nf4.NF4_ERR_NONFINITE)
     assert "unknown" in nf4.status_str(99)
 
 
@@ -356,3 +357,33 @@ def test_residual_validation():
     noptr = desc(rows=128, cols=128, codes=None, absmax=F)
     d.residual = ctypes.pointer(noptr)
     assert st_quant(d) == nf4.NF4_ERR_NULL
+
+
+def test_check_finite_validation():
+    v = ctypes.c_void_p
+    ws = nf4.workspace_bytes(nf4.NF4_OP_CHECK, 0, 0, 0, 0)
+    assert ws >= 4
+    assert lib.nf4_check_finite(v(C), 0, None, 0, None) == nf4.NF4_OK           # nothing to scan
+    assert lib.nf4_check_finite(v(C), -1, v(D), ws, None) == nf4.NF4_ERR_SHAPE
+    assert lib.nf4_check_finite(None, 16, v(D), ws, None) == nf4.NF4_ERR_NULL
+    assert lib.nf4_check_finite(v(C), 16, None, ws, None) == nf4.NF4_ERR_WORKSPACE
+    assert lib.nf4_check_finite(v(C), 16, v(D), ws - 1, None) == nf4.NF4_ERR_WORKSPACE
+    assert lib.nf4_check_finite(v(C + 4), 16, v(D), ws, None) == nf4.NF4_ERR_ALIGN
+    assert lib.nf4_check_finite(v(C), 16, v(C + 32), ws, None) == nf4.NF4_ERR_ALIAS
+
+
+def test_pass_size_bound():
+    """The passes over W accept at most (2^24 - 1) groups of 16384 weights (one launch stays below 2^32
+    work-items); storage sizes are still reported beyond that."""
+    v = ctypes.c_void_p
+    big_rows = (1 << 24) * 256      # x 64 columns = 2^24 groups: one past the bound
+    ok_rows = ((1 << 24) - 1) * 256
+    assert nf4.tensor_bytes(big_rows, 64, 0)[0] == big_rows * 32
+    assert st_quant(desc(rows=big_rows)) == nf4.NF4_ERR_SHAPE
+    assert lib.nf4_layer_error(v(C), big_rows, 64, 64, 0, 0, v(E), v(D), 1 << 40, None) == nf4.NF4_ERR_SHAPE
+    # one group fewer passes the size check and fails later on the workspace size
+    assert lib.nf4_layer_error(v(C), ok_rows, 64, 64, 0, 0, v(E), v(D), 16, None) == nf4.NF4_ERR_WORKSPACE
+    rows = (ctypes.c_int64 * 1)(big_rows)
+    cols = (ctypes.c_int64 * 1)(64)
+    b = ctypes.c_size_t()
+    assert lib.nf4_error_batch_workspace_bytes(rows, cols, 1, ctypes.byref(b)) == nf4.NF4_ERR_SHAPE
