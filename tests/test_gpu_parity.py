@@ -13,7 +13,13 @@ import synth
 
 pytestmark = pytest.mark.gpu
 
-nf4 = pytest.importorskip("quantized_lora_fine_amd")
+try:
+    import quantized_lora_fine_amd as nf4
+except ImportError as exc:
+    # on a GPU machine a missing or broken libnf4lora.so is a failure, not a skip
+    if torch.cuda.is_available():
+        raise
+    pytest.skip(f"libnf4lora.so not loaded: {exc}", allow_module_level=True)
 
 DEV = "cuda"
 TOL_MAX = 2e-2
@@ -222,6 +228,99 @@ def test_topk():
         e = rng.integers(0, 40, n).astype(np.float64) / 13.0
         got = nf4.topk(dev(e), k).cpu().numpy().tolist()
         assert got == oracle.topk(e, k), (n, k)
+
+
+def test_topk_nan():
+    """Errors of non-finite weights are NaN: they rank first, by index, as the oracle orders them."""
+    rng = np.random.default_rng(6)
+    for n, k in ((280, 8), (50, 50), (2000, 30)):
+        e = rng.integers(0, 40, n).astype(np.float64) / 13.0
+        e[rng.choice(n, size=max(2, n // 40), replace=False)] = np.nan
+        e[rng.integers(0, n)] = np.inf
+        got = nf4.topk(dev(e), k).cpu().numpy().tolist()
+        assert got == oracle.topk(e, k), (n, k)
+        assert len(set(got)) == k
+
+
+def test_check_finite():
+    """The checked mode: NF4_ERR_NONFINITE for an infinity or a NaN anywhere (first, middle, in the
+    last count % 4 values), NF4_OK otherwise; finite extremes and subnormals pass."""
+    rng = np.random.default_rng(8)
+    n = 4 * 100003 + 3
+    base = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    base[7] = np.float32(3.4e38)
+    base[9] = np.float32(1e-45)
+    W = dev(base)
+    assert nf4.check_finite(W)
+    assert nf4.check_finite(W[:5])
+    for pos, val in ((0, np.inf), (n // 2, np.nan), (n - 1, -np.inf), (n - 3, np.nan)):
+        b = base.copy()
+        b[pos] = val
+        assert not nf4.check_finite(dev(b)), pos
+        if pos == n - 1:
+            assert nf4.check_finite(dev(b)[: n - 1])    # the bad value is past the count
+
+
+def test_zero_weight_isolates_adapter():
+    """W = 0 (all codes of 0, zero scales, so w_hat = 0): Y = s T L2 and dX = G L1^T, checked at the
+    adapter term's own scale (the base term would otherwise hide it), with and without double quant."""
+    for dq in (0, 256):
+        d = synth.random_case(seed=26 + dq, rows=320, cols=448, M=300, r=16)
+        d["W"] = np.zeros_like(d["W"])
+        Y, T, dX, dL1, dL2 = run_layer(d, 2.0, dq)
+        Yr, Tr, dXr, dL1r, dL2r = oracle_layer(d, 2.0, dq)
+        say(f"W = 0, dq={dq}: max|Y| = {np.max(np.abs(Yr)):.3e}")
+        check_close("Y = s T L2", Y, Yr)
+        check_close("dX = G L1^T", dX, dXr)
+        check_close("dL1", dL1, dL1r)
+        check_close("dL2", dL2, dL2r)
+
+
+def heavy_weight(rng, shape, kind, sigma=0.02):
+    """Weights with the tails of the workloads: Student-t (df 3 or 5) scaled to variance sigma^2, or
+    normal with 0.1 % of the values x20, or a single large spike per row."""
+    if kind in ("t3", "t5"):
+        df = int(kind[1])
+        return (rng.standard_t(df, size=shape) * sigma * np.sqrt((df - 2) / df)).astype(np.float32)
+    W = (rng.standard_normal(shape) * sigma).astype(np.float32)
+    if kind == "outliers":
+        idx = rng.choice(W.size, size=max(1, W.size // 1000), replace=False)
+        W.reshape(-1)[idx] *= np.float32(20)
+    elif kind == "spike":
+        W[np.arange(shape[0]), rng.integers(0, shape[1], shape[0])] = np.float32(50 * sigma)
+    return W
+
+
+@pytest.mark.parametrize("M,o,h,r,dq,kind", [
+    (300, 256, 320, 128, 256, "t3"),        # two 64-column tail chunks
+    (200, 192, 256, 256, 0, "outliers"),    # the largest rank: four tail chunks, split adapter kernels
+    (520, 320, 192, 200, 256, "t5"),        # ragged padded rank 208
+    (2048, 256, 384, 128, 256, "spike"),    # many tokens at a rank past the unsplit kernels
+])
+def test_layer_wide_rank_heavy_tails(M, o, h, r, dq, kind):
+    say(f"wide rank M={M} o={o} h={h} r={r} dq={dq} weights={kind}")
+    d = synth.random_case(seed=500 + r, rows=o, cols=h, M=M, r=r)
+    d["W"] = heavy_weight(np.random.default_rng(600 + r), (o, h), kind)
+    check_layer(d, 2.0, dq)
+
+
+def test_layer_property_sweep():
+    """Seeded draws over the layer's parameter space (h and o multiples of 64 up to 768, M from 1 to
+    700, r from 1 to 256, double quant on or off, four weight distributions), each against the oracle."""
+    rng = np.random.default_rng(2024)
+    kinds = ("normal", "t3", "outliers", "spike")
+    for case in range(14):
+        o, h = 64 * int(rng.integers(1, 13)), 64 * int(rng.integers(1, 13))
+        M = int(rng.integers(1, 701))
+        r = int(rng.choice([1, 2, 8, 15, 16, 17, 33, 64, 65, 100, 128, 200, 256]))
+        dq = int(rng.choice([0, 256]))
+        kind = kinds[case % 4]
+        s = float(rng.choice([0.5, 1.0, 2.0, 16.0 / np.sqrt(r)]))
+        say(f"sweep {case}: M={M} o={o} h={h} r={r} dq={dq} s={s:.3f} weights={kind}")
+        d = synth.random_case(seed=700 + case, rows=o, cols=h, M=M, r=r)
+        if kind != "normal":
+            d["W"] = heavy_weight(rng, (o, h), kind)
+        check_layer(d, s, dq)
 
 
 # ---------------------------------------------------------------------------
