@@ -225,6 +225,29 @@ nf4_status nf4lora_fwd(const nf4_tensor *W, const uint16_t *X, int64_t M,
                        void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * nf4lora_fwd for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results (bit for bit) and errors as nf4lora_fwd, without the
+ * workspace: the library uses a fixed device area of 16 MiB per GPU instead,
+ * created with the library's code object on each GPU it runs on and held
+ * until the process ends.  The call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine).
+ *   - A layer whose forward workspace (nf4_workspace_bytes(NF4_OP_FWD, ...))
+ *     exceeds 16 MiB is rejected with NF4_ERR_WORKSPACE before any HIP call
+ *     (c2-c5 shapes at r <= 64 need 0.07 to 14.5 MiB; r = 256 at M = 16384
+ *     and o = 28672 needs 58 MiB: use nf4lora_fwd there).
+ *   - Every call on a GPU shares that GPU's area, and the area keeps the last
+ *     call's contents; each call clears what must start at zero with a kernel
+ *     of its own (no memset).  Calls that overlap on one GPU (several streams
+ *     or host threads at once) race on the area: serialize them.
+ *   - The first call on a device looks up the area's device address
+ *     (hipGetSymbolAddress) with that device current; later calls reuse it.
+ */
+nf4_status nf4lora_fwd_noalloc(const nf4_tensor *W, const uint16_t *X, int64_t M,
+                               const uint16_t *L1, const uint16_t *L2, int32_t r, float s,
+                               uint16_t *Y, uint16_t *T_out, void *stream);
+
+/*
  * Backward pass of equation (3) for the adapters and the input; the frozen
  * W gets no gradient ("Lesson 17", Warm-up):
  *   G   = s dY L2^T                 (bf16 [M][r], internal)

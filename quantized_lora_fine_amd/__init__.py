@@ -63,6 +63,7 @@ _SIGS = {
     "nf4_dequantize": ([_T, _vp, _i32, _vp], ctypes.c_int),
     "nf4_workspace_bytes": ([_i32, _i64, _i64, _i64, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
     "nf4lora_fwd": ([_T, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "nf4lora_fwd_noalloc": ([_T, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp], ctypes.c_int),
     "nf4lora_bwd": ([_T, _vp, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "bf16lora_fwd": ([_vp, _i64, _i64, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "bf16lora_bwd": ([_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
@@ -225,6 +226,19 @@ def fwd(q: NF4Weight, X: torch.Tensor, L1: torch.Tensor, L2: torch.Tensor, s: fl
         ws = workspace(NF4_OP_FWD, M, q, r)
     _check(_lib.nf4lora_fwd(ctypes.byref(q.desc), _ptr(_u16(X)), M, _ptr(_u16(L1)), _ptr(_u16(L2)), r, float(s),
                             _ptr(Y), _ptr(T), _ptr(ws), ws.numel(), _stream()), "nf4lora_fwd")
+    return Y, T
+
+
+def fwd_noalloc(q: NF4Weight, X: torch.Tensor, L1: torch.Tensor, L2: torch.Tensor, s: float, want_T: bool = True,
+                out: torch.Tensor | None = None, T_out: torch.Tensor | None = None):
+    """nf4lora_fwd_noalloc: nf4lora_fwd on the library's fixed device area (no workspace argument).
+    With `out` (and `T_out`) given, the call itself allocates nothing."""
+    M, r = X.shape[0], L1.shape[1]
+    Y = out if out is not None else torch.empty(M, q.rows, dtype=torch.bfloat16, device=X.device)
+    T = T_out if T_out is not None else (
+        torch.empty(M, r, dtype=torch.bfloat16, device=X.device) if want_T else None)
+    _check(_lib.nf4lora_fwd_noalloc(ctypes.byref(q.desc), _ptr(_u16(X)), M, _ptr(_u16(L1)), _ptr(_u16(L2)), r,
+                                    float(s), _ptr(Y), _ptr(T), _stream()), "nf4lora_fwd_noalloc")
     return Y, T
 
 

@@ -39,7 +39,7 @@ EXTRA = {"quant.hip": ["-ffp-contract=off"],
          "gemm.hip": ["-ffp-contract=off"],
          "merge.hip": ["-ffp-contract=off"]}
 
-HIP_SOURCES = ["quant.hip", "gemm.hip", "skinny.hip", "merge.hip", "probe.hip"]
+HIP_SOURCES = ["quant.hip", "gemm.hip", "skinny.hip", "merge.hip", "probe.hip", "scratch.hip"]
 CPP_SOURCES = ["api.cpp", "nf4_table.cpp", "plan.cpp"]
 
 

@@ -588,6 +588,21 @@ nf4_status nf4lora_fwd(const nf4_tensor* W, const uint16_t* X, int64_t M, const 
   return layer_fwd(w, X, M, L1, L2, r, s, Y, T_out, ws, ws_bytes, stream);
 }
 
+nf4_status nf4lora_fwd_noalloc(const nf4_tensor* W, const uint16_t* X, int64_t M, const uint16_t* L1,
+                               const uint16_t* L2, int32_t r, float s, uint16_t* Y, uint16_t* T_out, void* stream) {
+  WSrc w;
+  nf4_status st = wsrc_nf4(W, &w);
+  if (st != NF4_OK) return st;
+  st = check_batch(M, r);
+  if (st != NF4_OK) return st;
+  if (M == 0) return NF4_OK;
+  // the plan must fit the fixed area; checked before any HIP call
+  if (plan_fwd(M, w.rows, w.cols, r).total > kNoAllocScratchBytes) return NF4_ERR_WORKSPACE;
+  void* ws = nullptr;
+  NF4_TRY(noalloc_scratch(&ws));
+  return layer_fwd(w, X, M, L1, L2, r, s, Y, T_out, ws, kNoAllocScratchBytes, stream);
+}
+
 nf4_status nf4lora_bwd(const nf4_tensor* W, const uint16_t* X, const uint16_t* dY, int64_t M, const uint16_t* L1,
                        const uint16_t* L2, int32_t r, float s, const uint16_t* T, uint16_t* dX, float* dL1,
                        float* dL2, void* ws, size_t ws_bytes, void* stream) {

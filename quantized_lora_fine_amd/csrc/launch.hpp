@@ -31,6 +31,11 @@ hipError_t launch_error(const float* W, int64_t nblocks, bool dq, double* part, 
 hipError_t launch_error_batch(const float* const* W, const int64_t* rows, const int64_t* cols, int32_t n, bool dq,
                               double* part, double* err, const NF4Enc& c, hipStream_t st);
 hipError_t launch_topk(const double* e, int n, int k, int* idx, hipStream_t st);
+// Workspace of the allocation-free forward: one device array of this size per
+// GPU (scratch.hip).  noalloc_scratch gives its address on the current device.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // MFMA-only probe: `workgroups` x 512 threads, each wave `iters` rounds of 8
 // v_mfma_f32_32x32x16_bf16; out gets one float per thread.
 hipError_t launch_mfma_peak(int iters, int workgroups, float* out, hipStream_t st);

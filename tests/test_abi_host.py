@@ -387,3 +387,20 @@ def test_pass_size_bound():
     cols = (ctypes.c_int64 * 1)(64)
     b = ctypes.c_size_t()
     assert lib.nf4_error_batch_workspace_bytes(rows, cols, 1, ctypes.byref(b)) == nf4.NF4_ERR_SHAPE
+
+
+def test_fwd_noalloc_validation():
+    """The allocation-free forward validates like nf4lora_fwd and rejects, before any HIP call, a layer
+    whose workspace exceeds its fixed 16 MiB area."""
+    v = ctypes.c_void_p
+
+    def call(d, X=C, M=16, L1=D, L2=E, r=8, Y=F, T=G):
+        return lib.nf4lora_fwd_noalloc(ctypes.byref(d), v(X), M, v(L1), v(L2), r, 2.0, v(Y),
+                                       v(T) if T else None, None)
+    assert call(desc(rows=128, cols=128), r=0) == nf4.NF4_ERR_SHAPE
+    assert call(desc(rows=100, cols=128)) == nf4.NF4_ERR_SHAPE
+    assert call(desc(rows=128, cols=128), M=-1) == nf4.NF4_ERR_SHAPE
+    assert call(desc(rows=128, cols=128), M=0) == nf4.NF4_OK
+    big = desc(rows=28672, cols=8192, dq=256, dqs=D)
+    assert nf4.workspace_bytes(nf4.NF4_OP_FWD, 16384, 28672, 8192, 256) > 16 << 20
+    assert call(big, M=16384, r=256) == nf4.NF4_ERR_WORKSPACE
