@@ -1,0 +1,116 @@
+// Unit checks of the launch planners (plan.cpp), built for the CPU with the
+// sanitizers: the batched error pass's launch split at its two bounds (64
+// linears, 2^24 - 1 groups), and the split factors of the skinny products.
+// Exit status 0 when every check holds; each failure is printed.
+#include <cstdio>
+#include <vector>
+
+#include "launch.hpp"
+
+using namespace nf4k;
+
+static int failures = 0;
+#define CHECK(c)                                                   \
+  do {                                                             \
+    if (!(c)) {                                                    \
+      std::printf("FAIL %s:%d: %s\n", __FILE__, __LINE__, #c);     \
+      ++failures;                                                  \
+    }                                                              \
+  } while (0)
+
+// Linears of exactly g groups each: 256 blocks of 64 per row of 16384 columns.
+struct Shapes {
+  std::vector<int64_t> rows, cols;
+  void add(int64_t groups) {
+    rows.push_back(groups);
+    cols.push_back(16384);
+  }
+  int n() const { return (int)rows.size(); }
+};
+
+// Every linear lands in exactly one launch, in order, and each launch keeps
+// both bounds; returns the launches' sizes.
+static std::vector<int> chunks(const Shapes& s) {
+  std::vector<int> out;
+  int64_t g0[kErrBatch + 1];
+  for (int c0 = 0; c0 < s.n();) {
+    const int k = error_batch_chunk(s.rows.data(), s.cols.data(), s.n(), c0, g0);
+    if (k == 0) {
+      out.push_back(0);
+      break;
+    }
+    CHECK(k <= kErrBatch);
+    CHECK(g0[0] == 0);
+    for (int i = 0; i < k; ++i) CHECK(g0[i + 1] - g0[i] == error_groups(s.rows[c0 + i], s.cols[c0 + i]));
+    CHECK(g0[k] <= kMaxLaunchGroups);
+    CHECK((uint64_t)g0[k] * 256u < ((uint64_t)1 << 32));  // work-items of the launch
+    out.push_back(k);
+    c0 += k;
+  }
+  return out;
+}
+
+int main() {
+  CHECK(kMaxLaunchGroups * 256 < ((int64_t)1 << 32));
+  CHECK((kMaxLaunchGroups + 1) * 256 == ((int64_t)1 << 32));
+  {  // 65 one-group linears: 64, then 1
+    Shapes s;
+    for (int i = 0; i < 65; ++i) s.add(1);
+    const std::vector<int> c = chunks(s);
+    CHECK(c.size() == 2 && c[0] == 64 && c[1] == 1);
+  }
+  {  // one linear of exactly the bound fits alone; one group more is refused
+    Shapes s;
+    s.add(kMaxLaunchGroups);
+    std::vector<int> c = chunks(s);
+    CHECK(c.size() == 1 && c[0] == 1);
+    Shapes t;
+    t.add(kMaxLaunchGroups + 1);
+    c = chunks(t);
+    CHECK(c.size() == 1 && c[0] == 0);
+  }
+  {  // two linears that together pass the bound by one group: one launch each
+    Shapes s;
+    s.add(kMaxLaunchGroups - 9);
+    s.add(10);
+    const std::vector<int> c = chunks(s);
+    CHECK(c.size() == 2 && c[0] == 1 && c[1] == 1);
+    Shapes t;  // ... and exactly at the bound: one launch
+    t.add(kMaxLaunchGroups - 10);
+    t.add(10);
+    const std::vector<int> d = chunks(t);
+    CHECK(d.size() == 1 && d[0] == 2);
+  }
+  {  // empty linears take no groups but keep their place
+    Shapes s;
+    s.add(0);
+    s.add(3);
+    s.add(0);
+    const std::vector<int> c = chunks(s);
+    CHECK(c.size() == 1 && c[0] == 3);
+    int64_t g0[kErrBatch + 1];
+    CHECK(error_batch_chunk(s.rows.data(), s.cols.data(), 3, 0, g0) == 3 && g0[1] == 0 && g0[2] == 3 && g0[3] == 3);
+  }
+  {  // a ragged last group counts as one
+    const int64_t r[1] = {3}, c[1] = {64 * 100};  // 300 blocks: 2 groups
+    int64_t g0[kErrBatch + 1];
+    CHECK(error_batch_chunk(r, c, 1, 0, g0) == 1 && g0[1] == 2);
+  }
+  // skinny products: the split covers K (or the tokens) with aligned ranges and
+  // about 512 workgroups in all
+  for (int64_t M : {1, 37, 64, 700, 2048, 8192, 16384}) {
+    for (int K : {64, 192, 4096, 11008, 28672}) {
+      int ks = 0, kr = 0;
+      plan_nt(M, K, &ks, &kr);
+      CHECK(ks >= 1 && kr % 128 == 0 && (int64_t)ks * kr >= K && (int64_t)(ks - 1) * kr < K);
+      int ms = 0;
+      int64_t mr = 0;
+      plan_tn(M, K, &ms, &mr);
+      CHECK(ms >= 1 && mr % 256 == 0 && (int64_t)ms * mr >= M && (int64_t)(ms - 1) * mr < M);
+    }
+  }
+  CHECK(!skinny_nt_whole(16, 16) && skinny_nt_whole(2048, 16) && !skinny_nt_whole(2048, 80));
+  CHECK(skinny_tn_whole(512, 64) && !skinny_tn_whole(511, 64) && !skinny_tn_whole(4096, 128));
+  if (failures == 0) std::printf("plan units: ok\n");
+  return failures == 0 ? 0 : 1;
+}
