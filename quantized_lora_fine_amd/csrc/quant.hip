@@ -45,6 +45,21 @@ __device__ __forceinline__ void load_group(__amdgpu_buffer_rsrc_t wr, int wave, 
   }
 }
 
+// Round i of load_group alone.
+__device__ __forceinline__ void load_round(__amdgpu_buffer_rsrc_t wr, int wave, int sub, int l8, int i,
+                                           floatx4 (&v)[8][2]) {
+  const int lb = wave * 64 + 8 * i + sub;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    v[i][h] = __builtin_bit_cast(floatx4,
+                                 __builtin_amdgcn_raw_buffer_load_b128(wr, (lb * 64 + (8 * h + l8) * 4) * 4, 0, kNT));
+}
+// Rounds of loads kept in flight ahead of the round being encoded, when a
+// wave encodes its rounds as they arrive: 4 rounds (128 KB per CU) are more
+// than the memory system needs in flight, and the last round to arrive then
+// leaves one round of work after it instead of eight.
+constexpr int kAhead = 4;
+
 // Encoder table in LDS, one 16-byte entry per bucket (see NF4Enc):
 // {fp64 bound, code (quantize) or value bits (error) below / above the bound}.
 struct EncEntry {
@@ -200,8 +215,17 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
   enc_to_lds<false>(enc, etab, tid);
   if ((RES || ERR) && tid < 16) tab[tid] = cst.table[tid];
 
+  // PIPE: the rounds are encoded as they arrive, kAhead rounds of loads in
+  // flight ahead of the one being encoded (the error with 8-bit scales and the
+  // residual stage need every block of the group first)
+  constexpr bool PIPE = ERR != 2 && !RES;
   floatx4 v[8][2];
-  load_group(wr, wave, sub, l8, v);
+  if constexpr (PIPE) {
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) load_round(wr, wave, sub, l8, i, v);
+  } else {
+    load_group(wr, wave, sub, l8, v);
+  }
   __syncthreads();  // encoder tables
 
   float amax[8];
@@ -241,7 +265,11 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       // with the error, one round at a time keeps the fp64 temporaries short-lived
-      if constexpr (ERR != 0) __builtin_amdgcn_sched_barrier(0);
+      if constexpr (ERR != 0 || PIPE) __builtin_amdgcn_sched_barrier(0);
+      if constexpr (PIPE) {
+        if (i + kAhead < 8) load_round(wr, wave, sub, l8, i + kAhead, v);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const float m = (ERR == 2) ? amax[i] : block_absmax(v[i]);
       amax[i] = m;
       const BlockEnc be = block_enc(m);
