@@ -370,6 +370,92 @@ __global__ __launch_bounds__(1024) void k_skinny_nt_rows(NtArgs p) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// NT skinny at rank 16 with a row-major B ([16][K]: G = s dY L2^T), whole K per
+// workgroup, with whole-line loads: the same product as k_skinny_nt_rows<16,
+// false>.  A 1024-thread workgroup owns 8 rows of A; wave w takes the
+// 64-column units w, w + 16, ... of K.  For each unit it loads A as 8 rows x
+// 128 bytes (one load, 8 lanes per row) and B as 16 rows x 128 bytes (two
+// loads), so every load reads whole 128-byte lines; loads in the MFMA operand
+// layout read 64 bytes of each of 16 lines, half of every line they touch.  The
+// unit goes through the wave's own LDS area (rows padded to 144 bytes, so the
+// 16 rows of a fragment read fall on distinct banks) and is read back as the
+// operands of two v_mfma_f32_16x16x32_bf16.  Four units per wave are in flight
+// in registers.  The A operand's rows 8..15 repeat rows 0..7; those rows of the
+// result are not used.  The 16 wave tiles are added in LDS in wave order.
+// (A k-major B is read in whole lines by k_skinny_nt_rows already.)
+// ---------------------------------------------------------------------------
+constexpr int kLnRow = 144;  // LDS bytes per staged row of a 64-column unit
+
+__global__ __launch_bounds__(1024) void k_skinny_nt_lines(NtArgs p) {
+  constexpr int RW = 8, RPT = 16, UU = 4;
+  constexpr int SA = RW * kLnRow, SB = RPT * kLnRow;  // A stage: 8 rows; B stage: 16 rows
+  constexpr int RED = 16 * RW * RPT * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[RED + 16 * (SA + SB)];
+  float* red = (float*)smem;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  uint8_t* sa = smem + RED + wave * (SA + SB);
+  uint8_t* sb = sa + SA;
+  const int64_t m0 = (int64_t)blockIdx.x * RW;
+  const int64_t M = p.M;
+  const int K = p.K;
+  // load lanes: row lane/8, 16-byte piece lane%8 of a 128-byte row segment
+  const int lr = lane >> 3, lp = lane & 7;
+  const bool arow_ok = m0 + lr < M;
+  const uint16_t* arow = p.A + (arow_ok ? m0 + lr : 0) * (int64_t)K + 8 * lp;
+  // fragment lanes: row li, k offset kq of a 32-column step
+  const int li = lane & 15;
+  const int kq = (lane >> 4) * 8;
+  floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int kr = 0; kr < K; kr += 1024 * UU) {
+    u32x4 ar[UU], br[UU][2];
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+      const int c0 = kr + 1024 * u + 64 * wave;  // the unit's first column (K % 64 == 0)
+      const bool cv = c0 < K;
+      ar[u] = (cv && arow_ok) ? *(const u32x4*)(arow + c0) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        br[u][i] = cv ? *(const u32x4*)(p.B + (int64_t)(8 * i + lr) * K + c0 + 8 * lp) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+      if (kr + 1024 * u + 64 * wave >= K) break;
+      // stage the unit; the previous unit's reads of this area come first (the
+      // LDS operations of one wave complete in order)
+      *(u32x4*)(sa + lr * kLnRow + 16 * lp) = ar[u];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) *(u32x4*)(sb + (8 * i + lr) * kLnRow + 16 * lp) = br[u][i];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8 af = *(const bf16x8*)(sa + (li & 7) * kLnRow + 2 * (32 * st + kq));
+        const bf16x8 bk = *(const bf16x8*)(sb + li * kLnRow + 2 * (32 * st + kq));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bk, acc, 0, 0, 0);
+      }
+    }
+  }
+  // D[i][jj]: lane holds column jj = lane%16, rows i = 4*(lane/16) + v (rows 8..15 unused)
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int row = 4 * (lane >> 4) + v;
+    if (row < RW) red[(wave * RW + row) * RPT + li] = acc[v];
+  }
+  __syncthreads();
+  for (int e = tid; e < RW * RPT; e += 1024) {
+    const int64_t m = m0 + e / RPT;
+    if (m >= M) continue;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) sum += red[w * RW * RPT + e];
+    const int j = e % RPT;
+    if (p.out1 && j < p.r) p.out1[m * p.ld1 + j] = f32_to_bf16(p.alpha1 * sum);
+    if (p.out2) p.out2[m * RPT + j] = f32_to_bf16(p.alpha2 * sum);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // TN skinny: out[j][n] = alpha * sum_m P[m][j] * Q[m][n]   (j < r)
 // P [M][ldp] bf16 with ldp % 8 == 0 and columns r .. ceil8(r)-1 zero (P is
@@ -706,7 +792,10 @@ hipError_t launch_skinny_nt(const NtArgs& a, int RP, hipStream_t st) {
   if (a.bkn) hipLaunchKernelGGL((k_skinny_nt_rows<R, true>), gr, bl, 0, st, a);      \
   else hipLaunchKernelGGL((k_skinny_nt_rows<R, false>), gr, bl, 0, st, a);
       switch (RP) {
-        case 16: L_NTR(16) break;
+        case 16:
+          if (a.bkn) hipLaunchKernelGGL((k_skinny_nt_rows<16, true>), gr, bl, 0, st, a);
+          else hipLaunchKernelGGL(k_skinny_nt_lines, gr, bl, 0, st, a);
+          break;
         case 32: L_NTR(32) break;
         case 48: L_NTR(48) break;
         default: L_NTR(64) break;
