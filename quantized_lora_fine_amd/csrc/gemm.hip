@@ -38,8 +38,13 @@
 //     the fp32 dequantized weight.
 //   * LDS rows are 128 B (64 bf16) in 8 chunks of 16 B with an XOR swizzle so
 //     that the 16-byte MFMA fragment reads are bank-conflict free.
-//   * Workgroup ids are remapped so the tiles that run together on one XCD
-//     share the same rows of A (its L2 keeps that panel).
+//   * Workgroup ids are remapped so that the tiles running together on one XCD
+//     (workgroups are dealt to the 8 XCDs round-robin) are consecutive in a
+//     tile order that takes two row panels at a time, column by column.  The 32
+//     tiles an XCD runs at once then share 2 panels of A and 16 column tiles of
+//     codes, whose K steps its L2 serves to all of them: 20 % fewer bytes from
+//     memory than one panel with 32 column tiles, whose codes every XCD would
+//     read in full.
 //   * The adapter columns (R <= 64) are multiplied first: each consumer wave
 //     loads its tail fragments straight into registers while the producers
 //     dequantize the first tiles.  The bf16 result tile goes through LDS so
@@ -123,8 +128,13 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
   int lid = blockIdx.x;
   const int nwg = gridDim.x;
   if ((nwg & 7) == 0) lid = (lid & 7) * (nwg >> 3) + (lid >> 3);
-  const int tm = lid / p.tiles_n;
-  const int tn = lid - tm * p.tiles_n;
+  // groups of two row panels (one in a last odd panel), column by column
+  const int tiles_m = (int)((p.M + GBM - 1) / GBM);
+  const int grp = lid / (2 * p.tiles_n);
+  const int gm = min(2, tiles_m - 2 * grp);
+  const int gidx = lid - 2 * grp * p.tiles_n;
+  const int tm = 2 * grp + gidx % gm;
+  const int tn = gidx / gm;
   const int64_t m0 = (int64_t)tm * GBM;
   const int n0 = tn * GBN;
   const int64_t M = p.M;
