@@ -44,7 +44,10 @@
 //     tiles an XCD runs at once then share 2 panels of A and 16 column tiles of
 //     codes, whose K steps its L2 serves to all of them: 20 % fewer bytes from
 //     memory than one panel with 32 column tiles, whose codes every XCD would
-//     read in full.
+//     read in full.  A group's panels are read again for each batch of 16
+//     column tiles, so the 16 panels the XCDs hold at once must stay in the
+//     256 MB Infinity Cache: for K > 16384 (panels over 8 MB) the order takes
+//     one panel at a time.
 //   * The adapter columns (R <= 64) are multiplied first: each consumer wave
 //     loads its tail fragments straight into registers while the producers
 //     dequantize the first tiles.  The bf16 result tile goes through LDS so
@@ -81,6 +84,7 @@ struct GemmArgs {
   int R;     // tail width, a multiple of 16 (0 = no tail)
   int b2kn;  // 0: B2 is [N][R]; > 0: B2 is [R][N] with its first b2kn rows present
   int tiles_n;
+  int group_m;  // row panels per group of the tile order (1 or 2)
   int64_t nblocks;
 };
 
@@ -128,12 +132,13 @@ __global__ __launch_bounds__(GNT) void k_nf4_gemm(GemmArgs p, NF4Consts cst) {
   int lid = blockIdx.x;
   const int nwg = gridDim.x;
   if ((nwg & 7) == 0) lid = (lid & 7) * (nwg >> 3) + (lid >> 3);
-  // groups of two row panels (one in a last odd panel), column by column
+  // groups of group_m row panels (fewer in a last group), column by column
   const int tiles_m = (int)((p.M + GBM - 1) / GBM);
-  const int grp = lid / (2 * p.tiles_n);
-  const int gm = min(2, tiles_m - 2 * grp);
-  const int gidx = lid - 2 * grp * p.tiles_n;
-  const int tm = 2 * grp + gidx % gm;
+  const int G = p.group_m;
+  const int grp = lid / (G * p.tiles_n);
+  const int gm = min(G, tiles_m - G * grp);
+  const int gidx = lid - G * grp * p.tiles_n;
+  const int tm = G * grp + gidx % gm;
   const int tn = gidx / gm;
   const int64_t m0 = (int64_t)tm * GBM;
   const int n0 = tn * GBN;
@@ -645,6 +650,7 @@ hipError_t launch_nf4_gemm(int mode, int src, const uint16_t* A, const uint16_t*
   p.nblocks = (int64_t)N * K / 64;
   const int64_t tiles_m = (M + GBM - 1) / GBM;
   p.tiles_n = (N + GBN - 1) / GBN;
+  p.group_m = K <= 16384 ? 2 : 1;  // see the tile order in the header
   const int64_t nwg = tiles_m * p.tiles_n;
   const dim3 gr((unsigned)nwg), bl(GNT);
   const bool res = codes2 != nullptr && src != kSrcBF16;
