@@ -396,6 +396,8 @@ def test_gemm_k_steps(kt):
 
 @pytest.mark.parametrize("M,o,h,r", [
     (1000, 320, 192, 16),    # padded rank 16: 8-row whole-K workgroups, 16-wave token chunks
+    (1024, 320, 192, 8),     # rank 8 padded to 16: the whole-line G product reads zero rows of L2
+    (2048, 256, 320, 1),     # rank 1 padded to 16
     (2048, 320, 192, 20),    # padded rank 32, r not a multiple of 8 (padded T)
     (2048, 384, 256, 40),    # padded rank 48
     (2048, 320, 576, 64),    # padded rank 64
