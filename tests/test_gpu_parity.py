@@ -394,6 +394,28 @@ def test_gemm_k_steps(kt):
     check_close("dX", dX, f64(d["dY"]) @ wh + tail)
 
 
+def test_gemm_long_k():
+    """The fused GEMM with K = 16448 (257 K steps) in both directions: past 16384 the tile order
+    takes one row panel at a time; 300 rows give two row panels and a ragged tail."""
+    for o, h in ((128, 16448), (16448, 128)):
+        d = synth.random_case(seed=700 + o, rows=o, cols=h, M=300, r=16)
+        q = nf4.quantize(dev(d["W"]), 256)
+        wh = oracle.dequantize(oracle.quantize(d["W"], 64, 256)).astype(np.float64)
+        say(f"gemm long K: M=300, o={o}, h={h}")
+        if h > o:
+            A2 = (d["X"][:, :16].float() * 0.5).bfloat16()
+            B2 = (d["dY"][:16, :].t().float() * 0.02).bfloat16().contiguous()  # [o][16]
+            Y = nf4.matmul(q, dev(d["X"]), False, dev(A2), dev(B2))
+            torch.cuda.synchronize()
+            check_close("Y", Y, f64(d["X"]) @ wh.T + f64(A2) @ f64(B2).T)
+        else:
+            A2 = (d["dY"][:, :16].float() * 0.5).bfloat16()
+            B2 = (d["X"][:16, :].t().float() * 0.02).bfloat16().contiguous()  # [h][16]
+            dX = nf4.matmul(q, dev(d["dY"]), True, dev(A2), dev(B2))
+            torch.cuda.synchronize()
+            check_close("dX", dX, f64(d["dY"]) @ wh + f64(A2) @ f64(B2).T)
+
+
 @pytest.mark.parametrize("M,o,h,r", [
     (1000, 320, 192, 16),    # padded rank 16: 8-row whole-K workgroups, 16-wave token chunks
     (1024, 320, 192, 8),     # rank 8 padded to 16: the whole-line G product reads zero rows of L2
