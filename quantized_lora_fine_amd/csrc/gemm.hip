@@ -650,7 +650,7 @@ hipError_t launch_nf4_gemm(int mode, int src, const uint16_t* A, const uint16_t*
   p.nblocks = (int64_t)N * K / 64;
   const int64_t tiles_m = (M + GBM - 1) / GBM;
   p.tiles_n = (N + GBN - 1) / GBN;
-  p.group_m = K <= 16384 ? 2 : 1;  // see the tile order in the header
+  p.group_m = gemm_group_m(K);  // see the tile order in the header
   const int64_t nwg = tiles_m * p.tiles_n;
   const dim3 gr((unsigned)nwg), bl(GNT);
   const bool res = codes2 != nullptr && src != kSrcBF16;

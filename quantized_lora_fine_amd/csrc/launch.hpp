@@ -134,5 +134,13 @@ hipError_t launch_skinny_tn2(const TnArgs& a, const TnArgs* b, int RP, hipStream
 // per workgroup), which need neither the partial buffers nor the counters
 bool skinny_nt_whole(int64_t M, int RP);
 bool skinny_tn_whole(int64_t M, int RP);
+// column band of the all-token TN kernel for products of N0 and N1 columns
+// (N1 = 0: one product): 64 (whole 128-byte lines of Q per load) when that
+// still gives 192 workgroups or more, else 32
+int skinny_tn_band(int N0, int N1);
+// row panels per group of the fused GEMM's tile order for a contraction of K:
+// 2 while 16 panels of 256 rows (the 8 XCDs' working set) stay within the
+// Infinity Cache, i.e. K <= 16384, else 1
+int gemm_group_m(int K);
 
 }  // namespace nf4k

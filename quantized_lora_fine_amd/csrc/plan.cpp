@@ -48,6 +48,13 @@ bool skinny_nt_whole(int64_t M, int RP) {
 // all tokens per workgroup when the rank is small and the token count is not tiny
 bool skinny_tn_whole(int64_t M, int RP) { return RP <= 64 && M >= 512; }
 
+int skinny_tn_band(int N0, int N1) {
+  const int64_t wide = ((int64_t)N0 + 63) / 64 + ((int64_t)N1 + 63) / 64;
+  return wide >= 192 ? 64 : 32;
+}
+
+int gemm_group_m(int K) { return K <= 16384 ? 2 : 1; }
+
 
 int error_batch_chunk(const int64_t* rows, const int64_t* cols, int32_t n, int32_t c0, int64_t* g0) {
   int k = 0;

@@ -818,9 +818,9 @@ hipError_t launch_skinny_tn2(const TnArgs& a, const TnArgs* b, int RP, hipStream
   if (a.M == 0) return hipSuccess;
   // all tokens per workgroup when the rank is small: 64 columns each (each load
   // of Q reads whole 128-byte lines), or 32 when 64-column bands would leave
-  // fewer than 192 workgroups for the 256 CUs
+  // fewer than 192 workgroups for the 256 CUs (skinny_tn_band)
   if (skinny_tn_whole(a.M, RP)) {
-    const bool wide = (a.N + 63) / 64 + (b ? (b->N + 63) / 64 : 0) >= 192;
+    const bool wide = skinny_tn_band(a.N, b ? b->N : 0) == 64;
     const int nc = wide ? 64 : 32;
     const int nwg0 = (a.N + nc - 1) / nc, nwg1 = b ? (b->N + nc - 1) / nc : 0;
     const TnArgs& a1 = b ? *b : a;

@@ -1,6 +1,7 @@
 // Unit checks of the launch planners (plan.cpp), built for the CPU with the
 // sanitizers: the batched error pass's launch split at its two bounds (64
-// linears, 2^24 - 1 groups), and the split factors of the skinny products.
+// linears, 2^24 - 1 groups), the split factors and band widths of the skinny
+// products, and the fused GEMM's tile-order groups.
 // Exit status 0 when every check holds; each failure is printed.
 #include <cstdio>
 #include <vector>
@@ -111,6 +112,13 @@ int main() {
   }
   CHECK(!skinny_nt_whole(16, 16) && skinny_nt_whole(2048, 16) && !skinny_nt_whole(2048, 80));
   CHECK(skinny_tn_whole(512, 64) && !skinny_tn_whole(511, 64) && !skinny_tn_whole(4096, 128));
+  // band width of the all-token TN kernel: c2 (64 + 64 bands of 64) keeps 32 columns,
+  // c3 (172 + 64) and c5 (448 + 128) take 64; the bound is 192 bands
+  CHECK(skinny_tn_band(4096, 4096) == 32 && skinny_tn_band(11008, 4096) == 64 && skinny_tn_band(28672, 8192) == 64);
+  CHECK(skinny_tn_band(96 * 64, 96 * 64) == 64 && skinny_tn_band(96 * 64, 96 * 64 - 64) == 32);
+  CHECK(skinny_tn_band(12288, 0) == 64 && skinny_tn_band(12224, 0) == 32);
+  // tile-order groups of the fused GEMM: two panels up to K = 16384
+  CHECK(gemm_group_m(64) == 2 && gemm_group_m(16384) == 2 && gemm_group_m(16448) == 1 && gemm_group_m(28672) == 1);
   if (failures == 0) std::printf("plan units: ok\n");
   return failures == 0 ? 0 : 1;
 }
