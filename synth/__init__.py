@@ -64,6 +64,37 @@ def bf16(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
 
 
+def _hash_u24(i, j, seed: int):
+    """Counter-based integer hash of (row i, column j, seed) to 24 bits, for int64
+    numpy arrays or torch tensors alike: two multiply-xorshift rounds on 32 bits
+    (every product stays below 2^60, so int64 never overflows)."""
+    x = (i * 0x9E3779B1 + j * 0x85EBCA77 + seed * 0xC2B2AE3D) & 0xFFFFFFFF
+    x = x ^ (x >> 16)
+    x = (x * 0x045D9F3B) & 0xFFFFFFFF
+    x = x ^ (x >> 16)
+    x = (x * 0x045D9F3B) & 0xFFFFFFFF
+    x = x ^ (x >> 16)
+    return x >> 8
+
+
+def hash_weight(rows, cols, seed: int) -> np.ndarray:
+    """fp32 weights W[i][j] for the given row and column indices (numpy), uniform
+    on [-2^-5, 2^-5) in steps of 2^-28: the 24-bit hash minus 2^23, times 2^-28,
+    both exact in fp32.  Any block of a large weight can be drawn on its own."""
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.asarray(cols, dtype=np.int64)[None, :]
+    u = _hash_u24(i, j, seed)
+    return (u - (1 << 23)).astype(np.float32) * np.float32(2.0 ** -28)
+
+
+def hash_weight_rows_torch(row0: int, nrows: int, cols: int, seed: int, device) -> torch.Tensor:
+    """Rows row0 .. row0+nrows-1 of the same weights as hash_weight, on a torch device."""
+    i = torch.arange(row0, row0 + nrows, dtype=torch.int64, device=device)[:, None]
+    j = torch.arange(cols, dtype=torch.int64, device=device)[None, :]
+    u = _hash_u24(i, j, seed)
+    return (u - (1 << 23)).to(torch.float32) * (2.0 ** -28)
+
+
 def _normal(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
     x = rng.standard_normal(size=shape, dtype=np.float32)
     if sigma != 1.0:

@@ -236,3 +236,75 @@ def test_c4_stack_layers_fullsize():
             dL2r += b
         check_close("dL1", L["dL1"], dL1r)
         check_close("dL2", L["dL2"], dL2r)
+
+
+MAX_O, MAX_H = 1 << 20, 4096   # o * h = 2^32: the largest weight the fused kernels take
+
+
+def test_max_size_weight():
+    """The largest weight the header admits: o * h = 2^32 (1048576 x 4096, 16 GiB in fp32), where
+    the quantize pass and the input-grad GEMM (K = 1048576, 16384 K steps) address the codes
+    through 32-bit buffer ranges up to their ends.  W comes from the counter-based hash of synth
+    on both sides, so the oracle draws only what it checks: codes and scales of sampled 4-row
+    groups (one double-quantization group each) with and without the 8-bit scales, T and Y on
+    sampled output columns, dX on one 64-column block of h (all 1048576 rows of that block), and
+    dL1, dL2 over all 64 tokens."""
+    o, h, M, r, s, seed = MAX_O, MAX_H, 64, 16, 2.0, 11
+    say(f"max-size weight: W [{o}][{h}] ({o * h * 4 >> 30} GiB fp32), M={M}, r={r}")
+    W = torch.empty((o, h), dtype=torch.float32, device=DEV)
+    for r0 in range(0, o, 16384):
+        W[r0:r0 + 16384] = synth.hash_weight_rows_torch(r0, 16384, h, seed, DEV)
+    torch.cuda.synchronize()
+    groups = [0, o // 2 + 4, o - 4]      # first rows of sampled 4-row groups
+
+    say("  quantize with 8-bit scales, sampled groups against the oracle")
+    q8 = nf4.quantize(W, 256)
+    for r0 in groups:
+        ref = oracle.quantize(synth.hash_weight(np.arange(r0, r0 + 4), np.arange(h), seed), 64, 256)
+        got = q8.packed_codes[r0 * h // 2:(r0 + 4) * h // 2].cpu().numpy()
+        assert np.array_equal(got, ref.packed), ("codes, dq", r0)
+        assert np.array_equal(q8.c8[r0 * h // 64:(r0 + 4) * h // 64].cpu().numpy(), ref.c8), ("c8", r0)
+        step = q8.dq_step[r0 // 4:r0 // 4 + 1].cpu().numpy()
+        assert step.view(np.uint32)[0] == ref.dq_scale.view(np.uint32)[0], ("dq step", r0)
+    del q8
+
+    say("  quantize with fp32 scales, sampled groups against the oracle")
+    q = nf4.quantize(W, 0)
+    del W
+    torch.cuda.empty_cache()
+    for r0 in groups:
+        ref = oracle.quantize(synth.hash_weight(np.arange(r0, r0 + 4), np.arange(h), seed), 64, 0)
+        assert np.array_equal(q.packed_codes[r0 * h // 2:(r0 + 4) * h // 2].cpu().numpy(), ref.packed), ("codes", r0)
+        got = q.absmax_f32[r0 * h // 64:(r0 + 4) * h // 64].cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), ref.absmax.view(np.uint32)), ("absmax", r0)
+
+    rng = np.random.default_rng(seed)
+    X = synth.bf16(rng.standard_normal((M, h), dtype=np.float32))
+    L1 = synth.bf16(rng.standard_normal((h, r), dtype=np.float32) * np.float32(0.02))
+    L2 = synth.bf16(rng.standard_normal((r, o), dtype=np.float32) * np.float32(0.02))
+    dY = synth.bf16(rng.standard_normal((M, o), dtype=np.float32))
+    say("  HIP path: fwd, bwd")
+    Y, T = nf4.fwd(q, dev(X), dev(L1), dev(L2), s)
+    dX, dL1, dL2 = nf4.bwd(q, dev(X), dev(dY), dev(L1), dev(L2), s, T=T)
+    torch.cuda.synchronize()
+    del q
+
+    cols = np.array(sorted(set(rng.choice(o, size=30, replace=False).tolist()) | {0, o - 1}))
+    say(f"  oracle Y on {cols.size} output columns")
+    wh = oracle.dequantize(oracle.quantize(synth.hash_weight(cols, np.arange(h), seed), 64, 0))
+    Yr, Tr = oracle.fwd(X, wh, L1, L2[:, torch.from_numpy(cols)], s)
+    check_close("T", T, Tr)
+    check_close("Y columns", Y[:, torch.from_numpy(cols).to(DEV)], Yr)
+
+    b = 37
+    hc = np.arange(64 * b, 64 * b + 64)
+    say(f"  oracle dX on columns {hc[0]}..{hc[-1]} (all {o} rows of that block of W)")
+    whs = oracle.dequantize(oracle.quantize(synth.hash_weight(np.arange(o), hc, seed), 64, 0))
+    dXr = oracle.bwd(X[:, torch.from_numpy(hc)], dY, whs, L1[torch.from_numpy(hc)], L2, s)[0]
+    check_close("dX block", dX[:, torch.from_numpy(hc).to(DEV)], dXr)
+    del whs
+
+    say("  oracle adapter gradients over all tokens")
+    _, dL1r, dL2r = oracle.adapter_grads(X, dY, L1, L2, s)
+    check_close("dL1", dL1, dL1r)
+    check_close("dL2", dL2, dL2r)
