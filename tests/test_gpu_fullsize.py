@@ -308,3 +308,46 @@ def test_max_size_weight():
     _, dL1r, dL2r = oracle.adapter_grads(X, dY, L1, L2, s)
     check_close("dL1", dL1, dL1r)
     check_close("dL2", dL2, dL2r)
+
+
+def test_max_size_bf16_weight():
+    """The largest protected bf16 weight the boundary admits (rows * cols < 2^31: 1048512 x 2048,
+    4 GiB), whose input-grad GEMM reads the bf16 weight through a 32-bit buffer range of almost
+    4 GiB; its last column tile of the forward is ragged (1048512 = 8191.5 x 128).  W is the bf16
+    rounding of the counter-based hash on both sides; T and Y on sampled output columns, dX on
+    one 64-column block of h, dL1 and dL2 over all tokens against the oracle."""
+    o, h, M, r, s, seed = (1 << 20) - 64, 2048, 64, 16, 2.0, 12
+    say(f"max-size bf16 weight: W [{o}][{h}] ({o * h * 2 / 2 ** 30:.2f} GiB bf16), M={M}, r={r}")
+    W = torch.empty((o, h), dtype=torch.bfloat16, device=DEV)
+    for r0 in range(0, o, 16384):
+        n = min(16384, o - r0)
+        W[r0:r0 + n] = synth.hash_weight_rows_torch(r0, n, h, seed, DEV).to(torch.bfloat16)
+    rng = np.random.default_rng(seed)
+    X = synth.bf16(rng.standard_normal((M, h), dtype=np.float32))
+    L1 = synth.bf16(rng.standard_normal((h, r), dtype=np.float32) * np.float32(0.02))
+    L2 = synth.bf16(rng.standard_normal((r, o), dtype=np.float32) * np.float32(0.02))
+    dY = synth.bf16(rng.standard_normal((M, o), dtype=np.float32))
+    say("  HIP path: bf16 fwd, bwd")
+    Y, T = nf4.bf16_fwd(W, dev(X), dev(L1), dev(L2), s)
+    dX, dL1, dL2 = nf4.bf16_bwd(W, dev(X), dev(dY), dev(L1), dev(L2), s, T=T)
+    torch.cuda.synchronize()
+    del W
+
+    cols = np.array(sorted(set(rng.choice(o, size=30, replace=False).tolist()) | {0, o - 1}))
+    say(f"  oracle Y on {cols.size} output columns")
+    wr = synth.bf16(synth.hash_weight(cols, np.arange(h), seed))
+    Yr, Tr = oracle.fwd(X, wr, L1, L2[:, torch.from_numpy(cols)], s)
+    check_close("T", T, Tr)
+    check_close("Y columns", Y[:, torch.from_numpy(cols).to(DEV)], Yr)
+
+    hc = np.arange(64 * 21, 64 * 22)
+    say(f"  oracle dX on columns {hc[0]}..{hc[-1]} (all {o} rows of that block of W)")
+    ws = synth.bf16(synth.hash_weight(np.arange(o), hc, seed))
+    dXr = oracle.bwd(X[:, torch.from_numpy(hc)], dY, ws, L1[torch.from_numpy(hc)], L2, s)[0]
+    check_close("dX block", dX[:, torch.from_numpy(hc).to(DEV)], dXr)
+    del ws
+
+    say("  oracle adapter gradients over all tokens")
+    _, dL1r, dL2r = oracle.adapter_grads(X, dY, L1, L2, s)
+    check_close("dL1", dL1, dL1r)
+    check_close("dL2", dL2, dL2r)
