@@ -52,6 +52,7 @@
 //     loads its tail fragments straight into registers while the producers
 //     dequantize the first tiles.  The bf16 result tile goes through LDS so
 //     that every wave stores whole 128-byte lines.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -651,22 +652,37 @@ hipError_t launch_nf4_gemm(int mode, int src, const uint16_t* A, const uint16_t*
   const int64_t tiles_m = (M + GBM - 1) / GBM;
   p.tiles_n = (N + GBN - 1) / GBN;
   p.group_m = gemm_group_m(K);  // see the tile order in the header
-  const int64_t nwg = tiles_m * p.tiles_n;
-  const dim3 gr((unsigned)nwg), bl(GNT);
   const bool res = codes2 != nullptr && src != kSrcBF16;
-#define NF4K_GEMM(MD, SR, RS) hipLaunchKernelGGL((k_nf4_gemm<MD, SR, RS>), gr, bl, 0, st, p, c)
+  // A launch holds at most 2^32 - 1 work-items (GNT per tile).  Each row of C
+  // depends only on its own rows of A and A2, so a product with more tiles runs
+  // as launches over consecutive ranges of row panels.
+  static_assert(GNT == 512, "gemm_launch_panels counts 512 work-items per tile");
+  const int64_t panels = gemm_launch_panels(p.tiles_n);
+  for (int64_t t0 = 0; t0 < tiles_m; t0 += panels) {
+    const int64_t m0 = t0 * GBM;
+    const int64_t tm = std::min(panels, tiles_m - t0);
+    GemmArgs q = p;
+    q.A = A + m0 * K;
+    q.A2 = A2 ? A2 + m0 * R : nullptr;
+    q.C = C + m0 * N;
+    q.M = std::min(tm * GBM, M - m0);
+    const dim3 gr((unsigned)(tm * p.tiles_n)), bl(GNT);
+#define NF4K_GEMM(MD, SR, RS) hipLaunchKernelGGL((k_nf4_gemm<MD, SR, RS>), gr, bl, 0, st, q, c)
 #define NF4K_GEMM_SRC(MD)                                                                      \
   if (src == kSrcBF16) NF4K_GEMM(MD, kSrcBF16, false);                                         \
   else if (src == kSrcNF4DQ) { if (res) NF4K_GEMM(MD, kSrcNF4DQ, true); else NF4K_GEMM(MD, kSrcNF4DQ, false); } \
   else { if (res) NF4K_GEMM(MD, kSrcNF4, true); else NF4K_GEMM(MD, kSrcNF4, false); }
-  if (mode == MODE_FWD) {
-    NF4K_GEMM_SRC(MODE_FWD)
-  } else {
-    NF4K_GEMM_SRC(MODE_DX)
-  }
+    if (mode == MODE_FWD) {
+      NF4K_GEMM_SRC(MODE_FWD)
+    } else {
+      NF4K_GEMM_SRC(MODE_DX)
+    }
 #undef NF4K_GEMM_SRC
 #undef NF4K_GEMM
-  return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace nf4k

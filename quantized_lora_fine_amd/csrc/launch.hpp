@@ -142,5 +142,14 @@ int skinny_tn_band(int N0, int N1);
 // 2 while 16 panels of 256 rows (the 8 XCDs' working set) stay within the
 // Infinity Cache, i.e. K <= 16384, else 1
 int gemm_group_m(int K);
+// A launch holds at most 2^32 - 1 work-items.  Rows per launch of an NT
+// product over M token rows: M itself up to kNtLaunchRows, else equal
+// consecutive ranges, each a multiple of 64 rows and at least 2^22 rows (so
+// that each range takes the kernel the full product would).
+constexpr int64_t kNtLaunchRows = (int64_t)1 << 24;
+int64_t nt_launch_rows(int64_t M);
+// 256-row panels per launch of the fused GEMM with tiles_n column tiles
+// (512 work-items per tile)
+int64_t gemm_launch_panels(int64_t tiles_n);
 
 }  // namespace nf4k

@@ -55,6 +55,17 @@ int skinny_tn_band(int N0, int N1) {
 
 int gemm_group_m(int K) { return K <= 16384 ? 2 : 1; }
 
+int64_t nt_launch_rows(int64_t M) {
+  if (M <= kNtLaunchRows) return M;
+  const int64_t n = (M + kNtLaunchRows - 1) / kNtLaunchRows;
+  return ((M + n - 1) / n + 63) / 64 * 64;
+}
+
+int64_t gemm_launch_panels(int64_t tiles_n) {
+  const int64_t per = ((int64_t)0xFFFFFFFF / 512) / (tiles_n > 0 ? tiles_n : 1);
+  return per > 0 ? per : 1;
+}
+
 
 int error_batch_chunk(const int64_t* rows, const int64_t* cols, int32_t n, int32_t c0, int64_t* g0) {
   int k = 0;

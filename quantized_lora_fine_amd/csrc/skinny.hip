@@ -782,6 +782,24 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t st) {
 
 hipError_t launch_skinny_nt(const NtArgs& a, int RP, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
+  // A launch holds at most 2^32 - 1 work-items, and the whole-K kernel spends
+  // 1024 of them on 8 rows.  Each output row depends only on its own row of A,
+  // so more rows than kNtLaunchRows run as launches over consecutive row ranges
+  // (nt_launch_rows).  Past 2^24 rows the split kernel's K is never split.
+  if (a.M > kNtLaunchRows) {
+    if (a.ksplit != 1) return hipErrorInvalidValue;
+    const int64_t rows = nt_launch_rows(a.M);
+    for (int64_t m0 = 0; m0 < a.M; m0 += rows) {
+      NtArgs c = a;
+      c.A = a.A + m0 * a.K;
+      c.M = std::min(rows, a.M - m0);
+      if (c.out1) c.out1 = a.out1 + m0 * a.ld1;
+      if (c.out2) c.out2 = a.out2 + m0 * RP;
+      const hipError_t e = launch_skinny_nt(c, RP, st);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   if (a.bkn && !skinny_nt_whole(a.M, RP)) return hipErrorInvalidValue;  // k-major B: whole-K kernel only
   {
     if (skinny_nt_whole(a.M, RP)) {

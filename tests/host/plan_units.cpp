@@ -120,5 +120,25 @@ int main() {
   // tile-order groups of the fused GEMM: two panels up to K = 16384
   CHECK(gemm_group_m(64) == 2 && gemm_group_m(16384) == 2 && gemm_group_m(16448) == 1 && gemm_group_m(28672) == 1);
   if (failures == 0) std::printf("plan units: ok\n");
+  // NT launches: one launch up to 2^24 rows; beyond, ranges of 64-row multiples
+  // that cover M, stay within 2^32 work-items (1024 per 8 rows) and keep the
+  // whole-K kernel (64 workgroups or more) in every range, the last included
+  CHECK(nt_launch_rows(0) == 0 && nt_launch_rows(2048) == 2048 && nt_launch_rows(kNtLaunchRows) == kNtLaunchRows);
+  for (int64_t M : {kNtLaunchRows + 1, (int64_t)1 << 25, ((int64_t)1 << 25) + 77, (int64_t)3 << 24,
+                    ((int64_t)1 << 31) - 1, (int64_t)1 << 31}) {
+    const int64_t rows = nt_launch_rows(M);
+    CHECK(rows % 64 == 0 && rows <= kNtLaunchRows && rows >= ((int64_t)1 << 22));
+    CHECK(rows / 8 * 1024 < ((int64_t)1 << 32));
+    const int64_t n = (M + rows - 1) / rows;
+    CHECK(n == (M + kNtLaunchRows - 1) / kNtLaunchRows);
+    CHECK(M - (n - 1) * rows >= ((int64_t)1 << 22) && skinny_nt_whole(M - (n - 1) * rows, 16));
+  }
+  CHECK(nt_launch_rows(((int64_t)1 << 25) + 77) == 11184896);
+  // fused GEMM launches: whole 256-row panels, at most 2^32 - 1 work-items each
+  for (int64_t tn : {1, 32, 224, 4096, 32768}) {
+    const int64_t pl = gemm_launch_panels(tn);
+    CHECK(pl >= 1 && pl * tn * 512 < ((int64_t)1 << 32) && (pl + 1) * tn * 512 >= ((int64_t)1 << 32));
+  }
+  CHECK(gemm_launch_panels(32768) == 255 && gemm_launch_panels(1) == 8388607);
   return failures == 0 ? 0 : 1;
 }

@@ -351,3 +351,57 @@ def test_max_size_bf16_weight():
     _, dL1r, dL2r = oracle.adapter_grads(X, dY, L1, L2, s)
     check_close("dL1", dL1, dL1r)
     check_close("dL2", dL2, dL2r)
+
+
+def test_token_count_past_one_launch():
+    """A token count whose rank-16 adapter products need more work-items than one launch holds
+    (2^32 - 1; the whole-K kernel spends 1024 on 8 rows, so M > 2^25 used to overflow the grid):
+    M = 2^25 + 77 runs as three row ranges.  X is the counter-based hash (x 32) on both sides, so
+    the oracle draws only sampled rows, chosen at the range edges, at 2^24 and 2^25 and at random.
+    dY is zero except on half of those rows, so dL1 and dL2 over all M tokens come from those
+    rows alone, and dX is exactly zero on the others."""
+    M, h, o, r, s, seed = (1 << 25) + 77, 64, 64, 16, 2.0, 13
+    n = -(-M // (1 << 24))
+    per = (-(-M // n) + 63) // 64 * 64
+    edges = {0, 1, per - 1, per, per + 1, 2 * per - 1, 2 * per, (1 << 24) - 1, 1 << 24,
+             (1 << 25) - 1, 1 << 25, M - 2, M - 1}
+    rng = np.random.default_rng(seed)
+    rows = np.array(sorted(edges | set(rng.choice(M, size=24, replace=False).tolist())))
+    hot = rows[::2]                     # rows with a nonzero dY
+    say(f"token count past one launch: M={M} ({n} ranges of {per} rows), W [{o}][{h}], r={r}, "
+        f"{rows.size} sampled rows")
+    X = torch.empty((M, h), dtype=torch.bfloat16, device=DEV)
+    for r0 in range(0, M, 1 << 21):
+        k = min(1 << 21, M - r0)
+        X[r0:r0 + k] = (synth.hash_weight_rows_torch(r0, k, h, seed, DEV) * 32).to(torch.bfloat16)
+    W = rng.standard_normal((o, h), dtype=np.float32)
+    L1 = synth.bf16(rng.standard_normal((h, r), dtype=np.float32) * np.float32(0.1))
+    L2 = synth.bf16(rng.standard_normal((r, o), dtype=np.float32) * np.float32(0.1))
+    dYh = synth.bf16(rng.standard_normal((hot.size, o), dtype=np.float32))
+    dY = torch.zeros((M, o), dtype=torch.bfloat16, device=DEV)
+    dY[torch.from_numpy(hot).to(DEV)] = dev(dYh)
+    q = nf4.quantize(dev(W), 256)
+    say("  HIP path: fwd, bwd")
+    Y, T = nf4.fwd(q, X, dev(L1), dev(L2), s)
+    dX, dL1, dL2 = nf4.bwd(q, X, dY, dev(L1), dev(L2), s, T=T)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(rows).to(DEV)
+    T, Y, dX = T[idx], Y[idx], dX[idx]
+    del X, dY
+    torch.cuda.empty_cache()
+
+    wh = oracle.dequantize(oracle.quantize(W, 64, 256))
+    Xs = synth.bf16(synth.hash_weight(rows, np.arange(h), seed) * np.float32(32))
+    dYs = torch.zeros((rows.size, o), dtype=torch.bfloat16)
+    dYs[torch.from_numpy(np.searchsorted(rows, hot))] = dYh
+    say("  oracle on the sampled rows")
+    Yr, Tr = oracle.fwd(Xs, wh, L1, L2, s)
+    check_close("T rows", T, Tr)
+    check_close("Y rows", Y, Yr)
+    dXr = oracle.bwd(Xs, dYs, wh, L1, L2, s)[0]
+    check_close("dX rows", dX, dXr)
+    cold = np.setdiff1d(np.arange(rows.size), np.searchsorted(rows, hot))
+    assert not dX[torch.from_numpy(cold).to(DEV)].any(), "dX on rows with dY = 0"
+    _, dL1r, dL2r = oracle.adapter_grads(Xs, dYs, L1, L2, s)
+    check_close("dL1 (all tokens)", dL1, dL1r)
+    check_close("dL2 (all tokens)", dL2, dL2r)
