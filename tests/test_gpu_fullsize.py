@@ -359,7 +359,8 @@ def test_token_count_past_one_launch():
     M = 2^25 + 77 runs as three row ranges.  X is the counter-based hash (x 32) on both sides, so
     the oracle draws only sampled rows, chosen at the range edges, at 2^24 and 2^25 and at random.
     dY is zero except on half of those rows, so dL1 and dL2 over all M tokens come from those
-    rows alone, and dX is exactly zero on the others."""
+    rows alone, and dX is exactly zero on the others.  The backward runs with the saved T and
+    again recomputing T, whose product has row ranges of its own."""
     M, h, o, r, s, seed = (1 << 25) + 77, 64, 64, 16, 2.0, 13
     n = -(-M // (1 << 24))
     per = (-(-M // n) + 63) // 64 * 64
@@ -384,9 +385,11 @@ def test_token_count_past_one_launch():
     say("  HIP path: fwd, bwd")
     Y, T = nf4.fwd(q, X, dev(L1), dev(L2), s)
     dX, dL1, dL2 = nf4.bwd(q, X, dY, dev(L1), dev(L2), s, T=T)
+    say("  HIP path: bwd recomputing T (its own row ranges)")
+    dXb, dL1b, dL2b = nf4.bwd(q, X, dY, dev(L1), dev(L2), s)
     torch.cuda.synchronize()
     idx = torch.from_numpy(rows).to(DEV)
-    T, Y, dX = T[idx], Y[idx], dX[idx]
+    T, Y, dX, dXb = T[idx], Y[idx], dX[idx], dXb[idx]
     del X, dY
     torch.cuda.empty_cache()
 
@@ -405,3 +408,6 @@ def test_token_count_past_one_launch():
     _, dL1r, dL2r = oracle.adapter_grads(Xs, dYs, L1, L2, s)
     check_close("dL1 (all tokens)", dL1, dL1r)
     check_close("dL2 (all tokens)", dL2, dL2r)
+    check_close("dX rows, T recomputed", dXb, dXr)
+    check_close("dL1, T recomputed", dL1b, dL1r)
+    check_close("dL2, T recomputed", dL2b, dL2r)
