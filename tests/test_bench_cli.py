@@ -51,3 +51,14 @@ def test_stored_counters_name_the_current_kernel_hash_format():
     assert len(tr["kernel_source_hash"]) == 16
     for k in ("nf4_gemm_fwd", "nf4_gemm_dx"):
         assert tr["kernels"][k]["bytes_per_launch"] > 0
+
+
+def test_cpu_passes_rates():
+    import numpy as np
+    b = load_bench()
+    # algorithmic bytes per weight: fp32 read, 4-bit code, 8-bit scale per 64, fp32 step per 16384
+    assert abs(b.QUANT_DQ_BYTES_PER_WEIGHT - 4.5159) < 1e-4 and b.ERROR_BYTES_PER_WEIGHT == 4.0
+    W = (np.random.default_rng(0).standard_normal((128, 4096), dtype=np.float32) * np.float32(0.02))
+    r = b.cpu_passes(W, threads=2, reps=1)
+    assert r["quantize_dq_GBps"] > 0 and r["layer_error_GBps"] > 0 and r["threads"] == 2
+    assert "524288 weights" in r["sample"] and "2 chunks of 64 rows" in r["sample"]
