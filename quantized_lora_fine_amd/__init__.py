@@ -150,9 +150,42 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _u16(t: torch.Tensor) -> torch.Tensor:
-    assert t.dtype == torch.bfloat16 and t.is_cuda and t.is_contiguous(), "expected a contiguous cuda bf16 tensor"
+def _need(t, dtype, shape, name: str):
+    """t itself when it is a contiguous tensor of `dtype` on the current cuda device with the given shape
+    (entries None are free; shape None: any); else ValueError.  The library sees raw pointers only, so every
+    size it reads or writes through them is checked here, before any launch."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a tensor, got {type(t).__name__}")
+    if not t.is_cuda or t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name}: expected a tensor on the current cuda device, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if shape is not None and (t.dim() != len(shape) or any(w is not None and n != w for n, w in zip(t.shape, shape))):
+        raise ValueError(f"{name}: expected shape {tuple('*' if w is None else w for w in shape)}, "
+                         f"got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
     return t
+
+
+def _need_vec(t, dtype, n: int, name: str):
+    """A contiguous 1-D tensor of `dtype` with at least n entries (the library writes the first n)."""
+    _need(t, dtype, (None,), name)
+    if t.numel() < n:
+        raise ValueError(f"{name}: expected at least {n} entries, got {t.numel()}")
+    return t
+
+
+def _need_ws(ws, name: str = "ws"):
+    return _need(ws, torch.uint8, None, name)
+
+
+def _need_q(q, rows: int | None = None, cols: int | None = None, name: str = "q"):
+    if not isinstance(q, NF4Weight):
+        raise ValueError(f"{name}: expected an NF4Weight, got {type(q).__name__}")
+    if (rows is not None and q.rows != rows) or (cols is not None and q.cols != cols):
+        raise ValueError(f"{name}: expected a [{rows}][{cols}] weight, got [{q.rows}][{q.cols}]")
+    return q
 
 
 class NF4Weight:
@@ -194,8 +227,9 @@ def quantize(W: torch.Tensor, dq_group: int = 0, out: NF4Weight | None = None, c
              residual: bool = False) -> NF4Weight:
     """nf4_quantize of a cuda fp32 [rows][cols] tensor (into `out` when given; its codebook and residual stage
     then apply).  residual=True also quantizes what the first stage misses into q.residual."""
-    assert W.dtype == torch.float32 and W.is_cuda and W.is_contiguous() and W.dim() == 2
-    q = out if out is not None else NF4Weight(W.shape[0], W.shape[1], dq_group, W.device, codebook, residual)
+    _need(W, torch.float32, (None, None), "W")
+    q = _need_q(out, *W.shape, "out") if out is not None else NF4Weight(W.shape[0], W.shape[1], dq_group, W.device,
+                                                                        codebook, residual)
     _check(_lib.nf4_quantize(_ptr(W), ctypes.byref(q.desc), _stream()), "nf4_quantize")
     return q
 
@@ -204,8 +238,8 @@ def dequantize(q: NF4Weight, bf16: bool = False, out: torch.Tensor | None = None
     """nf4_dequantize into fp32 (or bf16) [rows][cols], into `out` when given."""
     if out is None:
         out = torch.empty(q.rows, q.cols, dtype=torch.bfloat16 if bf16 else torch.float32, device=q.codes.device)
-    assert out.dtype == (torch.bfloat16 if bf16 else torch.float32) and out.is_contiguous()
-    assert out.shape == (q.rows, q.cols)
+    _need_q(q)
+    _need(out, torch.bfloat16 if bf16 else torch.float32, (q.rows, q.cols), "out")
     _check(_lib.nf4_dequantize(ctypes.byref(q.desc), _ptr(out), 1 if bf16 else 0, _stream()), "nf4_dequantize")
     return out
 
@@ -215,16 +249,48 @@ def workspace(op: int, M: int, q: NF4Weight, r: int) -> torch.Tensor:
     return torch.empty(max(n, 1), dtype=torch.uint8, device=q.codes.device)
 
 
+def _fwd_args(o: int, h: int, X, L1, L2, want_T: bool, out, T_out):
+    """Checks the forward's tensors against W [o][h]; returns (M, r, Y, T), allocating the outputs not given."""
+    M = _need(X, torch.bfloat16, (None, h), "X").shape[0]
+    r = _need(L1, torch.bfloat16, (h, None), "L1").shape[1]
+    _need(L2, torch.bfloat16, (r, o), "L2")
+    Y = _need(out, torch.bfloat16, (M, o), "out") if out is not None else \
+        torch.empty(M, o, dtype=torch.bfloat16, device=X.device)
+    if T_out is not None:
+        T = _need(T_out, torch.bfloat16, (M, r), "T_out")
+    else:
+        T = torch.empty(M, r, dtype=torch.bfloat16, device=X.device) if want_T else None
+    return M, r, Y, T
+
+
+def _bwd_args(o: int, h: int, X, dY, L1, L2, T, want_dX: bool, outs):
+    """Checks the backward's tensors against W [o][h]; returns (M, r, dX, dL1, dL2), allocating the outputs
+    when `outs` is None (dX may be None in `outs`: no input gradient)."""
+    M = _need(X, torch.bfloat16, (None, h), "X").shape[0]
+    r = _need(L1, torch.bfloat16, (h, None), "L1").shape[1]
+    _need(L2, torch.bfloat16, (r, o), "L2")
+    _need(dY, torch.bfloat16, (M, o), "dY")
+    if T is not None:
+        _need(T, torch.bfloat16, (M, r), "T")
+    if outs is None:
+        dX = torch.empty(M, h, dtype=torch.bfloat16, device=X.device) if want_dX else None
+        dL1 = torch.empty(h, r, dtype=torch.float32, device=X.device)
+        dL2 = torch.empty(r, o, dtype=torch.float32, device=X.device)
+    else:
+        dX, dL1, dL2 = outs
+        if dX is not None:
+            _need(dX, torch.bfloat16, (M, h), "dX")
+        _need(dL1, torch.float32, (h, r), "dL1")
+        _need(dL2, torch.float32, (r, o), "dL2")
+    return M, r, dX, dL1, dL2
+
+
 def fwd(q: NF4Weight, X: torch.Tensor, L1: torch.Tensor, L2: torch.Tensor, s: float, want_T: bool = True,
         ws: torch.Tensor | None = None, out: torch.Tensor | None = None, T_out: torch.Tensor | None = None):
     """nf4lora_fwd: returns (Y bf16 [M][o], T bf16 [M][r] or None)."""
-    M, r = X.shape[0], L1.shape[1]
-    Y = out if out is not None else torch.empty(M, q.rows, dtype=torch.bfloat16, device=X.device)
-    T = T_out if T_out is not None else (
-        torch.empty(M, r, dtype=torch.bfloat16, device=X.device) if want_T else None)
-    if ws is None:
-        ws = workspace(NF4_OP_FWD, M, q, r)
-    _check(_lib.nf4lora_fwd(ctypes.byref(q.desc), _ptr(_u16(X)), M, _ptr(_u16(L1)), _ptr(_u16(L2)), r, float(s),
+    M, r, Y, T = _fwd_args(_need_q(q).rows, q.cols, X, L1, L2, want_T, out, T_out)
+    ws = _need_ws(ws) if ws is not None else workspace(NF4_OP_FWD, M, q, r)
+    _check(_lib.nf4lora_fwd(ctypes.byref(q.desc), _ptr(X), M, _ptr(L1), _ptr(L2), r, float(s),
                             _ptr(Y), _ptr(T), _ptr(ws), ws.numel(), _stream()), "nf4lora_fwd")
     return Y, T
 
@@ -233,11 +299,8 @@ def fwd_noalloc(q: NF4Weight, X: torch.Tensor, L1: torch.Tensor, L2: torch.Tenso
                 out: torch.Tensor | None = None, T_out: torch.Tensor | None = None):
     """nf4lora_fwd_noalloc: nf4lora_fwd on the library's fixed device area (no workspace argument).
     With `out` (and `T_out`) given, the call itself allocates nothing."""
-    M, r = X.shape[0], L1.shape[1]
-    Y = out if out is not None else torch.empty(M, q.rows, dtype=torch.bfloat16, device=X.device)
-    T = T_out if T_out is not None else (
-        torch.empty(M, r, dtype=torch.bfloat16, device=X.device) if want_T else None)
-    _check(_lib.nf4lora_fwd_noalloc(ctypes.byref(q.desc), _ptr(_u16(X)), M, _ptr(_u16(L1)), _ptr(_u16(L2)), r,
+    M, r, Y, T = _fwd_args(_need_q(q).rows, q.cols, X, L1, L2, want_T, out, T_out)
+    _check(_lib.nf4lora_fwd_noalloc(ctypes.byref(q.desc), _ptr(X), M, _ptr(L1), _ptr(L2), r,
                                     float(s), _ptr(Y), _ptr(T), _stream()), "nf4lora_fwd_noalloc")
     return Y, T
 
@@ -245,16 +308,9 @@ def fwd_noalloc(q: NF4Weight, X: torch.Tensor, L1: torch.Tensor, L2: torch.Tenso
 def bwd(q: NF4Weight, X: torch.Tensor, dY: torch.Tensor, L1: torch.Tensor, L2: torch.Tensor, s: float,
         T: torch.Tensor | None = None, want_dX: bool = True, ws: torch.Tensor | None = None, outs=None):
     """nf4lora_bwd: returns (dX bf16 [M][h] or None, dL1 fp32 [h][r], dL2 fp32 [r][o])."""
-    M, r = X.shape[0], L1.shape[1]
-    if outs is None:
-        dX = torch.empty(M, q.cols, dtype=torch.bfloat16, device=X.device) if want_dX else None
-        dL1 = torch.empty(q.cols, r, dtype=torch.float32, device=X.device)
-        dL2 = torch.empty(r, q.rows, dtype=torch.float32, device=X.device)
-    else:
-        dX, dL1, dL2 = outs
-    if ws is None:
-        ws = workspace(NF4_OP_BWD, M, q, r)
-    _check(_lib.nf4lora_bwd(ctypes.byref(q.desc), _ptr(_u16(X)), _ptr(_u16(dY)), M, _ptr(_u16(L1)), _ptr(_u16(L2)),
+    M, r, dX, dL1, dL2 = _bwd_args(_need_q(q).rows, q.cols, X, dY, L1, L2, T, want_dX, outs)
+    ws = _need_ws(ws) if ws is not None else workspace(NF4_OP_BWD, M, q, r)
+    _check(_lib.nf4lora_bwd(ctypes.byref(q.desc), _ptr(X), _ptr(dY), M, _ptr(L1), _ptr(L2),
                             r, float(s), _ptr(T), _ptr(dX), _ptr(dL1), _ptr(dL2), _ptr(ws), ws.numel(), _stream()),
            "nf4lora_bwd")
     return dX, dL1, dL2
@@ -262,21 +318,17 @@ def bwd(q: NF4Weight, X: torch.Tensor, dY: torch.Tensor, L1: torch.Tensor, L2: t
 
 def bf16_workspace(op: int, M: int, W: torch.Tensor, r: int) -> torch.Tensor:
     """Workspace for bf16lora_fwd / bf16lora_bwd on a bf16 weight [o][h]."""
+    _need(W, torch.bfloat16, (None, None), "W")
     return torch.empty(workspace_bytes(op, M, W.shape[0], W.shape[1], r), dtype=torch.uint8, device=W.device)
 
 
 def bf16_fwd(W: torch.Tensor, X: torch.Tensor, L1: torch.Tensor, L2: torch.Tensor, s: float, want_T: bool = True,
              ws: torch.Tensor | None = None, out: torch.Tensor | None = None, T_out: torch.Tensor | None = None):
     """bf16lora_fwd (a protected linear, bf16 W [o][h]): returns (Y, T or None)."""
-    assert W.dtype == torch.bfloat16 and W.is_cuda and W.is_contiguous() and W.dim() == 2
-    o, h = W.shape
-    M, r = X.shape[0], L1.shape[1]
-    Y = out if out is not None else torch.empty(M, o, dtype=torch.bfloat16, device=X.device)
-    T = T_out if T_out is not None else (
-        torch.empty(M, r, dtype=torch.bfloat16, device=X.device) if want_T else None)
-    if ws is None:
-        ws = bf16_workspace(NF4_OP_FWD, M, W, r)
-    _check(_lib.bf16lora_fwd(_ptr(W), o, h, _ptr(_u16(X)), M, _ptr(_u16(L1)), _ptr(_u16(L2)), r, float(s),
+    o, h = _need(W, torch.bfloat16, (None, None), "W").shape
+    M, r, Y, T = _fwd_args(o, h, X, L1, L2, want_T, out, T_out)
+    ws = _need_ws(ws) if ws is not None else bf16_workspace(NF4_OP_FWD, M, W, r)
+    _check(_lib.bf16lora_fwd(_ptr(W), o, h, _ptr(X), M, _ptr(L1), _ptr(L2), r, float(s),
                              _ptr(Y), _ptr(T), _ptr(ws), ws.numel(), _stream()), "bf16lora_fwd")
     return Y, T
 
@@ -284,18 +336,10 @@ def bf16_fwd(W: torch.Tensor, X: torch.Tensor, L1: torch.Tensor, L2: torch.Tenso
 def bf16_bwd(W: torch.Tensor, X: torch.Tensor, dY: torch.Tensor, L1: torch.Tensor, L2: torch.Tensor, s: float,
              T: torch.Tensor | None = None, want_dX: bool = True, ws: torch.Tensor | None = None, outs=None):
     """bf16lora_bwd: returns (dX or None, dL1, dL2)."""
-    assert W.dtype == torch.bfloat16 and W.is_cuda and W.is_contiguous() and W.dim() == 2
-    o, h = W.shape
-    M, r = X.shape[0], L1.shape[1]
-    if outs is None:
-        dX = torch.empty(M, h, dtype=torch.bfloat16, device=X.device) if want_dX else None
-        dL1 = torch.empty(h, r, dtype=torch.float32, device=X.device)
-        dL2 = torch.empty(r, o, dtype=torch.float32, device=X.device)
-    else:
-        dX, dL1, dL2 = outs
-    if ws is None:
-        ws = bf16_workspace(NF4_OP_BWD, M, W, r)
-    _check(_lib.bf16lora_bwd(_ptr(W), o, h, _ptr(_u16(X)), _ptr(_u16(dY)), M, _ptr(_u16(L1)), _ptr(_u16(L2)),
+    o, h = _need(W, torch.bfloat16, (None, None), "W").shape
+    M, r, dX, dL1, dL2 = _bwd_args(o, h, X, dY, L1, L2, T, want_dX, outs)
+    ws = _need_ws(ws) if ws is not None else bf16_workspace(NF4_OP_BWD, M, W, r)
+    _check(_lib.bf16lora_bwd(_ptr(W), o, h, _ptr(X), _ptr(dY), M, _ptr(L1), _ptr(L2),
                              r, float(s), _ptr(T), _ptr(dX), _ptr(dL1), _ptr(dL2), _ptr(ws), ws.numel(), _stream()),
            "bf16lora_bwd")
     return dX, dL1, dL2
@@ -304,10 +348,12 @@ def bf16_bwd(W: torch.Tensor, X: torch.Tensor, dY: torch.Tensor, L1: torch.Tenso
 def layer_error(W: torch.Tensor, dq_group: int = 0, out: torch.Tensor | None = None,
                 ws: torch.Tensor | None = None, codebook: str = "nf4") -> torch.Tensor:
     """nf4_layer_error: a cuda float64 tensor of shape [1] (no host sync)."""
-    assert W.dtype == torch.float32 and W.is_cuda and W.is_contiguous() and W.dim() == 2
-    rows, cols = W.shape
-    err = out if out is not None else torch.empty(1, dtype=torch.float64, device=W.device)
-    if ws is None:
+    rows, cols = _need(W, torch.float32, (None, None), "W").shape
+    err = _need_vec(out, torch.float64, 1, "out") if out is not None else \
+        torch.empty(1, dtype=torch.float64, device=W.device)
+    if ws is not None:
+        _need_ws(ws)
+    else:
         n = workspace_bytes(NF4_OP_ERROR, 0, rows, cols, 1)
         ws = torch.empty(n, dtype=torch.uint8, device=W.device)
     _check(_lib.nf4_layer_error(_ptr(W), rows, cols, BLOCK, dq_group, CODEBOOKS[codebook], _ptr(err), _ptr(ws),
@@ -335,13 +381,18 @@ def layer_error_batch(Ws, dq_group: int = 0, out: torch.Tensor | None = None, ws
                       codebook: str = "nf4") -> torch.Tensor:
     """nf4_layer_error_batch over a list of cuda fp32 [rows][cols] tensors: a cuda float64 [n] tensor whose
     entry i equals layer_error(Ws[i], dq_group, codebook=codebook) bit for bit (no host sync)."""
-    for W in Ws:
-        assert W.dtype == torch.float32 and W.is_cuda and W.is_contiguous() and W.dim() == 2
+    for i, W in enumerate(Ws):
+        _need(W, torch.float32, (None, None), f"Ws[{i}]")
     n = len(Ws)
     shapes = [tuple(W.shape) for W in Ws]
     dev = Ws[0].device if n else torch.device("cuda")
-    err = out if out is not None else torch.empty(max(n, 1), dtype=torch.float64, device=dev)
-    if ws is None:
+    if out is not None:
+        err = _need_vec(out, torch.float64, n, "out")
+    else:
+        err = torch.empty(max(n, 1), dtype=torch.float64, device=dev)
+    if ws is not None:
+        _need_ws(ws)
+    else:
         ws = torch.empty(error_batch_workspace_bytes(shapes), dtype=torch.uint8, device=dev)
     rows, cols = _shape_arrays(shapes)
     ptrs = (_vp * max(n, 1))(*[W.data_ptr() for W in Ws])
@@ -355,11 +406,13 @@ def quantize_error(W: torch.Tensor, dq_group: int = 0, err_dq_group: int = 0, ou
                    codebook: str = "nf4") -> tuple[NF4Weight, torch.Tensor]:
     """nf4_quantize_error: (q, err) from one pass over W; q as quantize() gives it (one stage; `out`'s codebook
     applies when given), err a cuda float64 [1] equal to layer_error(W, err_dq_group, codebook=q's)."""
-    assert W.dtype == torch.float32 and W.is_cuda and W.is_contiguous() and W.dim() == 2
-    rows, cols = W.shape
-    q = out if out is not None else NF4Weight(rows, cols, dq_group, W.device, codebook)
-    err = err if err is not None else torch.empty(1, dtype=torch.float64, device=W.device)
-    if ws is None:
+    rows, cols = _need(W, torch.float32, (None, None), "W").shape
+    q = _need_q(out, rows, cols, "out") if out is not None else NF4Weight(rows, cols, dq_group, W.device, codebook)
+    err = _need_vec(err, torch.float64, 1, "err") if err is not None else \
+        torch.empty(1, dtype=torch.float64, device=W.device)
+    if ws is not None:
+        _need_ws(ws)
+    else:
         ws = torch.empty(workspace_bytes(NF4_OP_ERROR, 0, rows, cols, 1), dtype=torch.uint8, device=W.device)
     _check(_lib.nf4_quantize_error(_ptr(W), ctypes.byref(q.desc), err_dq_group, _ptr(err), _ptr(ws), ws.numel(),
                                    _stream()), "nf4_quantize_error")
@@ -369,19 +422,28 @@ def quantize_error(W: torch.Tensor, dq_group: int = 0, err_dq_group: int = 0, ou
 def matmul(q: NF4Weight, A: torch.Tensor, transpose: bool = False, A2: torch.Tensor | None = None,
            B2: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
     """nf4_matmul: A * W_hat^T (+ A2 * B2^T), or A * W_hat (+ ...) with transpose=True."""
-    M = A.shape[0]
-    R = 0 if A2 is None else A2.shape[1]
-    N = q.cols if transpose else q.rows
-    C = out if out is not None else torch.empty(M, N, dtype=torch.bfloat16, device=A.device)
-    _check(_lib.nf4_matmul(ctypes.byref(q.desc), 1 if transpose else 0, _ptr(_u16(A)), M,
+    _need_q(q)
+    K, N = (q.rows, q.cols) if transpose else (q.cols, q.rows)
+    M = _need(A, torch.bfloat16, (None, K), "A").shape[0]
+    R = 0
+    if A2 is not None or B2 is not None:
+        if A2 is None or B2 is None:
+            raise ValueError("A2 and B2: give both or neither")
+        R = _need(A2, torch.bfloat16, (M, None), "A2").shape[1]
+        _need(B2, torch.bfloat16, (N, R), "B2")
+    C = _need(out, torch.bfloat16, (M, N), "out") if out is not None else \
+        torch.empty(M, N, dtype=torch.bfloat16, device=A.device)
+    _check(_lib.nf4_matmul(ctypes.byref(q.desc), 1 if transpose else 0, _ptr(A), M,
                            _ptr(A2), _ptr(B2), R, _ptr(C), _stream()), "nf4_matmul")
     return C
 
 
 def check_finite(W: torch.Tensor, ws: torch.Tensor | None = None) -> bool:
     """nf4_check_finite (synchronizes the stream): True when every value of the cuda fp32 W is finite."""
-    assert W.dtype == torch.float32 and W.is_cuda and W.is_contiguous()
-    if ws is None:
+    _need(W, torch.float32, None, "W")
+    if ws is not None:
+        _need_ws(ws)
+    else:
         ws = torch.empty(workspace_bytes(NF4_OP_CHECK, 0, 0, 0, 0), dtype=torch.uint8, device=W.device)
     st = _lib.nf4_check_finite(_ptr(W), W.numel(), _ptr(ws), ws.numel(), _stream())
     if st == NF4_ERR_NONFINITE:
@@ -392,14 +454,19 @@ def check_finite(W: torch.Tensor, ws: torch.Tensor | None = None) -> bool:
 
 def probe_mfma_peak(iters: int, workgroups: int, out: torch.Tensor) -> None:
     """nf4_probe_mfma_peak: 8 * iters bf16 MFMAs (32x32x16) per wave, 8 waves per workgroup (asynchronous)."""
-    assert out.dtype == torch.float32 and out.is_cuda and out.numel() >= workgroups * 512
+    _need(out, torch.float32, None, "out")
+    if out.numel() < workgroups * 512:
+        raise ValueError(f"out: expected at least {workgroups * 512} entries, got {out.numel()}")
     _check(_lib.nf4_probe_mfma_peak(int(iters), int(workgroups), _ptr(out), _stream()), "nf4_probe_mfma_peak")
 
 
 def topk(errors: torch.Tensor, k: int, out: torch.Tensor | None = None) -> torch.Tensor:
     """nf4_topk over a cuda float64 vector: int32 indices, largest first, ties to the lower index."""
-    assert errors.dtype == torch.float64 and errors.is_cuda and errors.is_contiguous()
-    idx = out if out is not None else torch.empty(max(k, 1), dtype=torch.int32, device=errors.device)
+    _need(errors, torch.float64, (None,), "errors")
+    if out is not None:
+        idx = _need_vec(out, torch.int32, k, "out")
+    else:
+        idx = torch.empty(max(k, 1), dtype=torch.int32, device=errors.device)
     _check(_lib.nf4_topk(_ptr(errors), errors.numel(), k, _ptr(idx), _stream()), "nf4_topk")
     return idx[:k]
 
@@ -410,12 +477,12 @@ def merge(base, L1: torch.Tensor, L2: torch.Tensor, s: float, bf16: bool = False
     if isinstance(base, NF4Weight):
         W, q, rows, cols, dev = None, ctypes.byref(base.desc), base.rows, base.cols, base.codes.device
     else:
-        assert base.dtype == torch.float32 and base.is_contiguous() and base.dim() == 2
-        W, q, (rows, cols), dev = base, None, base.shape, base.device
-    r = L1.shape[1]
-    if out is None:
-        out = torch.empty(rows, cols, dtype=torch.bfloat16 if bf16 else torch.float32, device=dev)
-    _check(_lib.nf4lora_merge(_ptr(W), q, rows, cols, _ptr(_u16(L1)), _ptr(_u16(L2)), r, float(s), _ptr(out),
+        W, q, (rows, cols), dev = _need(base, torch.float32, (None, None), "base"), None, base.shape, base.device
+    r = _need(L1, torch.bfloat16, (cols, None), "L1").shape[1]
+    _need(L2, torch.bfloat16, (r, rows), "L2")
+    odt = torch.bfloat16 if bf16 else torch.float32
+    out = _need(out, odt, (rows, cols), "out") if out is not None else torch.empty(rows, cols, dtype=odt, device=dev)
+    _check(_lib.nf4lora_merge(_ptr(W), q, rows, cols, _ptr(L1), _ptr(L2), r, float(s), _ptr(out),
                               1 if bf16 else 0, _stream()), "nf4lora_merge")
     return out
 
@@ -440,14 +507,24 @@ class Stack:
         for i, L in enumerate(linears):
             e = self.arr[i]
             if L.get("q") is not None:
-                e.q = ctypes.pointer(L["q"].desc)
+                q = _need_q(L["q"], name=f"linears[{i}].q")
+                e.q = ctypes.pointer(q.desc)
+                o, h = q.rows, q.cols
             else:
-                W = L["w"]
-                assert W.dtype == torch.bfloat16 and W.is_contiguous()
-                e.w_bf16, e.rows, e.cols = _ptr(W), W.shape[0], W.shape[1]
+                W = _need(L.get("w"), torch.bfloat16, (None, None), f"linears[{i}].w")
+                o, h = W.shape
+                e.w_bf16, e.rows, e.cols = _ptr(W), o, h
             e.r, e.s = int(L.get("r", 0)), float(L.get("s", 0.0))
-            for k in ("L1", "L2", "X", "Y", "T", "dY", "dX", "dL1", "dL2"):
-                setattr(e, k, _ptr(L.get(k)))
+            r = max(e.r, 0)
+            shapes = {"L1": (torch.bfloat16, (h, r)), "L2": (torch.bfloat16, (r, o)),
+                      "X": (torch.bfloat16, (M, h)), "Y": (torch.bfloat16, (M, o)), "T": (torch.bfloat16, (M, r)),
+                      "dY": (torch.bfloat16, (M, o)), "dX": (torch.bfloat16, (M, h)),
+                      "dL1": (torch.float32, (h, r)), "dL2": (torch.float32, (r, o))}
+            for k, (dt, shp) in shapes.items():
+                t = L.get(k)
+                if t is not None:
+                    _need(t, dt, shp, f"linears[{i}].{k}")
+                setattr(e, k, _ptr(t))
         n = _sz()
         _check(_lib.nf4_stack_workspace_bytes(self.arr, len(linears), M, ctypes.byref(n)),
                "nf4_stack_workspace_bytes")

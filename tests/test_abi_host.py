@@ -404,3 +404,12 @@ def test_fwd_noalloc_validation():
     big = desc(rows=28672, cols=8192, dq=256, dqs=D)
     assert nf4.workspace_bytes(nf4.NF4_OP_FWD, 16384, 28672, 8192, 256) > 16 << 20
     assert call(big, M=16384, r=256) == nf4.NF4_ERR_WORKSPACE
+
+
+def test_binding_refuses_host_tensors():
+    """The binding checks device, dtype, shape and layout before it hands a pointer to the library."""
+    import torch
+    with pytest.raises(ValueError, match="cuda"):
+        nf4._need(torch.zeros(4, 4), torch.float32, (4, 4), "W")
+    with pytest.raises(ValueError, match="expected a tensor"):
+        nf4._need(None, torch.float32, None, "W")

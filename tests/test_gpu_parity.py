@@ -721,3 +721,50 @@ def test_residual_layer_and_merge():
         viol = np.abs(got - ref) - tol
         i = np.unravel_index(np.argmax(viol), viol.shape)
         assert viol[i] <= 0, (i, got[i], ref[i], wh[i], tol[i], terms[i])
+
+
+def test_binding_rejects_bad_arguments():
+    """The library takes raw pointers, so the binding checks every tensor's device, dtype, shape and layout
+    against the weight before any launch; each bad argument below raises ValueError and nothing runs."""
+    d = synth.random_case(seed=27, rows=128, cols=192, M=64, r=16)
+    q = nf4.quantize(dev(d["W"]), 0)
+    X, L1, L2, dY = dev(d["X"]), dev(d["L1"]), dev(d["L2"]), dev(d["dY"])
+    Y, T = nf4.fwd(q, X, L1, L2, 2.0)
+    bad = [
+        ("X width", lambda: nf4.fwd(q, X[:, :128].contiguous(), L1, L2, 2.0)),
+        ("X not contiguous", lambda: nf4.fwd(q, torch.empty(192, 64, dtype=torch.bfloat16, device=DEV).t(), L1, L2,
+                                             2.0)),
+        ("X on the host", lambda: nf4.fwd(q, X.cpu(), L1, L2, 2.0)),
+        ("X dtype", lambda: nf4.fwd(q, X.float(), L1, L2, 2.0)),
+        ("L1 rows", lambda: nf4.fwd(q, X, L1[:128].contiguous(), L2, 2.0)),
+        ("L2 shape", lambda: nf4.fwd(q, X, L1, L2[:8].contiguous(), 2.0)),
+        ("out shape", lambda: nf4.fwd(q, X, L1, L2, 2.0, out=torch.empty(64, 64, dtype=torch.bfloat16, device=DEV))),
+        ("T_out shape", lambda: nf4.fwd(q, X, L1, L2, 2.0, T_out=torch.empty(32, 16, dtype=torch.bfloat16,
+                                                                              device=DEV))),
+        ("ws dtype", lambda: nf4.fwd(q, X, L1, L2, 2.0, ws=torch.empty(1 << 20, dtype=torch.float32, device=DEV))),
+        ("dY rows", lambda: nf4.bwd(q, X, dY[:32].contiguous(), L1, L2, 2.0)),
+        ("T rows", lambda: nf4.bwd(q, X, dY, L1, L2, 2.0, T=T[:32].contiguous())),
+        ("dL1 dtype", lambda: nf4.bwd(q, X, dY, L1, L2, 2.0, outs=(None, torch.empty(192, 16, dtype=torch.bfloat16,
+                                                                                      device=DEV),
+                                                                  torch.empty(16, 128, device=DEV)))),
+        ("quantize into another shape", lambda: nf4.quantize(dev(d["W"])[:64].contiguous(), 0, out=q)),
+        ("dequantize out shape", lambda: nf4.dequantize(q, out=torch.empty(64, 192, device=DEV))),
+        ("bf16 W width", lambda: nf4.bf16_fwd(torch.empty(128, 128, dtype=torch.bfloat16, device=DEV), X, L1, L2,
+                                              2.0)),
+        ("matmul A2 without B2", lambda: nf4.matmul(q, X, A2=T)),
+        ("matmul A width", lambda: nf4.matmul(q, X, transpose=True)),
+        ("topk out too short", lambda: nf4.topk(torch.zeros(8, dtype=torch.float64, device=DEV), 4,
+                                                out=torch.empty(2, dtype=torch.int32, device=DEV))),
+        ("error batch out too short", lambda: nf4.layer_error_batch([dev(d["W"])] * 3, 0,
+                                                                    out=torch.empty(2, dtype=torch.float64,
+                                                                                    device=DEV))),
+        ("merge L2 shape", lambda: nf4.merge(q, L1, L2[:, :64].contiguous(), 2.0)),
+        ("stack X shape", lambda: nf4.Stack([{"q": q, "r": 16, "s": 2.0, "L1": L1, "L2": L2,
+                                              "X": X[:, :64].contiguous(), "Y": Y}], 64)),
+    ]
+    for name, call in bad:
+        with pytest.raises(ValueError):
+            call()
+        torch.cuda.synchronize()
+    Y2, _ = nf4.fwd(q, X, L1, L2, 2.0)     # the same call with good arguments still runs
+    assert torch.equal(Y2, Y)
