@@ -296,6 +296,10 @@ def main():
         torch.mm(X, L1, out=Tst)
         Cf2.addmm_(Tst, L2, alpha=s)
 
+    # what plain streaming reaches at this size, as context for the passes over W: torch's fp32 copy of W
+    # (67 MB read, 67 MB written) and its fp32 sum of W (67 MB read)
+    Wc = torch.empty_like(W)
+    Wsum = torch.empty((), dtype=torch.float32, device=dev)
     probe_wg, probe_iters = 256, 180
     probe_out = torch.empty(probe_wg * 512, dtype=torch.float32, device=dev)
     probe_flops = probe_wg * 8 * (probe_iters + probe_iters % 2) * 8 * 32768.0
@@ -310,6 +314,8 @@ def main():
         "merge_nf4_to_bf16": (lambda: nf4.merge(q, L1, L2, s, bf16=True, out=Wm), "bytes",
                               n // 2 + n // 64 + 4 * (n // 64 // 256) + 2 * n),
         "merge_fp32_to_bf16": (lambda: nf4.merge(W, L1, L2, s, bf16=True, out=Wm), "bytes", 6 * n),
+        "torch_copy_fp32_W": (lambda: Wc.copy_(W), "bytes", 8 * n),
+        "torch_sum_fp32_W": (lambda: torch.sum(W, dim=(0, 1), out=Wsum), "bytes", 4 * n),
         "hipblaslt_bf16_fwd": (lambda: torch.mm(X, Wq.t(), out=Cf2), "flops", 2.0 * M * h * o),
         "hipblaslt_bf16_dx": (lambda: torch.mm(dY, Wq, out=Cb2), "flops", 2.0 * M * h * o),
         "unfused_stock_fwd": (stock_fwd, "flops", 2.0 * M * h * o + 2.0 * M * r * (h + o)),
