@@ -327,9 +327,12 @@ def main():
         st = stats[name]
         kernels[name] = dict(st)
         if kind == "flops":
-            kernels[name].update(tflops=round(amount / (st["us"] * 1e-6) / 1e12, 1), flops_per_launch=amount)
+            tf = amount / (st["us"] * 1e-6) / 1e12
+            kernels[name].update(tflops=round(tf, 1), pct_bf16_peak=round(100 * tf / PEAK_BF16_TFLOPS, 1),
+                                 flops_per_launch=amount)
         else:
-            kernels[name].update(GBps=round(amount / (st["us"] * 1e-6) / 1e9, 1), bytes=amount)
+            gb = amount / (st["us"] * 1e-6) / 1e9
+            kernels[name].update(GBps=round(gb, 1), pct_hbm_peak=round(100 * gb / PEAK_HBM_GBS, 1), bytes=amount)
     kernels["timing"] = (f"7 interleaved repetitions of {args.kernel_calls} back-to-back launches per op (HIP events on "
                          f"the launch stream); us = mean of the fastest half")
 
