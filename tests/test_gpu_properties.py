@@ -1,12 +1,18 @@
 """Property sweep of the HIP path against the oracle over generated layers (hypothesis).
 
-Shapes: h and o multiples of 64 up to 512, M from 1 to 300, r in {1, 8, 16, 17,
-64, 128}; double quant on or off; normal, Student-t, outlier and spike weights,
-some with all-zero blocks.  Each example checks the codes and scales bit for
+Shapes: h and o multiples of 64 up to 1536; M from 1 to 300 or at the token
+counts where the adapter kernels switch between split and whole-K / all-token
+forms (512, 1024 and 2048 rows, and their neighbours); r from 1 to 256 across
+the 16-column padding steps; double quant on or off; normal, Student-t,
+outlier and spike weights, some with all-zero blocks; the backward with the
+saved T or recomputing it.  Each example checks the codes and scales bit for
 bit, the layer error within 1e-6 relative, and Y, T, dX, dL1 and dL2 to the
 bar of the parity tests.  Examples are derandomized: every run draws the same
-cases, and each prints its parameters before it touches the GPU.
+cases, and each prints its parameters before it touches the GPU.  The example
+count is 24; NF4LORA_PROPERTY_EXAMPLES raises it for a wider sweep.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -28,25 +34,28 @@ except ImportError as exc:
 from tests.test_gpu_parity import check_close, check_quant, dev, heavy_weight, oracle_layer, run_layer, say
 
 layers = st.tuples(
-    st.integers(1, 8),                       # o / 64
-    st.integers(1, 8),                       # h / 64
-    st.integers(1, 300),                     # M
-    st.sampled_from([1, 8, 16, 17, 64, 128]),
+    st.integers(1, 24),                      # o / 64
+    st.integers(1, 24),                      # h / 64
+    st.one_of(st.integers(1, 300),           # M
+              st.sampled_from([504, 505, 511, 512, 513, 1023, 1024, 1025, 2047, 2048, 2049])),
+    st.sampled_from([1, 8, 16, 17, 31, 32, 33, 48, 64, 65, 128, 256]),
     st.sampled_from([0, 256]),
     st.sampled_from(["normal", "t3", "outliers", "spike"]),
     st.booleans(),                           # zero a run of blocks
     st.sampled_from([0.5, 2.0]),
+    st.booleans(),                           # backward with the saved T (else recomputed)
     st.integers(0, 2**31 - 1),
 )
 
 
-@settings(max_examples=24, deadline=None, derandomize=True, database=None,
+@settings(max_examples=int(os.environ.get("NF4LORA_PROPERTY_EXAMPLES", "24")), deadline=None, derandomize=True, database=None,
           suppress_health_check=[HealthCheck.too_slow])
 @given(layers)
 def test_layer_properties(case):
-    ob, hb, M, r, dq, kind, zeros, s, seed = case
+    ob, hb, M, r, dq, kind, zeros, s, use_T, seed = case
     o, h = 64 * ob, 64 * hb
-    say(f"property case: M={M} o={o} h={h} r={r} dq={dq} weights={kind} zero-blocks={zeros} s={s} seed={seed}")
+    say(f"property case: M={M} o={o} h={h} r={r} dq={dq} weights={kind} zero-blocks={zeros} s={s} "
+        f"T={'saved' if use_T else 'recomputed'} seed={seed}")
     rng = np.random.default_rng(seed)
     d = synth.random_case(seed=seed % 100000, rows=o, cols=h, M=M, r=r)
     if kind != "normal":
@@ -60,7 +69,7 @@ def test_layer_properties(case):
     got = float(nf4.layer_error(dev(d["W"]), dq).cpu()[0])
     want = oracle.layer_error(d["W"], 64, dq)
     assert abs(got - want) <= 1e-6 * max(want, 1e-300), (got, want)
-    Y, T, dX, dL1, dL2 = run_layer(d, s, dq)
+    Y, T, dX, dL1, dL2 = run_layer(d, s, dq, use_T=use_T)
     Yr, Tr, dXr, dL1r, dL2r = oracle_layer(d, s, dq)
     check_close("T", T, Tr)
     check_close("Y", Y, Yr)
