@@ -10,6 +10,10 @@ bit, the layer error within 1e-6 relative, and Y, T, dX, dL1 and dL2 to the
 bar of the parity tests.  Examples are derandomized: every run draws the same
 cases, and each prints its parameters before it touches the GPU.  The example
 count is 24; NF4LORA_PROPERTY_EXAMPLES raises it for a wider sweep.
+
+A second sweep (16 draws by default) covers the rows built on the same kernels:
+protected bf16 layers, the int4 and fp4 codebooks, the residual second stage
+and the merge from an fp32 or NF4 base, over the same kinds of shapes.
 """
 import os
 
@@ -31,7 +35,8 @@ except ImportError as exc:
         raise
     pytest.skip(f"libnf4lora.so not loaded: {exc}", allow_module_level=True)
 
-from tests.test_gpu_parity import check_close, check_quant, dev, heavy_weight, oracle_layer, run_layer, say
+from tests.test_gpu_parity import (check_bf16_layer, check_close, check_quant, dev, heavy_weight, oracle_layer,
+                                   run_layer, say)
 
 layers = st.tuples(
     st.integers(1, 24),                      # o / 64
@@ -76,3 +81,81 @@ def test_layer_properties(case):
     check_close("dX", dX, dXr)
     check_close("dL1", dL1, dL1r)
     check_close("dL2", dL2, dL2r)
+
+
+next_rows = st.tuples(
+    st.sampled_from(["bf16", "int4", "fp4", "residual", "merge-fp32", "merge-nf4"]),
+    st.integers(1, 24),                      # o / 64
+    st.integers(1, 24),                      # h / 64
+    st.one_of(st.integers(1, 300), st.sampled_from([511, 512, 513, 1024, 2048])),
+    st.sampled_from([1, 8, 16, 17, 33, 64, 65, 128, 256]),
+    st.sampled_from([0, 256]),
+    st.sampled_from(["normal", "t3", "outliers", "spike"]),
+    st.sampled_from([0.5, 2.0]),
+    st.booleans(),                           # backward with the saved T (else recomputed)
+    st.integers(0, 2**31 - 1),
+)
+
+
+def check_merge(src, ref_base, d, s, r):
+    """The merge against the oracle within the bounds its roundings allow (as test_merge states them)."""
+    ref = oracle.merge(ref_base, d["L1"], d["L2"], s)
+    L1, L2 = dev(d["L1"]), dev(d["L2"])
+    got = nf4.merge(src, L1, L2, s).cpu().numpy().astype(np.float64)
+    u = 2.0 ** -24
+    terms = s * (np.abs(oracle.lora._f64(d["L1"])) @ np.abs(oracle.lora._f64(d["L2"]))).T
+    tol32 = (r + 2) * u * terms + 2 * u * np.abs(ref)
+    assert np.all(np.abs(got - ref) <= tol32), float(np.max(np.abs(got - ref) - tol32))
+    gotb = nf4.merge(src, L1, L2, s, bf16=True).cpu().float().numpy().astype(np.float64)
+    tolb = 2.0 ** -8 * (np.abs(ref) + tol32) + tol32
+    assert np.all(np.abs(gotb - ref) <= tolb), float(np.max(np.abs(gotb - ref) - tolb))
+
+
+@settings(max_examples=int(os.environ.get("NF4LORA_PROPERTY_EXAMPLES", "16")), deadline=None, derandomize=True,
+          database=None, suppress_health_check=[HealthCheck.too_slow])
+@given(next_rows)
+def test_next_rows_properties(case):
+    """The rows built on the same kernels, over generated shapes: protected bf16 layers, the int4 and fp4
+    codebooks (codes, scales and dequantized weights bit for bit, the error within 1e-6, the layer), the
+    residual second stage (both stages bit for bit, the layer, the merge) and the merge from an fp32 or an
+    NF4 base."""
+    kind, ob, hb, M, r, dq, dist, s, use_T, seed = case
+    o, h = 64 * ob, 64 * hb
+    say(f"next-row case: {kind} M={M} o={o} h={h} r={r} dq={dq} weights={dist} s={s} "
+        f"T={'saved' if use_T else 'recomputed'} seed={seed}")
+    d = synth.random_case(seed=seed % 100000, rows=o, cols=h, M=M, r=r)
+    if dist != "normal":
+        d["W"] = heavy_weight(np.random.default_rng(seed), (o, h), dist)
+    if kind == "bf16":
+        check_bf16_layer(d, s, use_T=use_T)
+        return
+    if kind == "merge-fp32":
+        check_merge(dev(d["W"]), d["W"], d, s, r)
+        return
+    if kind == "merge-nf4":
+        check_merge(nf4.quantize(dev(d["W"]), dq), oracle.dequantize(oracle.quantize(d["W"], 64, dq)), d, s, r)
+        return
+    if kind == "residual":
+        q = nf4.quantize(dev(d["W"]), dq, residual=True)
+        r1, r2 = oracle.quantize_residual(d["W"], 64, dq)
+        check_quant(q, r1)
+        check_quant(q.residual, r2)
+        wh = oracle.dequantize_residual(r1, r2)
+    else:
+        q = nf4.quantize(dev(d["W"]), dq, codebook=kind)
+        ref = oracle.quantize(d["W"], 64, dq, kind)
+        check_quant(q, ref)
+        wh = oracle.dequantize(ref)
+        got = float(nf4.layer_error(dev(d["W"]), dq, codebook=kind).cpu()[0])
+        want = oracle.layer_error(d["W"], 64, dq, kind)
+        assert abs(got - want) <= 1e-6 * max(want, 1e-300), (got, want)
+    assert np.array_equal(nf4.dequantize(q).cpu().numpy().view(np.uint32), wh.view(np.uint32)), "dequantized weight"
+    X, L1, L2, dY = (dev(d[k]) for k in ("X", "L1", "L2", "dY"))
+    Y, T = nf4.fwd(q, X, L1, L2, s)
+    dX, dL1, dL2 = nf4.bwd(q, X, dY, L1, L2, s, T=T if use_T else None)
+    Yr, Tr = oracle.fwd(d["X"], wh, d["L1"], d["L2"], s)
+    dXr, dL1r, dL2r, _ = oracle.bwd(d["X"], d["dY"], wh, d["L1"], d["L2"], s)
+    for name, g, w in (("T", T, Tr), ("Y", Y, Yr), ("dX", dX, dXr), ("dL1", dL1, dL1r), ("dL2", dL2, dL2r)):
+        check_close(name, g, w)
+    if kind == "residual":
+        check_merge(q, wh, d, s, r)
