@@ -2,7 +2,7 @@
 
 api.cpp, nf4_table.cpp and plan.cpp are built with g++ -fsanitize=address,undefined into a
 library whose kernel launchers are stubs (tests/host/launch_stubs.cpp): every host check
-of the ABI runs before a launch.  The launch planners' unit driver (tests/host/plan_units.cpp)
+of the ABI runs before a launch.  The launch planners' unit-check program (tests/host/plan_units.cpp)
 runs under the same sanitizers, and the ABI host tests (tests/test_abi_host.py) run against
 that library in a child process with the ASan runtime preloaded.  Any sanitizer report fails
 the test.
