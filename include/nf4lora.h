@@ -234,8 +234,9 @@ nf4_status nf4lora_fwd(const nf4_tensor *W, const uint16_t *X, int64_t M,
  * hipFree, no allocating library routine).
  *   - A layer whose forward workspace (nf4_workspace_bytes(NF4_OP_FWD, ...))
  *     exceeds 16 MiB is rejected with NF4_ERR_WORKSPACE before any HIP call
- *     (c2-c5 shapes at r <= 64 need 0.07 to 14.5 MiB; r = 256 at M = 16384
- *     and o = 28672 needs 58 MiB: use nf4lora_fwd there).
+ *     (layers from 4096 x 4096 at 2048 tokens to 28672 x 8192 at 16384
+ *     tokens need 0.07 to 14.5 MiB at r <= 64; r = 256 at M = 16384 and
+ *     o = 28672 needs 58 MiB: use nf4lora_fwd there).
  *   - Every call on a GPU shares that GPU's area, and the area keeps the last
  *     call's contents; each call clears what must start at zero with a kernel
  *     of its own (no memset).  Calls that overlap on one GPU (several streams

@@ -594,9 +594,10 @@ __global__ __launch_bounds__(256) void k_skinny_tn(TnArgs p) {
 
 // ---------------------------------------------------------------------------
 // TN skinny, all tokens per workgroup (RP <= 64): the same product as
-// k_skinny_tn without a token split.  A workgroup of WAVES waves (16 for rank
-// 16, else 8 so the larger tiles fit in registers) owns NC = 64 (or 32)
-// columns of Q.  Wave w takes the 32-token chunks w, w+WAVES, ...: it copies
+// k_skinny_tn without a token split.  A workgroup of WAVES = 8 waves owns
+// NC = 64 (or 32) columns of Q; with 8 waves rather than 16, each wave takes
+// enough chunks at 2048 tokens (64 chunks of 32) for its loads to run ahead
+// of its staging and MFMAs.  Wave w takes the 32-token chunks w, w+WAVES, ...: it copies
 // each chunk of Q ([32][NC]) and P ([32][RP]) row-major into its own LDS
 // area with 16-byte stores (DEPTH chunks ahead in registers) and builds both
 // MFMA operands with ds_read_b64_tr_b16, which hands each lane 4 consecutive
@@ -615,7 +616,7 @@ struct TnCols {
   static constexpr int PPR = RPT / 8, PTL = 64 / PPR, PL = (32 + PTL - 1) / PTL;
   static constexpr int STAGE = 32 * (QROW + PROW);                       // bytes per wave
   // chunks in flight per wave, as many as the register budget allows
-  static constexpr int DEPTH = WAVES == 16 ? (NC == 32 ? 4 : 2) : (QL + PL <= 6 ? 3 : 2);
+  static constexpr int DEPTH = QL + PL <= 6 ? 3 : 2;
   static constexpr int SMEM = WAVES * STAGE > 4 * RPT * NC * 4 ? WAVES * STAGE : 4 * RPT * NC * 4;
 };
 
@@ -842,10 +843,10 @@ hipError_t launch_skinny_tn2(const TnArgs& a, const TnArgs* b, int RP, hipStream
     const int nc = wide ? 64 : 32;
     const int nwg0 = (a.N + nc - 1) / nc, nwg1 = b ? (b->N + nc - 1) / nc : 0;
     const TnArgs& a1 = b ? *b : a;
-    const dim3 gr((unsigned)(nwg0 + nwg1)), bl(RP == 16 ? 1024 : 512);
+    const dim3 gr((unsigned)(nwg0 + nwg1)), bl(512);
 #define L_TNC(R)                                                                                          \
-  if (wide) hipLaunchKernelGGL((k_skinny_tn_cols<R, 64, R == 16 ? 16 : 8>), gr, bl, 0, st, a, a1, nwg0, nwg1); \
-  else hipLaunchKernelGGL((k_skinny_tn_cols<R, 32, R == 16 ? 16 : 8>), gr, bl, 0, st, a, a1, nwg0, nwg1);
+  if (wide) hipLaunchKernelGGL((k_skinny_tn_cols<R, 64, 8>), gr, bl, 0, st, a, a1, nwg0, nwg1); \
+  else hipLaunchKernelGGL((k_skinny_tn_cols<R, 32, 8>), gr, bl, 0, st, a, a1, nwg0, nwg1);
     switch (RP) {
       case 16: L_TNC(16) break;
       case 32: L_TNC(32) break;
