@@ -435,6 +435,51 @@ def pin_bwd_special(bwd_fn=olora.bwd, fwd_fn=olora.fwd, seed=13):
     assert not dL2b.any()
 
 
+def pin_adapter_grads(grads_fn=olora.adapter_grads, fwd_fn=olora.fwd, seed=19):
+    """The adapter gradients on their own, as the chunked full-size checks use them.
+
+    Central differences of f = <dY, Y> in each adapter factor (exact up to
+    rounding: Y is linear in L1 and in L2 separately), G against its
+    definition by brute force, and token additivity: the gradients of a batch
+    are the sums over any split of its tokens, and G's rows are those of the
+    parts.
+    """
+    X, W, L1, L2, dY = _small_layer(seed, M=5, h=64, o=7, r=3)
+    s = 0.75
+    G, dL1, dL2 = grads_fn(X, dY, L1, L2, s)
+    assert G.shape == (5, 3) and dL1.shape == (64, 3) and dL2.shape == (3, 7)
+    for m in range(5):
+        for j in range(3):
+            ref = s * sum(float(dY[m][n]) * float(L2[j][n]) for n in range(7))
+            assert abs(G[m][j] - ref) < 1e-12 * max(1.0, abs(ref))
+
+    def f(A, B):
+        Y, _ = fwd_fn(X, W, A, B, s)
+        return float(np.sum(dY * Y))
+
+    eps = 1e-3
+    rng = np.random.default_rng(seed + 1)
+    for _ in range(10):
+        k, j = rng.integers(0, 64), rng.integers(0, 3)
+        Ap, Am = L1.copy(), L1.copy()
+        Ap[k, j] += eps
+        Am[k, j] -= eps
+        g = (f(Ap, L2) - f(Am, L2)) / (2 * eps)
+        assert abs(g - dL1[k, j]) < 1e-8 * max(1.0, abs(g))
+        j2, n = rng.integers(0, 3), rng.integers(0, 7)
+        Bp, Bm = L2.copy(), L2.copy()
+        Bp[j2, n] += eps
+        Bm[j2, n] -= eps
+        g = (f(L1, Bp) - f(L1, Bm)) / (2 * eps)
+        assert abs(g - dL2[j2, n]) < 1e-8 * max(1.0, abs(g))
+    for cut in (1, 3):
+        Ga, a1, a2 = grads_fn(X[:cut], dY[:cut], L1, L2, s)
+        Gb, b1, b2 = grads_fn(X[cut:], dY[cut:], L1, L2, s)
+        assert np.allclose(np.concatenate([Ga, Gb]), G, rtol=1e-12, atol=1e-14)
+        assert np.allclose(a1 + b1, dL1, rtol=1e-12, atol=1e-14)
+        assert np.allclose(a2 + b2, dL2, rtol=1e-12, atol=1e-14)
+
+
 # ---------------------------------------------------------------------------
 # P11-P12: error, counts
 # ---------------------------------------------------------------------------
@@ -691,5 +736,5 @@ ALL_PINS = [
     pin_fwd_bruteforce, pin_fwd_merge, pin_fwd_special, pin_bwd_finite_diff, pin_bwd_special,
     pin_error_bruteforce, pin_error_zero_on_grid, pin_error_tails, pin_counts, pin_topk,
     pin_codebook_tables, pin_codebook_encoders, pin_codebook_roundtrip, pin_residual, pin_bf16_rounding,
-    pin_topk_nan,
+    pin_topk_nan, pin_adapter_grads,
 ]

@@ -149,6 +149,38 @@ def test_mistake_bwd_adapter_term():
     assert _fails(pins.pin_bwd_finite_diff, bwd_fn=bad_bwd)
 
 
+def test_mistake_adapter_grads_unscaled_dl2():
+    # dL2 without the adapter scale s
+    def bad(X, dY, L1, L2, s):
+        G, dL1, dL2 = olora.adapter_grads(X, dY, L1, L2, s)
+        return G, dL1, dL2 / s
+    assert _fails(pins.pin_adapter_grads, grads_fn=bad)
+
+
+def test_mistake_adapter_grads_dl1_from_dy():
+    # dL1 taken against dY L2^T without s (G before scaling)
+    def bad(X, dY, L1, L2, s):
+        G, dL1, dL2 = olora.adapter_grads(X, dY, L1, L2, s)
+        return G, dL1 / s, dL2
+    assert _fails(pins.pin_adapter_grads, grads_fn=bad)
+
+
+def test_mistake_adapter_grads_unscaled_g():
+    def bad(X, dY, L1, L2, s):
+        G, dL1, dL2 = olora.adapter_grads(X, dY, L1, L2, s)
+        return G / s, dL1, dL2
+    assert _fails(pins.pin_adapter_grads, grads_fn=bad)
+
+
+def test_mistake_adapter_grads_mean_over_tokens():
+    # averaging instead of summing over tokens breaks additivity
+    def bad(X, dY, L1, L2, s):
+        G, dL1, dL2 = olora.adapter_grads(X, dY, L1, L2, s)
+        m = len(X)
+        return G, dL1 / m, dL2 / m
+    assert _fails(pins.pin_adapter_grads, grads_fn=bad)
+
+
 def test_mistake_error_without_sqrt():
     def bad_error(W, block=64, dq=0):
         return onf4.layer_error(W, block, dq) ** 2
