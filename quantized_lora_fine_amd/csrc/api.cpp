@@ -337,7 +337,7 @@ nf4_status layer_fwd(const WSrc& W, const uint16_t* X, int64_t M, const uint16_t
   PrepArgs pa{};
   pa.pad[0] = pad_job(L1, 1, r, r, h, l1t, p.RP, h);
   pa.pad[1] = pad_job(L2, 1, o, o, r, l2t, o, p.RP);
-  if (!skinny_nt_whole(M, p.RP)) pa.zero[0] = ZeroJob{cnt, p.ncnt};
+  if (!skinny_nt_use_whole(M, (int)h, p.RP, false)) pa.zero[0] = ZeroJob{cnt, p.ncnt};
   NF4_TRY(launch_prep(pa, hs));
   // T = X L1 (split K, fixed-order reduction) -> T_out (bf16) and s*T (bf16, padded)
   NtArgs nt{X, l1t, M, (int)h, p.ks, p.kr, part, cnt, r, 1.0f, T_out, r, s, ts};
@@ -412,7 +412,9 @@ nf4_status layer_bwd(const WSrc& W, const uint16_t* X, const uint16_t* dY, int64
   }
   if (!T) pa.pad[2] = pad_job(L1, 1, r, r, h, l1t, p.RP, h);
   else if (r % 8 != 0) pa.pad[2] = pad_job(T, r, 1, M, r, tb, M, p.RP);
-  if (!skinny_nt_whole(M, p.RP) || !skinny_tn_whole(M, p.RP)) pa.zero[0] = ZeroJob{cnt, p.ncnt};
+  if (!skinny_nt_use_whole(M, (int)h, p.RP, false) || !skinny_nt_use_whole(M, (int)o, p.RP, false) ||
+      !skinny_tn_whole(M, p.RP))
+    pa.zero[0] = ZeroJob{cnt, p.ncnt};
   NF4_TRY(launch_prep(pa, hs));
   const uint16_t* tsrc = T;
   int ldt = r;

@@ -134,6 +134,8 @@ hipError_t launch_skinny_tn2(const TnArgs& a, const TnArgs* b, int RP, hipStream
 // per workgroup), which need neither the partial buffers nor the counters
 bool skinny_nt_whole(int64_t M, int RP);
 bool skinny_tn_whole(int64_t M, int RP);
+// the kernel one NT product takes (its contraction K; bkn: k-major B)
+bool skinny_nt_use_whole(int64_t M, int K, int RP, bool bkn);
 // column band of the all-token TN kernel for products of N0 and N1 columns
 // (N1 = 0: one product): 64 (whole 128-byte lines of Q per load) when that
 // still gives 192 workgroups or more, else 32

@@ -45,6 +45,17 @@ bool skinny_nt_whole(int64_t M, int RP) {
   return (M + rw - 1) / rw >= 64;
 }
 
+// The whole-K kernel for one NT product, given its contraction K and B layout.
+// A k-major B takes it always.  A rank-64 product with a long contraction over
+// many rows (G at 8192+ tokens against 8192+ outputs) takes the split kernel
+// instead: a whole-K workgroup of 32 rows reads the entire 64 x K operand from
+// L2, a split workgroup of 64 rows half of that per row.
+bool skinny_nt_use_whole(int64_t M, int K, int RP, bool bkn) {
+  if (!skinny_nt_whole(M, RP)) return false;
+  if (bkn) return true;
+  return !(RP == 64 && M >= 8192 && K >= 8192);
+}
+
 // all tokens per workgroup when the rank is small and the token count is not tiny
 bool skinny_tn_whole(int64_t M, int RP) { return RP <= 64 && M >= 512; }
 

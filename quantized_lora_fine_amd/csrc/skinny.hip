@@ -803,7 +803,7 @@ hipError_t launch_skinny_nt(const NtArgs& a, int RP, hipStream_t st) {
   }
   if (a.bkn && !skinny_nt_whole(a.M, RP)) return hipErrorInvalidValue;  // k-major B: whole-K kernel only
   {
-    if (skinny_nt_whole(a.M, RP)) {
+    if (skinny_nt_use_whole(a.M, a.K, RP, a.bkn != 0)) {
       const int rw = RP <= 16 ? 8 : (RP <= 32 ? 16 : 32);
       const int64_t nwg = (a.M + rw - 1) / rw;
       const dim3 gr((unsigned)nwg), bl(1024);

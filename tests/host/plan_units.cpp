@@ -112,6 +112,13 @@ int main() {
   }
   CHECK(!skinny_nt_whole(16, 16) && skinny_nt_whole(2048, 16) && !skinny_nt_whole(2048, 80));
   CHECK(skinny_tn_whole(512, 64) && !skinny_tn_whole(511, 64) && !skinny_tn_whole(4096, 128));
+  // NT kernel per product: rank 64 with 8192+ rows and an 8192+ contraction splits
+  // (c5's G over 28672, c3's gate/up G over 11008); c3's down G (4096), a k-major B,
+  // c2 (rank 16) and too few rows do not
+  CHECK(!skinny_nt_use_whole(16384, 28672, 64, false) && !skinny_nt_use_whole(8192, 11008, 64, false));
+  CHECK(skinny_nt_use_whole(8192, 4096, 64, false) && skinny_nt_use_whole(16384, 28672, 64, true));
+  CHECK(skinny_nt_use_whole(2048, 4096, 16, false) && skinny_nt_use_whole(4096, 8192, 64, false));
+  CHECK(!skinny_nt_use_whole(16, 8192, 16, false) && !skinny_nt_use_whole(16, 8192, 16, true));
   // band width of the all-token TN kernel: c2 (64 + 64 bands of 64) keeps 32 columns,
   // c3 (172 + 64) and c5 (448 + 128) take 64; the bound is 192 bands
   CHECK(skinny_tn_band(4096, 4096) == 32 && skinny_tn_band(11008, 4096) == 64 && skinny_tn_band(28672, 8192) == 64);
